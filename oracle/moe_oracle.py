@@ -1,0 +1,395 @@
+"""Plain, slow, obviously-correct CPU oracle for 4-bit MoE prefill.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU library.
+
+What it follows. The pages describe the prefill route of an A3B-class MoE
+model whose experts are stored as 4-bit integers with a per-block scale:
+the hipfire 0.4.3 benchmarks page, section "Read this before comparing
+columns" (defaults table: the MoE prefill route is either "per-expert
+buffers" or "symmetric IU4 MoE") and section "Known limits" (the fast route
+needs the symmetric expert recipe; the older asymmetric file prefills
+slower and its numerics differ slightly), and the prefill-chunk row of the
+same table (prompts are processed in chunks of 8192 rows). hipEngine's
+announcement ("hipEngine: Fast Native Qwen 3.6 Inference for RDNA3",
+section "Implementation Notes") keeps a CPU-reference oracle for each
+kernel; this module is that practice for this layer. The pages fix neither
+the router, the expert FFN form, the group size nor the nibble layout; the
+readings used here (all listed with the workload recipe) are:
+
+* the router is an fp32 linear map over bf16 activations, optionally with a
+  per-expert bias; the k largest biased logits are selected (ties go to the
+  lower expert index, in descending logit order) and their weights are the
+  softmax over the k selected logits;
+* each expert is a SwiGLU MLP: h = silu(x Wg^T) * (x Wu^T), y = h Wd^T with
+  silu(z) = z / (1 + exp(-z)); gate rows come first in the packed gate/up
+  matrix;
+* 4-bit weights, two per byte, even K index in the low nibble; a group of G
+  consecutive K elements of a row shares an fp16 scale (and, for the
+  asymmetric format, an fp16 minimum): symmetric w = (nibble - 8) * scale,
+  asymmetric w = nibble * scale + min;
+* an optional shared expert runs on every token and is added with weight
+  sigmoid(x . w_s);
+* stacked layers are pre-norm: x <- bf16(x + MoE(bf16(RMSNorm(x)))).
+
+Precision: float64 throughout, except where a floating-point value decides
+an integer: the top-k choice is made on fp32 logits, the precision of the
+GPU router's output. Layer inputs and outputs are bf16 by definition of the
+interface, so the stack rounds to bf16 at those boundaries only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64",
+    "round_to_bf16",
+    "unpack_nibbles",
+    "dequant",
+    "router_logits",
+    "shared_gate",
+    "select_topk",
+    "permute",
+    "unpermute",
+    "swiglu_expert",
+    "expert_ffn",
+    "combine",
+    "moe_layer",
+    "moe_layer_rows",
+    "rmsnorm",
+    "moe_stack",
+    "silu",
+    "sigmoid",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact: bf16 is the top half
+    of an IEEE binary32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(bits_or_half) -> np.ndarray:
+    a = np.asarray(bits_or_half)
+    if a.dtype == np.uint16:
+        a = a.view(np.float16)
+    return a.astype(np.float64)
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), returned as
+    uint16 bit patterns. bf16 keeps 8 significant bits and the binary32
+    exponent range; below 2^-126 the spacing is fixed at 2^-133."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.float64)
+    finite = np.isfinite(v) & (v != 0)
+    _, e = np.frexp(np.where(finite, v, 1.0))          # v = m * 2^e, 0.5 <= |m| < 1
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))   # spacing of 8-bit significands
+    r = np.rint(v / quantum) * quantum                  # rint: ties to even
+    out[...] = np.where(finite, r, v)
+    big = np.abs(out) > 3.3895313892515355e38            # largest finite bf16
+    out = np.where(big & finite, np.copysign(np.inf, out), out)
+    bits32 = out.astype(np.float32).view(np.uint32)     # exact: value has 8 bits
+    return (bits32 >> 16).astype(np.uint16)
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ---------------------------------------------------------------------------
+# 4-bit block dequantization
+# ---------------------------------------------------------------------------
+
+def unpack_nibbles(packed) -> np.ndarray:
+    """[R][K/2] bytes -> [R][K] nibble values 0..15. Byte j of a row holds
+    element 2j in bits 0-3 and element 2j+1 in bits 4-7."""
+    p = np.asarray(packed, dtype=np.uint8)
+    R, half = p.shape
+    out = np.empty((R, 2 * half), dtype=np.int64)
+    out[:, 0::2] = p & 0x0F
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def dequant(packed, scale, minv, G: int, quant: str) -> np.ndarray:
+    """Dequantize one weight matrix [R][K] to float64.
+
+    symmetric (quant == "sym"):  w[r,k] = (nib[r,k] - 8) * scale[r, k//G]
+    asymmetric (quant == "asym"): w[r,k] = nib[r,k] * scale[r, k//G] + min[r, k//G]
+    """
+    nib = unpack_nibbles(packed).astype(np.float64)
+    R, K = nib.shape
+    if K % G:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.repeat(f16_to_f64(scale).reshape(R, K // G), G, axis=1)
+    if quant == "sym":
+        return (nib - 8.0) * s
+    if quant == "asym":
+        m = np.repeat(f16_to_f64(minv).reshape(R, K // G), G, axis=1)
+        return nib * s + m
+    raise ValueError(quant)
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def router_logits(xf, w_router, bias=None) -> np.ndarray:
+    """L[t,e] = sum_h x[t,h] * Wr[e,h] (+ b[e]), float64."""
+    L = np.asarray(xf, np.float64) @ np.asarray(w_router, np.float64).T
+    if bias is not None:
+        L = L + np.asarray(bias, np.float64)[None, :]
+    return L
+
+
+def shared_gate(xf, w_s) -> np.ndarray:
+    """sigmoid(x . w_s) per token, float64."""
+    return sigmoid(np.asarray(xf, np.float64) @ np.asarray(w_s, np.float64))
+
+
+def select_topk(logits32, k: int):
+    """Top-k selection on fp32 logits.
+
+    ids[t] lists the k experts with the largest logit, largest first; equal
+    logits are ordered by ascending expert index (-0.0 equals +0.0, since the
+    comparison is numeric). weights[t,j] = exp(L_j - L_max) / sum over the k
+    selected of exp(L_i - L_max), computed in float64.
+    """
+    L = np.asarray(logits32, dtype=np.float32)
+    T, E = L.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # lexsort: last key is primary. Primary: -logit (numeric, so -0.0 == +0.0),
+    # secondary: expert index ascending.
+    Ld = L.astype(np.float64)
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.empty((T, E), dtype=np.int64)
+    for t in range(T):
+        order[t] = np.lexsort((idx[t], -Ld[t]))
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(Ld, ids.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return ids, w
+
+
+def permute(ids, E: int):
+    """Group the T*k (token, slot) pairs by expert.
+
+    Pair p = t*k + j. counts[e] = number of pairs routed to e; offsets is the
+    exclusive prefix sum (E+1 entries); sorted_pairs lists, expert by expert,
+    the pairs of that expert in ascending p; inv[p] is the position of p in
+    sorted_pairs.
+    """
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    P = flat.size
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    if counts.size != E:
+        raise ValueError("expert id out of range")
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    sorted_pairs = np.argsort(flat, kind="stable").astype(np.int64)
+    inv = np.empty(P, dtype=np.int64)
+    inv[sorted_pairs] = np.arange(P)
+    return counts, offsets, sorted_pairs, inv
+
+
+def unpermute(rows_sorted, inv):
+    """Back to pair order: out[p] = rows_sorted[inv[p]]."""
+    return np.asarray(rows_sorted)[np.asarray(inv)]
+
+
+# ---------------------------------------------------------------------------
+# experts
+# ---------------------------------------------------------------------------
+
+def swiglu_expert(X, W13, W2):
+    """One SwiGLU expert on rows X [n][H]: W13 [2I][H] (gate rows first),
+    W2 [H][I]. Returns (h [n][I], y [n][H])."""
+    I = W13.shape[0] // 2
+    g = X @ W13[:I].T
+    u = X @ W13[I:].T
+    h = silu(g) * u
+    return h, h @ W2.T
+
+
+def _expert_mats(w, e, G, quant, prefix="w"):
+    def m(name):
+        t = w.get(f"{prefix}{name}")
+        if t is None:
+            return None
+        return t[e] if e is not None else t
+    W13 = dequant(m("13"), m("13_scale"), m("13_min"), G, quant)
+    W2 = dequant(m("2"), m("2_scale"), m("2_min"), G, quant)
+    return W13, W2
+
+
+def expert_ffn(xf, sorted_pairs, offsets, k: int, w: dict, G: int, quant: str):
+    """Run every routed expert on its rows, in expert-sorted order.
+
+    Row r of expert e (offsets[e] <= r < offsets[e+1]) is the token
+    sorted_pairs[r] // k. Returns (h_perm [P][I], y_perm [P][H]) float64,
+    unweighted.
+    """
+    xf = np.asarray(xf, np.float64)
+    E = len(offsets) - 1
+    P = int(offsets[-1])
+    I = w["w13"].shape[1] // 2
+    H = xf.shape[1]
+    h_perm = np.zeros((P, I))
+    y_perm = np.zeros((P, H))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        W13, W2 = _expert_mats(w, e, G, quant)
+        X = xf[np.asarray(sorted_pairs[a:b]) // k]
+        h, y = swiglu_expert(X, W13, W2)
+        h_perm[a:b] = h
+        y_perm[a:b] = y
+    return h_perm, y_perm
+
+
+def shared_expert(xf, w: dict, G: int, quant: str):
+    W13, W2 = _expert_mats(w, None, G, quant, prefix="s")
+    return swiglu_expert(np.asarray(xf, np.float64), W13, W2)
+
+
+def combine(y_perm, inv, topk_w, y_shared=None, shared_w=None, residual=None):
+    """out[t] = sum_j w[t,j] * y_perm[inv[t*k+j]] (+ sigma[t] * y_shared[t])
+    (+ residual[t]), float64."""
+    T, k = np.asarray(topk_w).shape
+    yp = np.asarray(y_perm, np.float64)[np.asarray(inv).reshape(T, k)]   # [T][k][H]
+    out = np.einsum("tk,tkh->th", np.asarray(topk_w, np.float64), yp)
+    if y_shared is not None:
+        out = out + np.asarray(shared_w, np.float64)[:, None] * np.asarray(y_shared, np.float64)
+    if residual is not None:
+        out = out + np.asarray(residual, np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def _weights_dict(li) -> dict:
+    """Accept either a dict of numpy arrays or an object with attributes
+    (numpy or CPU torch tensors)."""
+    names = ["w_router", "router_bias", "shared_gate", "w13", "w13_scale", "w13_min",
+             "w2", "w2_scale", "w2_min", "s13", "s13_scale", "s13_min",
+             "s2", "s2_scale", "s2_min", "norm_weight"]
+    d = {}
+    for n in names:
+        v = li.get(n) if isinstance(li, dict) else getattr(li, n, None)
+        if v is None:
+            d[n] = None
+            continue
+        if hasattr(v, "detach"):
+            v = v.detach().cpu()
+            if str(v.dtype) == "torch.float16":
+                v = v.view(dtype=__import__("torch").int16).numpy().view(np.uint16)
+            else:
+                v = v.numpy()
+        d[n] = np.asarray(v)
+    return d
+
+
+def moe_layer(x_bits, li, k: int, G: int, quant: str, logits32=None, residual_bits=None):
+    """One MoE layer on bf16 activations x_bits [T][H] (uint16 bit patterns).
+
+    If logits32 is given (fp32 [T][E]) the top-k decision is taken on those
+    logits instead of the oracle's own (teacher forcing for parity checks);
+    everything after the decision is recomputed here. Returns a dict with
+    every intermediate: logits (float64), logits32, ids, weights, counts,
+    offsets, sorted_pairs, inv, h_perm, y_perm, shared_w, y_shared, out
+    (float64, before the final bf16 rounding).
+    """
+    w = _weights_dict(li)
+    xf = bf16_to_f64(x_bits)
+    E = w["w_router"].shape[0]
+    L = router_logits(xf, w["w_router"], w["router_bias"])
+    L32 = L.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
+    ids, tw = select_topk(L32, k)
+    counts, offsets, sorted_pairs, inv = permute(ids, E)
+    h_perm, y_perm = expert_ffn(xf, sorted_pairs, offsets, k, w, G, quant)
+    sw = ys = hs = None
+    if w["s13"] is not None:
+        sw = shared_gate(xf, w["shared_gate"])
+        hs, ys = shared_expert(xf, w, G, quant)
+    res = bf16_to_f64(residual_bits) if residual_bits is not None else None
+    out = combine(y_perm, inv, tw, ys, sw, res)
+    return dict(logits=L, logits32=L32, ids=ids, weights=tw, counts=counts, offsets=offsets,
+                sorted_pairs=sorted_pairs, inv=inv, h_perm=h_perm, y_perm=y_perm,
+                shared_w=sw, h_shared=hs, y_shared=ys, out=out)
+
+
+def moe_layer_rows(x_bits, rows, li, k: int, G: int, quant: str, logits32_rows=None,
+                   residual_bits=None, cache=None):
+    """Layer output for a subset of tokens only (tokens do not interact in
+    an MoE FFN, so each token's output depends on its own row alone).
+
+    rows: token indices; x_bits: the full [T][H] activation tensor (only the
+    listed rows are read); logits32_rows: fp32 logits of those rows for
+    teacher forcing. `cache` (a dict) keeps dequantized experts between calls.
+    Returns dict(ids, weights, logits, out) for the listed rows.
+    """
+    w = _weights_dict(li)
+    rows = np.asarray(rows, dtype=np.int64)
+    xf = bf16_to_f64(np.asarray(x_bits)[rows])
+    L = router_logits(xf, w["w_router"], w["router_bias"])
+    L32 = L.astype(np.float32) if logits32_rows is None else np.asarray(logits32_rows, np.float32)
+    ids, tw = select_topk(L32, k)
+    cache = {} if cache is None else cache
+    out = np.zeros_like(xf)
+    for i in range(len(rows)):
+        for j in range(k):
+            e = int(ids[i, j])
+            if e not in cache:
+                cache[e] = _expert_mats(w, e, G, quant)
+            W13, W2 = cache[e]
+            _, y = swiglu_expert(xf[i:i + 1], W13, W2)
+            out[i] += tw[i, j] * y[0]
+    if w["s13"] is not None:
+        if "shared" not in cache:
+            cache["shared"] = _expert_mats(w, None, G, quant, prefix="s")
+        W13, W2 = cache["shared"]
+        _, ys = swiglu_expert(xf, W13, W2)
+        out += shared_gate(xf, w["shared_gate"])[:, None] * ys
+    if residual_bits is not None:
+        out += bf16_to_f64(np.asarray(residual_bits)[rows])
+    return dict(ids=ids, weights=tw, logits=L, out=out)
+
+
+def rmsnorm(x_bits, weight, eps: float) -> np.ndarray:
+    """RMSNorm: x * (mean_h x^2 + eps)^(-1/2) * g, float64 (eps inside the
+    square root)."""
+    xf = bf16_to_f64(x_bits)
+    r = 1.0 / np.sqrt(np.mean(xf * xf, axis=1, keepdims=True) + eps)
+    return xf * r * np.asarray(weight, np.float64)[None, :]
+
+
+def moe_stack(x_bits, layers, k: int, G: int, quant: str, eps: float, chunk: int = 0):
+    """Pre-norm stack: for each chunk of rows, for each layer l,
+    x <- bf16(x + MoE_l(bf16(RMSNorm_l(x)))). Returns bf16 bits [T][H]."""
+    x = np.array(x_bits, dtype=np.uint16, copy=True)
+    T = x.shape[0]
+    chunk = T if chunk <= 0 else chunk
+    for r0 in range(0, T, chunk):
+        xc = x[r0:r0 + chunk]
+        for li in layers:
+            w = _weights_dict(li)
+            xn = round_to_bf16(rmsnorm(xc, w["norm_weight"], eps))
+            res = moe_layer(xn, li, k, G, quant, residual_bits=xc)
+            xc = round_to_bf16(res["out"])
+        x[r0:r0 + chunk] = xc
+    return x

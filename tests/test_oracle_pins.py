@@ -1,0 +1,449 @@
+"""Pins of the CPU oracle against things other than itself: closed forms,
+hand-worked layers, exact sums, brute force on tiny inputs, invariants and
+special cases that reduce to textbook operations. CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, make_layer, make_tokens, quantize_asym, quantize_sym
+from synth.gen import f32_to_bf16_bits, make_stack_layer
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_layers.json")
+
+
+# ---------------------------------------------------------------------------
+# helpers written independently of the oracle
+# ---------------------------------------------------------------------------
+
+def _pack_rows(nib_rows):
+    """Pack nibble rows by hand: byte j = n[2j] | n[2j+1] << 4."""
+    n = np.asarray(nib_rows, dtype=np.uint8)
+    return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _const_f16(shape, value):
+    return np.full(shape, value, dtype=np.float16).view(np.uint16)
+
+
+def _bf16(vals):
+    return f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def test_unpack_nibble_order_hand_bytes():
+    # byte 0x21: element 0 = 1 (low nibble), element 1 = 2 (high nibble)
+    p = np.array([[0x21, 0xF0, 0x0F, 0x8A]], dtype=np.uint8)
+    assert oracle.unpack_nibbles(p).tolist() == [[1, 2, 0, 15, 15, 0, 10, 8]]
+
+
+def test_dequant_sym_all_nibbles_closed_form():
+    # one row holding nibbles 0..15 in order; scale 0.5 on both groups of 8
+    nib = [list(range(16))]
+    packed = _pack_rows(nib)
+    scale = _const_f16((1, 2), 0.5)
+    w = oracle.dequant(packed, scale, None, 8, "sym")
+    expect = [-4.0, -3.5, -3.0, -2.5, -2.0, -1.5, -1.0, -0.5,
+              0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 3.5]
+    assert w.tolist() == [expect]
+
+
+def test_dequant_asym_all_nibbles_closed_form():
+    nib = [list(range(16))]
+    packed = _pack_rows(nib)
+    scale = _const_f16((1, 1), 0.25)
+    mn = _const_f16((1, 1), -1.0)
+    w = oracle.dequant(packed, scale, mn, 16, "asym")
+    expect = [-1.0 + 0.25 * n for n in range(16)]
+    assert w.tolist() == [expect]
+
+
+def test_dequant_group_boundaries_use_own_scale():
+    # G = 2: elements 0,1 use scale[0], 2,3 use scale[1]; two rows
+    nib = [[9, 10, 9, 10], [7, 8, 15, 0]]
+    packed = _pack_rows(nib)
+    scale = np.array([[1.0, 0.125], [2.0, 4.0]], dtype=np.float16).view(np.uint16)
+    w = oracle.dequant(packed, scale, None, 2, "sym")
+    assert w.tolist() == [[1.0, 2.0, 0.125, 0.25], [-2.0, 0.0, 28.0, -32.0]]
+    mn = np.array([[0.5, -0.5], [0.0, 1.0]], dtype=np.float16).view(np.uint16)
+    wa = oracle.dequant(packed, scale, mn, 2, "asym")
+    assert wa.tolist() == [[9.5, 10.5, 1.125 - 0.5 + 0.0, 1.25 - 0.5],
+                           [14.0, 16.0, 61.0, 1.0]]
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantizer_roundtrip_error_sym(G):
+    g = torch.Generator().manual_seed(11)
+    w = torch.randn(48, 256, generator=g) * 0.02
+    packed, s16 = quantize_sym(w, G)
+    deq = oracle.dequant(packed.numpy(), s16.numpy().view(np.uint16), None, G, "sym")
+    s = np.repeat(s16.float().numpy().astype(np.float64), G, axis=1)
+    amax = np.repeat(w.reshape(48, -1, G).abs().amax(-1).numpy().astype(np.float64), G, axis=1)
+    err = np.abs(deq - w.numpy().astype(np.float64))
+    # rounding to the nearest level, plus the slack from fp16 rounding of the
+    # scale at the clamped extreme (|q| <= 8, |s16 - s| <= 2^-11 s)
+    assert np.all(err <= s / 2 + 8 * s * 2.0 ** -10 + 1e-12)
+    # a wrong nibble order or offset would give errors of order amax
+    assert err.max() < 0.2 * amax.max()
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_quantizer_roundtrip_error_asym(G):
+    g = torch.Generator().manual_seed(12)
+    w = torch.randn(40, 256, generator=g) * 0.02
+    packed, s16, m16 = quantize_asym(w, G)
+    deq = oracle.dequant(packed.numpy(), s16.numpy().view(np.uint16),
+                         m16.numpy().view(np.uint16), G, "asym")
+    s = np.repeat(s16.float().numpy().astype(np.float64), G, axis=1)
+    err = np.abs(deq - w.numpy().astype(np.float64))
+    assert np.all(err <= s / 2 + 16 * s * 2.0 ** -10 + 2.0 ** -11 * 0.1)
+
+
+def test_round_to_bf16_matches_torch_on_f32_values():
+    g = torch.Generator().manual_seed(3)
+    v = torch.cat([torch.randn(20000, generator=g) * 10.0 ** torch.randint(-30, 30, (20000,), generator=g),
+                   torch.tensor([0.0, -0.0, 1.0, -1.0, 3.3895313892515355e38])])
+    ours = oracle.round_to_bf16(v.double().numpy())
+    ref = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_round_to_bf16_ties_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1.0
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: ties to even -> 1+2^-6
+    vals = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30])
+    out = oracle.bf16_to_f64(oracle.round_to_bf16(vals))
+    assert out.tolist() == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7]
+
+
+# ---------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------
+
+def test_router_logits_exact_sum():
+    rng = np.random.default_rng(5)
+    x = _bf16(rng.standard_normal((3, 64)))
+    wr = rng.standard_normal((5, 64)).astype(np.float32) * 0.02
+    b = rng.standard_normal(5).astype(np.float32)
+    L = oracle.router_logits(oracle.bf16_to_f64(x), wr, b)
+    xf = oracle.bf16_to_f64(x)
+    for t in range(3):
+        for e in range(5):
+            exact = sum(Fraction(float(xf[t, h])) * Fraction(float(wr[e, h])) for h in range(64))
+            exact += Fraction(float(b[e]))
+            assert abs(L[t, e] - float(exact)) <= 1e-13 * max(1.0, abs(float(exact)))
+
+
+def _brute_topk(row, k):
+    # full sort of (value desc, index asc) pairs, written independently
+    pairs = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))
+    ids = pairs[:k]
+    vals = [float(row[e]) for e in ids]
+    m = max(vals)
+    ex = [math.exp(v - m) for v in vals]
+    s = math.fsum(ex)
+    return ids, [v / s for v in ex]
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (16, 1), (16, 16), (128, 8), (256, 8)])
+def test_select_topk_matches_brute_force(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    L = (rng.standard_normal((40, E)) * 0.9).astype(np.float32)
+    ids, w = oracle.select_topk(L, k)
+    for t in range(40):
+        bi, bw = _brute_topk(L[t], k)
+        assert ids[t].tolist() == bi
+        assert np.allclose(w[t], bw, rtol=1e-15, atol=0)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-15)
+    assert np.all(w >= 0) and np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_select_topk_ties_and_special_cases():
+    L = np.array([[1.0, 3.0, 3.0, 0.5, 3.0, -1.0],
+                  [0.0, -0.0, 0.0, -0.0, 0.0, 0.0],
+                  [2.0, 2.0, 2.0, 2.0, 2.0, 2.0]], dtype=np.float32)
+    ids, w = oracle.select_topk(L, 3)
+    assert ids.tolist() == [[1, 2, 4], [0, 1, 2], [0, 1, 2]]
+    assert np.allclose(w, 1.0 / 3.0, rtol=1e-15)
+    ids1, w1 = oracle.select_topk(L, 1)
+    assert ids1[:, 0].tolist() == [1, 0, 0] and np.all(w1 == 1.0)
+    # k = E: the weights are the full softmax
+    Lr = np.array([[0.1, -0.3, 2.0, 0.7]], dtype=np.float32)
+    ids4, w4 = oracle.select_topk(Lr, 4)
+    ex = np.exp(Lr[0].astype(np.float64))
+    full = ex / ex.sum()
+    assert np.allclose(w4[0], full[ids4[0]], rtol=1e-14)
+    assert ids4[0].tolist() == [2, 3, 0, 1]
+
+
+def test_permute_invariants_and_identity():
+    rng = np.random.default_rng(9)
+    T, k, E = 300, 8, 32
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, offsets, sp, inv = oracle.permute(ids, E)
+    P = T * k
+    assert counts.sum() == P and offsets[0] == 0 and offsets[-1] == P
+    assert np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(sp[inv], np.arange(P))
+    flat = ids.reshape(-1)
+    for e in range(E):
+        seg = sp[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)          # ascending pair index (stable)
+    M = rng.standard_normal((P, 5))
+    assert np.array_equal(oracle.unpermute(M[sp], inv), M)   # permute then unpermute
+    # hand example: ids [[1,0],[1,2]] -> pairs by expert: e0:[1], e1:[0,2], e2:[3]
+    c, o, s, i = oracle.permute(np.array([[1, 0], [1, 2]]), 3)
+    assert c.tolist() == [1, 2, 1] and o.tolist() == [0, 1, 3, 4]
+    assert s.tolist() == [1, 0, 2, 3] and i.tolist() == [1, 0, 2, 3]
+
+
+# ---------------------------------------------------------------------------
+# whole layer: worked examples, brute force and special cases
+# ---------------------------------------------------------------------------
+
+def _golden_layer(case):
+    H, E, I, G = case["H"], case["E"], case["I"], case["G"]
+    w = {"w_router": np.array(case["w_router"], np.float32),
+         "router_bias": None if case.get("router_bias") is None else np.array(case["router_bias"], np.float32)}
+    sc = case.get("scale")
+    mn = case.get("min")
+    w13, w13s, w13m, w2, w2s, w2m = [], [], [], [], [], []
+    for ex in case["experts"]:
+        w13.append(_pack_rows(ex["w13_nibbles"]))
+        w2.append(_pack_rows(ex["w2_nibbles"]))
+        s13 = ex.get("w13_scale", sc)
+        s2 = ex.get("w2_scale", sc)
+        w13s.append(_const_f16((2 * I, H // G), s13))
+        w2s.append(_const_f16((H, I // G), s2))
+        if case["quant"] == "asym":
+            w13m.append(_const_f16((2 * I, H // G), mn))
+            w2m.append(_const_f16((H, I // G), mn))
+    w.update(w13=np.stack(w13), w13_scale=np.stack(w13s), w2=np.stack(w2), w2_scale=np.stack(w2s),
+             w13_min=np.stack(w13m) if w13m else None, w2_min=np.stack(w2m) if w2m else None)
+    if "shared" in case:
+        sh = case["shared"]
+        w.update(s13=_pack_rows(sh["w13_nibbles"]), s2=_pack_rows(sh["w2_nibbles"]),
+                 s13_scale=_const_f16((2 * I, H // G), sc), s2_scale=_const_f16((H, I // G), sc),
+                 s13_min=_const_f16((2 * I, H // G), mn), s2_min=_const_f16((H, I // G), mn),
+                 shared_gate=np.array(case["shared_gate"], np.float32))
+    return w
+
+
+def test_golden_worked_layers():
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        w = _golden_layer(case)
+        x = _bf16([case["x"]])
+        res = _bf16([case["residual"]]) if "residual" in case else None
+        r = oracle.moe_layer(x, w, case["k"], case["G"], case["quant"], residual_bits=res)
+        assert r["ids"].tolist() == case["expect_ids"], case["name"]
+        assert np.allclose(r["weights"], case["expect_weights"], rtol=1e-14, atol=0), case["name"]
+        assert np.allclose(r["out"], case["expect_out"], rtol=1e-13, atol=1e-15), case["name"]
+
+
+def _dense_bruteforce(x_bits, li, k, G, quant):
+    """Every expert on every token, then masked by the routing weights;
+    written without the oracle's permutation or expert loop."""
+    xf = oracle.bf16_to_f64(x_bits)
+    wr = li.w_router.numpy().astype(np.float64)
+    L = xf @ wr.T
+    if li.router_bias is not None:
+        L = L + li.router_bias.numpy().astype(np.float64)
+    L32 = L.astype(np.float32)
+    T, E = L32.shape
+    mask = np.zeros((T, E))
+    for t in range(T):
+        ids, ws = _brute_topk(L32[t], k)
+        for e, wv in zip(ids, ws):
+            mask[t, e] = wv
+
+    def f16(t):
+        return t.numpy().view(np.uint16)
+
+    out = np.zeros_like(xf)
+    for e in range(E):
+        W13 = oracle.dequant(li.w13[e].numpy(), f16(li.w13_scale[e]),
+                             None if li.w13_min is None else f16(li.w13_min[e]), G, quant)
+        W2 = oracle.dequant(li.w2[e].numpy(), f16(li.w2_scale[e]),
+                            None if li.w2_min is None else f16(li.w2_min[e]), G, quant)
+        I = W13.shape[0] // 2
+        g = xf @ W13[:I].T
+        u = xf @ W13[I:].T
+        y = ((g / (1 + np.exp(-g))) * u) @ W2.T
+        out += mask[:, e:e + 1] * y
+    if li.s13 is not None:
+        W13 = oracle.dequant(li.s13.numpy(), f16(li.s13_scale),
+                             None if li.s13_min is None else f16(li.s13_min), G, quant)
+        W2 = oracle.dequant(li.s2.numpy(), f16(li.s2_scale),
+                            None if li.s2_min is None else f16(li.s2_min), G, quant)
+        I = W13.shape[0] // 2
+        g = xf @ W13[:I].T
+        u = xf @ W13[I:].T
+        ys = ((g / (1 + np.exp(-g))) * u) @ W2.T
+        gate = 1 / (1 + np.exp(-(xf @ li.shared_gate.numpy().astype(np.float64))))
+        out += gate[:, None] * ys
+    return out
+
+
+def _xbits(x):
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_sparse_matches_dense_bruteforce_tiny():
+    cfg = CONFIGS["tiny"]
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, cfg.k, cfg.G, cfg.quant)
+    d = _dense_bruteforce(xb, li, cfg.k, cfg.G, cfg.quant)
+    assert np.allclose(r["out"], d, rtol=1e-9, atol=1e-12)
+
+
+def test_sparse_matches_dense_bruteforce_shrunken_skew_shared():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["skew_shared"], T=24, H=256, E=16, I=64, shared_I=64)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, cfg.k, cfg.G, cfg.quant)
+    d = _dense_bruteforce(xb, li, cfg.k, cfg.G, cfg.quant)
+    assert np.allclose(r["out"], d, rtol=1e-9, atol=1e-12)
+    # the Zipf bias concentrates load on low expert indices
+    assert r["counts"][0] >= r["counts"][-1]
+
+
+def test_sparse_matches_dense_bruteforce_shrunken_a3b():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["a3b_pp512"], T=16, H=256, E=32, I=128)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, cfg.k, cfg.G, cfg.quant)
+    d = _dense_bruteforce(xb, li, cfg.k, cfg.G, cfg.quant)
+    assert np.allclose(r["out"], d, rtol=1e-9, atol=1e-12)
+
+
+def test_single_expert_is_textbook_swiglu_mlp():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny"], E=1, k=1)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, 1, cfg.G, cfg.quant)
+    assert np.all(r["weights"] == 1.0)
+    W13 = oracle.dequant(li.w13[0].numpy(), li.w13_scale[0].numpy().view(np.uint16), None, cfg.G, "sym")
+    W2 = oracle.dequant(li.w2[0].numpy(), li.w2_scale[0].numpy().view(np.uint16), None, cfg.G, "sym")
+    xt = torch.from_numpy(oracle.bf16_to_f64(xb))
+    gate = torch.nn.functional.linear(xt, torch.from_numpy(W13[:cfg.I]))
+    up = torch.nn.functional.linear(xt, torch.from_numpy(W13[cfg.I:]))
+    ref = torch.nn.functional.linear(torch.nn.functional.silu(gate) * up, torch.from_numpy(W2))
+    assert np.allclose(r["out"], ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_zero_weights_give_zero_output():
+    cfg = CONFIGS["tiny"]
+    li = make_layer(cfg)
+    li.w13 = torch.full_like(li.w13, 0x88)     # every nibble 8 -> w = 0
+    li.w2 = torch.full_like(li.w2, 0x88)
+    r = oracle.moe_layer(_xbits(make_tokens(cfg)), li, cfg.k, cfg.G, cfg.quant)
+    assert np.all(r["out"] == 0.0)
+
+
+def test_shared_expert_only():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["skew_shared"], T=8, H=128, E=8, I=64, shared_I=64)
+    li = make_layer(cfg)
+    li.w2 = torch.zeros_like(li.w2)            # nibble 0, scale*0+min ... force zero rows:
+    li.w2_scale = torch.zeros_like(li.w2_scale)
+    li.w2_min = torch.zeros_like(li.w2_min)    # routed down projections are exactly 0
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, cfg.k, cfg.G, cfg.quant)
+    xf = oracle.bf16_to_f64(xb)
+    W13 = oracle.dequant(li.s13.numpy(), li.s13_scale.numpy().view(np.uint16),
+                         li.s13_min.numpy().view(np.uint16), cfg.G, "asym")
+    W2 = oracle.dequant(li.s2.numpy(), li.s2_scale.numpy().view(np.uint16),
+                        li.s2_min.numpy().view(np.uint16), cfg.G, "asym")
+    xt = torch.from_numpy(xf)
+    h = torch.nn.functional.silu(xt @ torch.from_numpy(W13[:64]).T) * (xt @ torch.from_numpy(W13[64:]).T)
+    ys = (h @ torch.from_numpy(W2).T).numpy()
+    gate = torch.sigmoid(xt @ li.shared_gate.double()).numpy()
+    assert np.allclose(r["out"], gate[:, None] * ys, rtol=1e-12, atol=1e-15)
+
+
+def test_one_hot_routing_selects_expert_row():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny"], T=4, k=1)
+    li = make_layer(cfg)
+    li.w_router = torch.zeros_like(li.w_router)
+    li.router_bias = torch.tensor([0.0, 0.0, 0.0, 5.0, 0.0, 0.0, 0.0, 0.0])
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer(xb, li, 1, cfg.G, cfg.quant)
+    assert np.all(r["ids"] == 3) and r["counts"].tolist() == [0, 0, 0, 4, 0, 0, 0, 0]
+    W13 = oracle.dequant(li.w13[3].numpy(), li.w13_scale[3].numpy().view(np.uint16), None, cfg.G, "sym")
+    W2 = oracle.dequant(li.w2[3].numpy(), li.w2_scale[3].numpy().view(np.uint16), None, cfg.G, "sym")
+    _, y = oracle.swiglu_expert(oracle.bf16_to_f64(xb), W13, W2)
+    assert np.allclose(r["out"], y, rtol=1e-14)
+
+
+def test_rows_subset_matches_full_layer():
+    cfg = CONFIGS["tiny"]
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    full = oracle.moe_layer(xb, li, cfg.k, cfg.G, cfg.quant)
+    rows = [0, 5, 63, 17]
+    sub = oracle.moe_layer_rows(xb, rows, li, cfg.k, cfg.G, cfg.quant)
+    assert np.array_equal(sub["ids"], full["ids"][rows])
+    assert np.allclose(sub["out"], full["out"][rows], rtol=1e-12, atol=1e-15)
+
+
+def test_rmsnorm_closed_form():
+    x = _bf16([[3.0, 4.0, 0.0, 0.0], [1.0, 1.0, 1.0, 1.0]])
+    g = np.array([1.0, 2.0, 1.0, 0.5])
+    out = oracle.rmsnorm(x, g, 0.0)
+    # row 0: mean square = 25/4 -> rms 2.5 ; row 1: rms 1
+    assert np.allclose(out, [[1.2, 3.2, 0.0, 0.0], [1.0, 2.0, 1.0, 0.5]], rtol=1e-15)
+    out_eps = oracle.rmsnorm(x, g, 1e-6)
+    assert np.allclose(out_eps[1], np.array([1.0, 2.0, 1.0, 0.5]) / math.sqrt(1 + 1e-6), rtol=1e-15)
+
+
+def _small_stack(n_layers=3):
+    from dataclasses import replace
+    cfg = replace(CONFIGS["stack40"], T=48, H=128, E=8, I=64, shared_I=64, n_layers=n_layers, chunk=16)
+    layers = [make_stack_layer(cfg, l) for l in range(n_layers)]
+    return cfg, layers
+
+
+def test_stack_chunked_equals_unchunked():
+    cfg, layers = _small_stack()
+    xb = _xbits(make_tokens(cfg))
+    a = oracle.moe_stack(xb, layers, cfg.k, cfg.G, cfg.quant, cfg.rms_eps, chunk=16)
+    b = oracle.moe_stack(xb, layers, cfg.k, cfg.G, cfg.quant, cfg.rms_eps, chunk=0)
+    assert np.array_equal(a, b)
+
+
+def test_stack_token_permutation_equivariance():
+    cfg, layers = _small_stack()
+    xb = _xbits(make_tokens(cfg))
+    perm = np.random.default_rng(1).permutation(cfg.T)
+    a = oracle.moe_stack(xb, layers, cfg.k, cfg.G, cfg.quant, cfg.rms_eps)
+    b = oracle.moe_stack(xb[perm], layers, cfg.k, cfg.G, cfg.quant, cfg.rms_eps)
+    assert np.array_equal(a[perm], b)
+
+
+def test_stack_layer_is_residual_plus_moe_of_norm():
+    cfg, layers = _small_stack(1)
+    xb = _xbits(make_tokens(cfg))
+    a = oracle.moe_stack(xb, layers, cfg.k, cfg.G, cfg.quant, cfg.rms_eps)
+    # one layer written out by hand from the pieces
+    xf = oracle.bf16_to_f64(xb)
+    g = layers[0].norm_weight.numpy().astype(np.float64)
+    xn = xf / np.sqrt((xf ** 2).mean(1, keepdims=True) + cfg.rms_eps) * g
+    xn_b = oracle.round_to_bf16(xn)
+    moe = oracle.moe_layer(xn_b, layers[0], cfg.k, cfg.G, cfg.quant)["out"]
+    assert np.array_equal(a, oracle.round_to_bf16(xf + moe))
