@@ -1,0 +1,210 @@
+/*
+ * moe.h - C ABI of the 4-bit block-quantized MoE prefill library (gfx950).
+ *
+ * One MoE FFN layer over a prefill chunk of T tokens:
+ *   route   : fp32 router logits, top-k selection, softmax over the k chosen
+ *   permute : group the T*k (token, slot) pairs by expert
+ *   experts : per expert, SwiGLU FFN with 4-bit block-quantized weights
+ *   combine : weighted sum of each token's k expert outputs (+ shared expert,
+ *             + residual)
+ *
+ * The pages this follows describe the route, not an interface: the hipfire
+ * 0.4.3 benchmarks page, "Read this before comparing columns" (the MoE
+ * prefill route is "per-expert buffers" or "symmetric IU4 MoE", prompts are
+ * processed in row chunks of 8192) and "Known limits" (symmetric vs
+ * asymmetric 4-bit expert files). Everything below the method level (the
+ * router form, the nibble layout, the group size) is this library's
+ * definition, stated per argument.
+ *
+ * Conventions for every call:
+ *  - Tensors are row-major, little-endian, densely packed. bf16 and fp16
+ *    values travel as uint16_t bit patterns.
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent),
+ *    owned by the caller, 16-byte aligned, and must stay valid until the
+ *    enqueued work has finished. The library never allocates or frees device
+ *    memory on the call path and keeps no state between calls (except the
+ *    optional profiling pool, see moe_profile_*).
+ *  - Calls only enqueue work on `stream` (NULL = the default stream) and
+ *    return; faults inside kernels surface at the caller's next
+ *    synchronization.
+ *  - Validation happens on the host before anything is launched. On a non-OK
+ *    status nothing was launched and no output was touched; moe_last_error()
+ *    describes the problem. T == 0 is a valid no-op that returns MOE_OK.
+ *  - No output may alias an input, except that moe_combine's and
+ *    moe_layer_forward's `out` may alias `residual`.
+ *  - No C++ exception crosses this interface. Calls on different streams
+ *    with disjoint buffers may run concurrently.
+ *
+ * Supported shapes (MOE_ERR_UNSUPPORTED otherwise):
+ *    hidden H % 128 == 0, 128 <= H <= 16384;  1 <= E <= 256;  1 <= k <= min(E, 8);
+ *    group_size G in {32, 64, 128};  H % G == 0;  inter I % 64 == 0 and I % G == 0;
+ *    shared_inter == 0 or (shared_inter % 64 == 0 and shared_inter % G == 0);
+ *    T * k < 2^31.
+ */
+#ifndef QMOE_MOE_H
+#define QMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null/negative/mismatched argument */
+  MOE_ERR_UNSUPPORTED = 2,        /* legal but not implemented (shape, G, alignment) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} moe_status_t;
+
+/* 4-bit formats. Two weights per byte: byte j of a row holds element 2j in
+ * bits 0-3 and element 2j+1 in bits 4-7. A group of G consecutive elements
+ * along K (the input dimension) of one row shares one fp16 scale (and min).
+ *   MOE_Q4_SYM : w = (nibble - 8) * scale          (all 16 codes decode)
+ *   MOE_Q4_ASYM: w = nibble * scale + min                                     */
+typedef enum { MOE_Q4_SYM = 0, MOE_Q4_ASYM = 1 } moe_quant_t;
+
+typedef struct {
+  int64_t hidden;        /* H */
+  int64_t num_experts;   /* E routed experts */
+  int64_t top_k;         /* k experts per token */
+  int64_t inter;         /* I, routed expert intermediate size */
+  int64_t group_size;    /* G, quantization group along K */
+  int32_t quant;         /* moe_quant_t */
+  int32_t reserved;      /* must be 0 */
+  int64_t shared_inter;  /* I_s of the always-on shared expert; 0 = none */
+} moe_shape_t;
+
+/* Expert weights (device pointers, read only). For MOE_Q4_SYM every *_min
+ * must be NULL; for MOE_Q4_ASYM every *_min of a present matrix is required.
+ * The shared-expert pointers are NULL iff shape.shared_inter == 0. */
+typedef struct {
+  const uint8_t  *w13;        /* [E][2I][H/2]: rows 0..I-1 gate, I..2I-1 up  */
+  const uint16_t *w13_scale;  /* fp16 [E][2I][H/G]                           */
+  const uint16_t *w13_min;    /* fp16 [E][2I][H/G] or NULL                   */
+  const uint8_t  *w2;         /* [E][H][I/2]: down projection                */
+  const uint16_t *w2_scale;   /* fp16 [E][H][I/G]                            */
+  const uint16_t *w2_min;     /* fp16 [E][H][I/G] or NULL                    */
+  const uint8_t  *s13;        /* shared expert [2I_s][H/2]                   */
+  const uint16_t *s13_scale;  /* fp16 [2I_s][H/G]                            */
+  const uint16_t *s13_min;
+  const uint8_t  *s2;         /* shared expert [H][I_s/2]                    */
+  const uint16_t *s2_scale;   /* fp16 [H][I_s/G]                             */
+  const uint16_t *s2_min;
+} moe_experts_t;
+
+/* Which call a workspace is sized for. Any call accepts a workspace of the
+ * MOE_WS_LAYER size for the same shape and T. */
+typedef enum {
+  MOE_WS_LAYER = 0,       /* moe_layer_forward */
+  MOE_WS_ROUTE = 1,       /* moe_route */
+  MOE_WS_PERMUTE = 2,     /* moe_permute */
+  MOE_WS_EXPERT_FFN = 3   /* moe_expert_ffn */
+} moe_ws_kind_t;
+
+int moe_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *moe_last_error(void);
+
+/* Bytes of device workspace a call needs for this shape and T (host only,
+ * launches nothing). */
+moe_status_t moe_workspace_size(const moe_shape_t *shape, int64_t T, int32_t kind,
+                                size_t *bytes);
+
+/* Router: L[t,e] = sum_h x[t,h] * w_router[e,h] (+ router_bias[e]), fp32;
+ * ids[t] = the k experts with the largest L (largest first; equal logits
+ * ordered by ascending expert index; -0.0 == +0.0; inputs must be finite);
+ * topk_w[t,j] = exp(L_j - L_max) / sum over the k chosen of exp(L_i - L_max).
+ * If shared_gate is given, shared_w[t] = 1 / (1 + exp(-(x[t] . shared_gate))).
+ * The dot products are formed from exact products of the bf16 activations
+ * with an exact three-term bf16 split of each fp32 router weight, summed in
+ * fp32 on the matrix cores (an fp32 GEMM to within its usual error bound).
+ *   x           [T][H] bf16          w_router [E][H] fp32
+ *   router_bias [E] fp32 or NULL     shared_gate [H] fp32 or NULL
+ *   logits      [T][E] fp32 or NULL: receives the (biased) logits used for selection
+ *   topk_ids    [T][k] int32         topk_w [T][k] fp32
+ *   shared_w    [T] fp32, required iff shared_gate != NULL
+ *   ws          >= moe_workspace_size(MOE_WS_ROUTE) bytes of scratch        */
+moe_status_t moe_route(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                       const float *w_router, const float *router_bias,
+                       const float *shared_gate, float *logits, int32_t *topk_ids,
+                       float *topk_w, float *shared_w, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Expert grouping of the P = T*k pairs, pair p = t*k + j:
+ *   counts[e]      number of pairs routed to expert e            [E] int32
+ *   offsets[e]     exclusive prefix sum of counts                [E+1] int32
+ *   sorted_pairs   expert by expert, that expert's pairs in ascending p  [P] int32
+ *   inv[p]         position of pair p in sorted_pairs            [P] int32
+ * topk_ids entries must lie in [0, E). Deterministic (no atomics). ws may be
+ * NULL when moe_workspace_size(MOE_WS_PERMUTE) is 0. */
+moe_status_t moe_permute(const moe_shape_t *shape, int64_t T, const int32_t *topk_ids,
+                         int32_t *counts, int32_t *offsets, int32_t *sorted_pairs,
+                         int32_t *inv, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFNs. Row r of expert e (offsets[e] <= r < offsets[e+1]) is token
+ * sorted_pairs[r] / k; it is multiplied by the dequantized expert weights:
+ *   h = silu(x W_gate^T) * (x W_up^T),  silu(z) = z / (1 + exp(-z))
+ *   y_perm[r] = h W_down^T                       (unweighted, fp16 [P][H])
+ * The shared expert (if present) runs the same FFN on every token into
+ * y_shared [T][H] fp16 (required iff shape.shared_inter > 0).
+ * Numerics: activations are converted exactly to fp16 (|x| must be below
+ * 65504; magnitudes under 2^-14 keep fewer bits), weights are dequantized in
+ * registers to fp16 (q * scale, or q * scale + min, rounded once), both
+ * products run on the fp16 matrix cores with fp32 accumulation, and h is
+ * rounded to fp16 between them. counts/offsets/sorted_pairs are
+ * moe_permute's outputs. */
+moe_status_t moe_expert_ffn(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                            const moe_experts_t *experts, const int32_t *counts,
+                            const int32_t *offsets, const int32_t *sorted_pairs,
+                            uint16_t *y_perm, uint16_t *y_shared, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* out[t] = bf16( sum_j topk_w[t,j] * y_perm[inv[t*k+j]]
+ *                (+ shared_w[t] * y_shared[t]) (+ residual[t]) ), fp32 sums.
+ * y_perm [P][H] and y_shared [T][H] are fp16 (moe_expert_ffn's outputs);
+ * y_shared and shared_w go together (both NULL or both set); residual
+ * [T][H] bf16 may be NULL and may alias out; out [T][H] bf16. */
+moe_status_t moe_combine(const moe_shape_t *shape, int64_t T, const uint16_t *y_perm,
+                         const int32_t *inv, const float *topk_w, const uint16_t *y_shared,
+                         const float *shared_w, const uint16_t *residual, uint16_t *out,
+                         hipStream_t stream);
+
+/* The whole layer: route -> permute -> experts -> combine, all on `stream`,
+ * with every intermediate in ws (>= moe_workspace_size(MOE_WS_LAYER)).
+ * x [T][H] bf16 (|x| < 65504, see moe_expert_ffn), out [T][H] bf16.
+ * shared_gate is required iff shape.shared_inter > 0. residual may be NULL
+ * and may alias out. No device-to-host transfer happens. */
+moe_status_t moe_layer_forward(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                               const float *w_router, const float *router_bias,
+                               const float *shared_gate, const moe_experts_t *experts,
+                               const uint16_t *residual, uint16_t *out, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* RMSNorm over rows of [T][H] bf16:
+ *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )
+ * computed in fp32; weight [H] fp32. out must not alias x. */
+moe_status_t moe_rmsnorm(int64_t T, int64_t H, const uint16_t *x, const float *weight,
+                         float eps, uint16_t *out, hipStream_t stream);
+
+/* Optional kernel timing. While enabled, the library brackets each of its
+ * kernel launches with HIP events recorded on the launch stream (a pool of
+ * `max_launches` event pairs is created by moe_profile_enable; this is the
+ * only allocation the library ever makes, and it happens outside the call
+ * path). moe_profile_read synchronizes on the recorded events and returns,
+ * for the kernel named `kernel`, the number of recorded launches and their
+ * summed duration in milliseconds. moe_profile_enable(0) frees the pool. */
+moe_status_t moe_profile_enable(int32_t max_launches);
+moe_status_t moe_profile_reset(void);
+moe_status_t moe_profile_read(const char *kernel, int64_t *launches, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_MOE_H */

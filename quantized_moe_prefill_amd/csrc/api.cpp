@@ -1,0 +1,543 @@
+// C ABI of the MoE prefill library: host-side validation, workspace layout,
+// kernel sequencing on the caller's stream, error reporting and optional
+// per-kernel event timing. See include/moe.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace qmoe {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+
+static thread_local char g_err[512] = "";
+
+static moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static moe_status_t hip_fail(const char* what, hipError_t e) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// profiling pool (events around each launch, only while enabled)
+// ---------------------------------------------------------------------------
+
+struct ProfRecord {
+  const char* name;
+  int slot;
+};
+
+static std::mutex g_prof_mu;
+static std::vector<hipEvent_t> g_prof_events;  // 2 per slot
+static std::vector<ProfRecord> g_prof_records;
+static int g_prof_slots = 0;
+static int g_prof_next = 0;
+
+LaunchScope::LaunchScope(const char* n, hipStream_t s) : name(n), stream(s), slot(-1) {
+  if (g_prof_slots == 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_slots == 0 || g_prof_next >= g_prof_slots) return;
+  slot = g_prof_next++;
+  (void)hipEventRecord(g_prof_events[2 * slot], stream);
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof_events[2 * slot + 1], stream);
+  g_prof_records.push_back({name, slot});
+}
+
+// ---------------------------------------------------------------------------
+// shapes and workspace
+// ---------------------------------------------------------------------------
+
+struct Shape {
+  int H, E, k, I, G, Is;
+  bool asym;
+};
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
+  if (s == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %lld)", (long long)T);
+  if (s->hidden <= 0 || s->num_experts <= 0 || s->top_k <= 0 || s->inter <= 0 ||
+      s->group_size <= 0 || s->shared_inter < 0 || s->reserved != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shape fields must be positive (reserved must be 0)");
+  if (s->quant != MOE_Q4_SYM && s->quant != MOE_Q4_ASYM)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "quant must be MOE_Q4_SYM or MOE_Q4_ASYM");
+  if (s->top_k > s->num_experts)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "top_k (%lld) > num_experts (%lld)",
+                (long long)s->top_k, (long long)s->num_experts);
+  const int64_t G = s->group_size;
+  if (G != 32 && G != 64 && G != 128)
+    return fail(MOE_ERR_UNSUPPORTED, "group_size must be 32, 64 or 128 (got %lld)", (long long)G);
+  if (s->hidden % 128 != 0 || s->hidden > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of 128 and <= 16384");
+  if (s->hidden % G != 0) return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of G");
+  if (s->inter % 64 != 0 || s->inter % G != 0 || s->inter > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "inter must be a multiple of 64 and of G");
+  if (s->shared_inter != 0 && (s->shared_inter % 64 != 0 || s->shared_inter % G != 0 ||
+                               s->shared_inter > 65536))
+    return fail(MOE_ERR_UNSUPPORTED, "shared_inter must be 0 or a multiple of 64 and of G");
+  if (s->num_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "num_experts must be <= 256");
+  if (s->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 8");
+  if (T * s->top_k >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * top_k must be < 2^31");
+  out->H = (int)s->hidden;
+  out->E = (int)s->num_experts;
+  out->k = (int)s->top_k;
+  out->I = (int)s->inter;
+  out->G = (int)G;
+  out->Is = (int)s->shared_inter;
+  out->asym = s->quant == MOE_Q4_ASYM;
+  return MOE_OK;
+}
+
+static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t split, ids, tw, sw, counts, offsets, sorted, inv, x16, h, hs, yperm, ysh, total;
+};
+
+// Carve-up of the layer workspace. Each region is 256-byte aligned.
+static Layout layer_layout(const Shape& s, int64_t T) {
+  Layout L{};
+  const size_t P = (size_t)T * s.k;
+  size_t o = 0;
+  L.split = o;   o = al(o + router_split_bytes(s.E, s.Is > 0, s.H));
+  L.ids = o;     o = al(o + P * 4);
+  L.tw = o;      o = al(o + P * 4);
+  L.sw = o;      o = al(o + (size_t)T * 4);
+  L.counts = o;  o = al(o + (size_t)s.E * 4);
+  L.offsets = o; o = al(o + (size_t)(s.E + 1) * 4);
+  L.sorted = o;  o = al(o + P * 4);
+  L.inv = o;     o = al(o + P * 4);
+  L.x16 = o;     o = al(o + (size_t)T * s.H * 2);
+  L.h = o;       o = al(o + P * s.I * 2);
+  L.hs = o;      o = al(o + (size_t)T * s.Is * 2);
+  L.yperm = o;   o = al(o + P * s.H * 2);
+  L.ysh = o;     o = al(o + (size_t)T * (s.Is > 0 ? s.H : 0) * 2);
+  L.total = o;
+  return L;
+}
+
+static size_t route_ws(const Shape& s) { return al(router_split_bytes(s.E, s.Is > 0, s.H)); }
+// moe_expert_ffn scratch: fp16 activations, h, shared h.
+static size_t ffn_ws(const Shape& s, int64_t T) {
+  const size_t P = (size_t)T * s.k;
+  return al((size_t)T * s.H * 2) + al(P * s.I * 2) + al((size_t)T * s.Is * 2);
+}
+
+static moe_status_t check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(ws)) return fail(MOE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (have < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", have, need);
+  return MOE_OK;
+}
+
+#define QMOE_REQUIRE(p, what)                                                   \
+  do {                                                                          \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "%s is NULL", what); \
+    if (!aligned16(p)) return fail(MOE_ERR_UNSUPPORTED, "%s must be 16-byte aligned", what); \
+  } while (0)
+#define QMOE_OPTIONAL(p, what)                                                  \
+  do {                                                                          \
+    if ((p) != nullptr && !aligned16(p))                                        \
+      return fail(MOE_ERR_UNSUPPORTED, "%s must be 16-byte aligned", what);     \
+  } while (0)
+#define QMOE_HIP(call, what)                                                    \
+  do {                                                                          \
+    hipError_t e_ = (call);                                                     \
+    if (e_ != hipSuccess) return hip_fail(what, e_);                            \
+  } while (0)
+
+static moe_status_t check_experts(const Shape& s, const moe_experts_t* w) {
+  if (w == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "experts is NULL");
+  QMOE_REQUIRE(w->w13, "experts->w13");
+  QMOE_REQUIRE(w->w13_scale, "experts->w13_scale");
+  QMOE_REQUIRE(w->w2, "experts->w2");
+  QMOE_REQUIRE(w->w2_scale, "experts->w2_scale");
+  if (s.asym) {
+    QMOE_REQUIRE(w->w13_min, "experts->w13_min");
+    QMOE_REQUIRE(w->w2_min, "experts->w2_min");
+  } else if (w->w13_min != nullptr || w->w2_min != nullptr || w->s13_min != nullptr ||
+             w->s2_min != nullptr) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "min tensors must be NULL for MOE_Q4_SYM");
+  }
+  if (s.Is > 0) {
+    QMOE_REQUIRE(w->s13, "experts->s13");
+    QMOE_REQUIRE(w->s13_scale, "experts->s13_scale");
+    QMOE_REQUIRE(w->s2, "experts->s2");
+    QMOE_REQUIRE(w->s2_scale, "experts->s2_scale");
+    if (s.asym) {
+      QMOE_REQUIRE(w->s13_min, "experts->s13_min");
+      QMOE_REQUIRE(w->s2_min, "experts->s2_min");
+    }
+  } else if (w->s13 != nullptr || w->s2 != nullptr) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared-expert weights given but shared_inter == 0");
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// implementations (arguments already validated)
+// ---------------------------------------------------------------------------
+
+static moe_status_t route_impl(const Shape& s, int64_t T, const uint16_t* x, const float* wr,
+                               const float* bias, const float* sg, float* logits,
+                               int32_t* ids, float* tw, float* sw, uint16_t* split,
+                               hipStream_t st) {
+  QMOE_HIP(launch_router_split(wr, sg, s.E, s.H, split, st), "router_split launch");
+  QMOE_HIP(launch_router_topk(x, split, bias, (int)T, s.H, s.E, s.k, sg != nullptr, logits, ids,
+                              tw, sw, st),
+           "router_topk launch");
+  return MOE_OK;
+}
+
+static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
+                             const moe_experts_t* w, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* sorted, uint16_t* yperm,
+                             uint16_t* ysh, uint16_t* x16, uint16_t* h, uint16_t* hs,
+                             hipStream_t st) {
+  const int P = (int)(T * s.k);
+  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+  GroupedGemm g{};
+  g.A = x16;
+  g.gather = sorted;
+  g.gather_div = s.k;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.E = s.E;
+  g.max_rows = P;
+  g.W = w->w13;
+  g.Wscale = w->w13_scale;
+  g.Wmin = s.asym ? w->w13_min : nullptr;
+  g.N = 2 * s.I;
+  g.K = s.H;
+  g.G = s.G;
+  g.C = h;
+  g.ldc = s.I;
+  QMOE_HIP(launch_gateup(g, st), "gateup launch");
+
+  GroupedGemm d = g;
+  d.A = h;
+  d.gather = nullptr;
+  d.W = w->w2;
+  d.Wscale = w->w2_scale;
+  d.Wmin = s.asym ? w->w2_min : nullptr;
+  d.N = s.H;
+  d.K = s.I;
+  d.C = yperm;
+  d.ldc = s.H;
+  QMOE_HIP(launch_down(d, st), "down launch");
+
+  if (s.Is > 0) {
+    GroupedGemm gs{};
+    gs.A = x16;
+    gs.gather = nullptr;
+    gs.gather_div = 1;
+    gs.counts = nullptr;
+    gs.offsets = nullptr;
+    gs.rows_single = (int)T;
+    gs.E = 1;
+    gs.max_rows = (int)T;
+    gs.W = w->s13;
+    gs.Wscale = w->s13_scale;
+    gs.Wmin = s.asym ? w->s13_min : nullptr;
+    gs.N = 2 * s.Is;
+    gs.K = s.H;
+    gs.G = s.G;
+    gs.C = hs;
+    gs.ldc = s.Is;
+    QMOE_HIP(launch_gateup(gs, st, "shared_gateup_gemm"), "shared gateup launch");
+    GroupedGemm ds = gs;
+    ds.A = hs;
+    ds.W = w->s2;
+    ds.Wscale = w->s2_scale;
+    ds.Wmin = s.asym ? w->s2_min : nullptr;
+    ds.N = s.H;
+    ds.K = s.Is;
+    ds.C = ysh;
+    ds.ldc = s.H;
+    QMOE_HIP(launch_down(ds, st, "shared_down_gemm"), "shared down launch");
+  }
+  return MOE_OK;
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+// ---------------------------------------------------------------------------
+// exported C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status_t moe_workspace_size(const moe_shape_t* shape, int64_t T, int32_t kind,
+                                size_t* bytes) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  switch (kind) {
+    case MOE_WS_LAYER: *bytes = layer_layout(s, T).total; break;
+    case MOE_WS_ROUTE: *bytes = route_ws(s); break;
+    case MOE_WS_PERMUTE: *bytes = 0; break;
+    case MOE_WS_EXPERT_FFN: *bytes = ffn_ws(s, T); break;
+    default: return fail(MOE_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", kind);
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                       const float* w_router, const float* router_bias,
+                       const float* shared_gate, float* logits, int32_t* topk_ids,
+                       float* topk_w, float* shared_w, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(topk_ids, "topk_ids");
+  QMOE_REQUIRE(topk_w, "topk_w");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(shared_gate, "shared_gate");
+  QMOE_OPTIONAL(logits, "logits");
+  if ((shared_gate == nullptr) != (shared_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate and shared_w go together");
+  QMOE_OPTIONAL(shared_w, "shared_w");
+  // the router pads for a shared-gate row whenever the shape has a shared expert
+  Shape sr = s;
+  sr.Is = shared_gate != nullptr ? 1 : 0;
+  st = check_ws(ws, ws_bytes, route_ws(sr));
+  if (st != MOE_OK) return st;
+  return route_impl(s, T, x, w_router, router_bias, shared_gate, logits, topk_ids, topk_w,
+                    shared_w, static_cast<uint16_t*>(ws), stream);
+}
+
+moe_status_t moe_permute(const moe_shape_t* shape, int64_t T, const int32_t* topk_ids,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                         int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  QMOE_REQUIRE(counts, "counts");
+  QMOE_REQUIRE(offsets, "offsets");
+  if (T == 0) {
+    // counts/offsets of an empty batch are all zero; written by a kernel so
+    // that the call stays asynchronous
+    QMOE_HIP(launch_permute(topk_ids, 0, s.E, counts, offsets, sorted_pairs, inv, stream),
+             "permute launch");
+    return MOE_OK;
+  }
+  QMOE_REQUIRE(topk_ids, "topk_ids");
+  QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
+  QMOE_REQUIRE(inv, "inv");
+  QMOE_HIP(launch_permute(topk_ids, (int)(T * s.k), s.E, counts, offsets, sorted_pairs, inv,
+                          stream),
+           "permute launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                            const moe_experts_t* experts, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* sorted_pairs,
+                            uint16_t* y_perm, uint16_t* y_shared, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  st = check_experts(s, experts);
+  if (st != MOE_OK) return st;
+  QMOE_REQUIRE(counts, "counts");
+  QMOE_REQUIRE(offsets, "offsets");
+  QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
+  QMOE_REQUIRE(y_perm, "y_perm");
+  if (s.Is > 0) {
+    QMOE_REQUIRE(y_shared, "y_shared");
+  } else if (y_shared != nullptr) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "y_shared given but shared_inter == 0");
+  }
+  st = check_ws(ws, ws_bytes, ffn_ws(s, T));
+  if (st != MOE_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t P = (size_t)T * s.k;
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2));
+  uint16_t* hs = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2) + al(P * s.I * 2));
+  return ffn_impl(s, T, x, experts, counts, offsets, sorted_pairs, y_perm, y_shared, x16, h,
+                  hs, stream);
+}
+
+moe_status_t moe_combine(const moe_shape_t* shape, int64_t T, const uint16_t* y_perm,
+                         const int32_t* inv, const float* topk_w, const uint16_t* y_shared,
+                         const float* shared_w, const uint16_t* residual, uint16_t* out,
+                         hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(y_perm, "y_perm");
+  QMOE_REQUIRE(inv, "inv");
+  QMOE_REQUIRE(topk_w, "topk_w");
+  QMOE_REQUIRE(out, "out");
+  QMOE_OPTIONAL(y_shared, "y_shared");
+  QMOE_OPTIONAL(residual, "residual");
+  if ((y_shared == nullptr) != (shared_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "y_shared and shared_w go together");
+  QMOE_HIP(launch_combine(y_perm, inv, topk_w, y_shared, shared_w, residual, out, (int)T, s.H,
+                          s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                               const float* w_router, const float* router_bias,
+                               const float* shared_gate, const moe_experts_t* experts,
+                               const uint16_t* residual, uint16_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(out, "out");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(residual, "residual");
+  st = check_experts(s, experts);
+  if (st != MOE_OK) return st;
+  if (s.Is > 0) {
+    QMOE_REQUIRE(shared_gate, "shared_gate");
+  } else if (shared_gate != nullptr) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate given but shared_inter == 0");
+  }
+  const Layout L = layer_layout(s, T);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  auto* split = reinterpret_cast<uint16_t*>(b + L.split);
+  auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
+  auto* tw = reinterpret_cast<float*>(b + L.tw);
+  auto* sw = s.Is > 0 ? reinterpret_cast<float*>(b + L.sw) : nullptr;
+  auto* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  auto* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  auto* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  auto* x16 = reinterpret_cast<uint16_t*>(b + L.x16);
+  auto* h = reinterpret_cast<uint16_t*>(b + L.h);
+  auto* hs = reinterpret_cast<uint16_t*>(b + L.hs);
+  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
+  auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
+
+  st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
+                  stream);
+  if (st != MOE_OK) return st;
+  QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, stream),
+           "permute launch");
+  st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs, stream);
+  if (st != MOE_OK) return st;
+  QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_rmsnorm(int64_t T, int64_t H, const uint16_t* x, const float* weight, float eps,
+                         uint16_t* out, hipStream_t stream) {
+  if (T < 0 || H <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 and H > 0");
+  if (H % 8 != 0 || H > 65536) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 8");
+  if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(weight, "weight");
+  QMOE_REQUIRE(out, "out");
+  if (x == out) return fail(MOE_ERR_INVALID_ARGUMENT, "out must not alias x");
+  QMOE_HIP(launch_rmsnorm(x, weight, eps, out, (int)T, (int)H, stream), "rmsnorm launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_profile_enable(int32_t max_launches) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (hipEvent_t ev : g_prof_events) (void)hipEventDestroy(ev);
+  g_prof_events.clear();
+  g_prof_records.clear();
+  g_prof_slots = 0;
+  g_prof_next = 0;
+  if (max_launches < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "max_launches must be >= 0");
+  if (max_launches == 0) return MOE_OK;
+  g_prof_events.resize(2 * (size_t)max_launches, nullptr);
+  for (auto& ev : g_prof_events) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      for (hipEvent_t x : g_prof_events)
+        if (x) (void)hipEventDestroy(x);
+      g_prof_events.clear();
+      return hip_fail("hipEventCreate", e);
+    }
+  }
+  g_prof_records.reserve(max_launches);
+  g_prof_slots = max_launches;
+  return MOE_OK;
+}
+
+moe_status_t moe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_records.clear();
+  g_prof_next = 0;
+  return MOE_OK;
+}
+
+moe_status_t moe_profile_read(const char* kernel, int64_t* launches, double* total_ms) {
+  if (kernel == nullptr || launches == nullptr || total_ms == nullptr)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int64_t n = 0;
+  double ms = 0.0;
+  for (const ProfRecord& r : g_prof_records) {
+    if (std::strcmp(r.name, kernel) != 0) continue;
+    hipEvent_t a = g_prof_events[2 * r.slot], b = g_prof_events[2 * r.slot + 1];
+    hipError_t e = hipEventSynchronize(b);
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, a, b);
+    if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return MOE_OK;
+}
+
+}  // extern "C"

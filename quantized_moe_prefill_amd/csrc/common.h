@@ -1,0 +1,92 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of the MoE prefill
+// library: vector types for the bf16 matrix-core instructions, bit-pattern
+// conversions, and wave-level reductions for 64-wide wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Low / high bf16 of a packed pair.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// Low / high fp16 of a packed pair.
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+// Two fp32 -> packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// D = A(16x32) * B(32x16) + C on the bf16 matrix cores, fp32 accumulation.
+// Operand layout per lane l: A row l%16 / B column l%16, eight consecutive K
+// values starting at 8*(l/16). Result: lane l holds rows 4*(l/16)+0..3 of
+// column l%16. (The K order inside an operand only has to agree between A
+// and B, which it does by construction.)
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Same shape and operand layout on fp16 operands.
+__device__ __forceinline__ f32x4 mfma_16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// K order of the fp16 expert operands. Unpacking a 32-bit word of eight
+// nibbles as (w >> 4i) & 0x000F000F yields element pairs (i, i+4), so every
+// 8-element chunk of an fp16 operand holds its elements in the order
+// 0,4,1,5,2,6,3,7. Activations (and h) are stored in that order too, so both
+// matrix-core operands agree; position p of a chunk holds element kperm(p),
+// and element i sits at position kpos(i).
+__host__ __device__ constexpr inline int kperm(int p) { return (p >> 1) + 4 * (p & 1); }
+__host__ __device__ constexpr inline int kpos(int i) { return 2 * (i & 3) + (i >> 2); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace qmoe

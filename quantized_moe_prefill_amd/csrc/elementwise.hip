@@ -1,0 +1,110 @@
+// Combine (weighted unpermute) and RMSNorm for the MoE prefill layer on
+// gfx950. Both are HBM-bound row operations: each thread owns 8 consecutive
+// bf16 channels (one 16-byte load/store), consecutive threads cover
+// consecutive channels of a row, so every row is read and written with
+// fully coalesced 16-byte accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace qmoe {
+
+namespace {
+
+__device__ __forceinline__ void acc8_bf16(float* a, u32x4 v, float w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = fmaf(w, bf16lo(v[i]), a[2 * i]);
+    a[2 * i + 1] = fmaf(w, bf16hi(v[i]), a[2 * i + 1]);
+  }
+}
+__device__ __forceinline__ void acc8_f16(float* a, u32x4 v, float w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = fmaf(w, f16lo(v[i]), a[2 * i]);
+    a[2 * i + 1] = fmaf(w, f16hi(v[i]), a[2 * i + 1]);
+  }
+}
+
+// out[t] = sum_j w[t,j] y_perm[inv[t*k+j]] (+ sw[t] y_sh[t]) (+ res[t]);
+// y_perm and y_sh are fp16, res and out bf16.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const uint16_t* __restrict__ yperm, const int32_t* __restrict__ inv,
+    const float* __restrict__ tw, const uint16_t* __restrict__ ysh,
+    const float* __restrict__ sw, const uint16_t* res, uint16_t* out, int T, int H, int k) {
+  const int cpr = H / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)T * cpr) return;
+  const int t = (int)(idx / cpr);
+  const int c = (int)(idx - (int64_t)t * cpr) * 8;
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t p = (int64_t)t * k + j;
+    const int r = inv[p];
+    acc8_f16(a, ld16(yperm + (int64_t)r * H + c), tw[p]);
+  }
+  if (ysh != nullptr) acc8_f16(a, ld16(ysh + (int64_t)t * H + c), sw[t]);
+  if (res != nullptr) acc8_bf16(a, ld16(res + (int64_t)t * H + c), 1.f);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
+  st16(out + (int64_t)t * H + c, o);
+}
+
+// One wave per row.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ w, float eps,
+                                                     uint16_t* __restrict__ out, int T, int H) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const uint16_t* xr = x + (int64_t)row * H;
+  float ss = 0.f;
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = ld16(xr + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l = bf16lo(v[i]), h = bf16hi(v[i]);
+      ss = fmaf(l, l, ss);
+      ss = fmaf(h, h, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)H + eps);
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = ld16(xr + c);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l = bf16lo(v[i]) * r * w[c + 2 * i];
+      const float h = bf16hi(v[i]) * r * w[c + 2 * i + 1];
+      o[i] = pack_bf16x2(l, h);
+    }
+    st16(out + (int64_t)row * H + c, o);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const float* topk_w,
+                          const uint16_t* y_shared, const float* shared_w,
+                          const uint16_t* residual, uint16_t* out, int T, int H, int k,
+                          hipStream_t s) {
+  const int64_t n = (int64_t)T * (H / 8);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  LaunchScope ls("combine", s);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y_perm, inv, topk_w, y_shared, shared_w,
+                     residual, out, T, H, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* out, int T,
+                          int H, hipStream_t s) {
+  const dim3 grid(cdiv(T, 4)), block(256);
+  LaunchScope ls("rmsnorm", s);
+  hipLaunchKernelGGL(rmsnorm_kernel, grid, block, 0, s, x, w, eps, out, T, H);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels. Each returns the HIP error of
+// its launch(es); argument validation happens in the C ABI layer (api.cpp)
+// before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// Hook used by the launchers to bracket each kernel with profiling events.
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  const char* name;
+  hipStream_t stream;
+  int slot;
+};
+
+// ---- router -----------------------------------------------------------
+// Rows of the router matrix padded to a multiple of 16: E routed rows, then
+// the shared-gate row (if any), then zeros.
+int router_padded_rows(int E, bool has_shared);
+size_t router_split_bytes(int E, bool has_shared, int H);
+hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
+                               uint16_t* split, hipStream_t s);
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, const float* bias, int T,
+                              int H, int E, int k, bool has_shared, float* logits, int32_t* ids,
+                              float* topk_w, float* shared_w, hipStream_t s);
+
+// ---- permutation ------------------------------------------------------
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* inv, hipStream_t s);
+
+// ---- grouped expert GEMMs --------------------------------------------
+// bf16 [n] (n % 8 == 0) -> fp16 in the kperm chunk order of the expert GEMMs.
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStream_t s);
+
+struct GroupedGemm {
+  const uint16_t* A;       // fp16 activation rows, kperm chunk order
+  const int32_t* gather;   // row r -> A row gather[r] / gather_div ; NULL: A row r
+  int gather_div;
+  const int32_t* counts;   // [E] rows per group; NULL: one group of rows_single rows
+  const int32_t* offsets;  // [E+1] first row of each group
+  int rows_single;
+  int E;
+  int max_rows;            // upper bound of all rows (sizes the grid)
+  const uint8_t* W;        // [E][N][K/2] packed nibbles
+  const uint16_t* Wscale;  // fp16 [E][N][K/G]
+  const uint16_t* Wmin;    // fp16 [E][N][K/G] or NULL (symmetric)
+  int N, K, G;
+  uint16_t* C;             // output rows, fp16, leading dimension ldc
+  int ldc;
+};
+// gate/up with fused SwiGLU: N = 2I weight rows, writes h = silu(g)*u
+// (fp16, kperm chunk order), ldc = I.
+hipError_t launch_gateup(const GroupedGemm& g, hipStream_t s, const char* name = "gateup_gemm");
+// down projection: N = H weight rows, writes y (fp16, natural order), ldc = H.
+hipError_t launch_down(const GroupedGemm& g, hipStream_t s, const char* name = "down_gemm");
+
+// ---- combine / norm ---------------------------------------------------
+hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const float* topk_w,
+                          const uint16_t* y_shared, const float* shared_w,
+                          const uint16_t* residual, uint16_t* out, int T, int H, int k,
+                          hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* out, int T,
+                          int H, hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,206 @@
+"""Python binding of the C ABI (include/moe.h), one function per entry point.
+
+Argument marshalling only: each function checks dtypes, devices and
+contiguity, allocates outputs and the workspace with torch (device memory is
+the only thing torch provides here), and passes raw device pointers and
+torch's current HIP stream to the library. Every step of the computation
+runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _native as N
+
+_U16 = (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
+
+
+def make_shape(H: int, E: int, k: int, I: int, G: int, quant: str, shared_I: int = 0) -> N.MoeShape:
+    q = {"sym": N.MOE_Q4_SYM, "asym": N.MOE_Q4_ASYM}[quant]
+    return N.MoeShape(H, E, k, I, G, q, 0, shared_I)
+
+
+def shape_of(cfg) -> N.MoeShape:
+    """Shape struct of a synth.MoEConfig."""
+    return make_shape(cfg.H, cfg.E, cfg.k, cfg.I, cfg.G, cfg.quant, cfg.shared_I)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None, device=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Experts:
+    """Packed expert weights of one layer as the C struct (keeps the tensors
+    alive). Accepts any object with the attribute names of synth.LayerInputs."""
+
+    def __init__(self, li):
+        u8 = (torch.uint8,)
+        names = ["w13", "w13_scale", "w13_min", "w2", "w2_scale", "w2_min",
+                 "s13", "s13_scale", "s13_min", "s2", "s2_scale", "s2_min"]
+        self.tensors = {n: getattr(li, n, None) for n in names}
+        vals = []
+        for n in names:
+            t = self.tensors[n]
+            dt = u8 if n in ("w13", "w2", "s13", "s2") else _U16
+            vals.append(_ptr(t, n, dt))
+        self.struct = N.MoeExperts(*vals)
+        self.device = self.tensors["w13"].device
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def moe_workspace_size(shape: N.MoeShape, T: int, kind: int = N.MOE_WS_LAYER) -> int:
+    n = ctypes.c_size_t(0)
+    N.check(N.lib().moe_workspace_size(ctypes.byref(shape), int(T), int(kind), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(shape: N.MoeShape, T: int, device, kind: int = N.MOE_WS_LAYER) -> torch.Tensor:
+    n = moe_workspace_size(shape, T, kind)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(shape, x, w_router, router_bias=None, shared_gate=None, want_logits=False,
+              ws=None):
+    T = x.shape[0]
+    dev = x.device
+    E, k = shape.num_experts, shape.top_k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    sw = torch.empty((T,), dtype=torch.float32, device=dev) if shared_gate is not None else None
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_ROUTE)
+    N.check(N.lib().moe_route(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev),
+        _ptr(shared_gate, "shared_gate", (torch.float32,), dev), _ptr(logits, "logits"),
+        _ptr(ids, "ids"), _ptr(tw, "tw"), _ptr(sw, "sw"), _ptr(ws, "ws"), ws.numel(), _stream(dev)))
+    return logits, ids, tw, sw
+
+
+def moe_permute(shape, topk_ids):
+    T = topk_ids.shape[0]
+    dev = topk_ids.device
+    E, k = shape.num_experts, shape.top_k
+    P = T * k
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    sp = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
+    inv = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
+    N.check(N.lib().moe_permute(
+        ctypes.byref(shape), T, _ptr(topk_ids, "topk_ids", (torch.int32,), dev), _ptr(counts, "counts"),
+        _ptr(offsets, "offsets"), _ptr(sp, "sorted_pairs"), _ptr(inv, "inv"), None, 0, _stream(dev)))
+    return counts, offsets, sp[:P], inv[:P]
+
+
+def moe_expert_ffn(shape, x, experts: Experts, counts, offsets, sorted_pairs, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    P = T * shape.top_k
+    y_perm = torch.empty((max(P, 1), shape.hidden), dtype=torch.float16, device=dev)
+    y_sh = (torch.empty((T, shape.hidden), dtype=torch.float16, device=dev)
+            if shape.shared_inter else None)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_EXPERT_FFN)
+    N.check(N.lib().moe_expert_ffn(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), experts.ref(),
+        _ptr(counts, "counts", (torch.int32,), dev), _ptr(offsets, "offsets", (torch.int32,), dev),
+        _ptr(sorted_pairs, "sorted_pairs", (torch.int32,), dev), _ptr(y_perm, "y_perm"),
+        _ptr(y_sh, "y_shared"), _ptr(ws, "ws"), ws.numel(), _stream(dev)))
+    return y_perm[:P], y_sh
+
+
+def moe_combine(shape, y_perm, inv, topk_w, y_shared=None, shared_w=None, residual=None,
+                out=None):
+    T = topk_w.shape[0]
+    dev = topk_w.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    N.check(N.lib().moe_combine(
+        ctypes.byref(shape), T, _ptr(y_perm, "y_perm", _U16, dev), _ptr(inv, "inv", (torch.int32,), dev),
+        _ptr(topk_w, "topk_w", (torch.float32,), dev), _ptr(y_shared, "y_shared", _U16, dev),
+        _ptr(shared_w, "shared_w", (torch.float32,), dev), _ptr(residual, "residual", _U16, dev),
+        _ptr(out, "out", _U16, dev), _stream(dev)))
+    return out
+
+
+def moe_layer_forward(shape, x, w_router, router_bias, shared_gate, experts: Experts,
+                      residual=None, out=None, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_LAYER)
+    N.check(N.lib().moe_layer_forward(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev),
+        _ptr(shared_gate, "shared_gate", (torch.float32,), dev), experts.ref(),
+        _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _ptr(ws, "ws"),
+        ws.numel(), _stream(dev)))
+    return out
+
+
+def moe_rmsnorm(x, weight, eps: float, out=None):
+    T, H = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    N.check(N.lib().moe_rmsnorm(T, H, _ptr(x, "x", _U16, dev), _ptr(weight, "weight", (torch.float32,), dev),
+                                ctypes.c_float(eps), _ptr(out, "out", _U16, dev), _stream(dev)))
+    return out
+
+
+# ---- profiling ------------------------------------------------------------
+
+def profile_enable(max_launches: int):
+    N.check(N.lib().moe_profile_enable(int(max_launches)))
+
+
+def profile_reset():
+    N.check(N.lib().moe_profile_reset())
+
+
+def profile_read(kernel: str):
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    N.check(N.lib().moe_profile_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+class MoELayer:
+    """One layer's weights resident on the device, with a reusable
+    workspace, for repeated moe_layer_forward calls."""
+
+    def __init__(self, cfg, li, device, T_max: int):
+        self.cfg = cfg
+        self.shape = shape_of(cfg)
+        self.li = li
+        self.experts = Experts(li)
+        self.ws = workspace(self.shape, T_max, device)
+
+    def forward(self, x, residual=None, out=None):
+        return moe_layer_forward(self.shape, x, self.li.w_router, self.li.router_bias,
+                                 self.li.shared_gate, self.experts, residual=residual, out=out,
+                                 ws=self.ws)

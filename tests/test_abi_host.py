@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI: the built library loads, exports every
+symbol include/moe.h declares, sizes workspaces, and rejects bad arguments
+with the documented status codes before launching anything (no GPU needed:
+every call here fails validation or is a pure host query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_prefill_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _lib():
+    if not os.path.exists(N.LIB_PATH):
+        pytest.skip("library not built")
+    return N.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_list():
+    assert _declared() == sorted(N.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+
+
+def _shape(**kw):
+    d = dict(hidden=2048, num_experts=128, top_k=8, inter=768, group_size=128, quant=0,
+             reserved=0, shared_inter=0)
+    d.update(kw)
+    return N.MoeShape(**d)
+
+
+def _ws(shape, T, kind=N.MOE_WS_LAYER):
+    n = ctypes.c_size_t(0)
+    st = _lib().moe_workspace_size(ctypes.byref(shape), T, kind, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    _lib()
+    st, n = _ws(_shape(), 8192)
+    assert st == N.MOE_OK
+    P = 8192 * 8
+    # at least y_perm and h (bf16) plus the routing arrays
+    assert n >= P * 2048 * 2 + P * 768 * 2 + 4 * P * 4
+    st, r = _ws(_shape(), 8192, N.MOE_WS_ROUTE)
+    assert st == N.MOE_OK and r >= 3 * 128 * 2048 * 2
+    st, p = _ws(_shape(), 8192, N.MOE_WS_PERMUTE)
+    assert st == N.MOE_OK and p == 0
+    st, f = _ws(_shape(), 8192, N.MOE_WS_EXPERT_FFN)
+    assert st == N.MOE_OK and f >= P * 768 * 2
+    assert n >= max(r, f)
+    st, z = _ws(_shape(), 0)
+    assert st == N.MOE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group_size=16), N.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=0), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(hidden=2000), N.MOE_ERR_UNSUPPORTED),
+    (dict(inter=700), N.MOE_ERR_UNSUPPORTED),
+    (dict(num_experts=300), N.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=9, num_experts=16), N.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=9, num_experts=8), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(quant=5), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(reserved=1), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(shared_inter=100), N.MOE_ERR_UNSUPPORTED),
+    (dict(shared_inter=-64), N.MOE_ERR_INVALID_ARGUMENT),
+])
+def test_shape_validation(kw, code):
+    st, _ = _ws(_shape(**kw), 16)
+    assert st == code
+    assert _lib().moe_last_error()
+
+
+def test_negative_T_and_null_shape():
+    L = _lib()
+    n = ctypes.c_size_t(0)
+    assert L.moe_workspace_size(ctypes.byref(_shape()), -1, 0, ctypes.byref(n)) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_workspace_size(None, 4, 0, ctypes.byref(n)) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_workspace_size(ctypes.byref(_shape()), 4, 9, ctypes.byref(n)) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_workspace_size(ctypes.byref(_shape()), (1 << 31) // 8, 0, ctypes.byref(n)) == N.MOE_ERR_UNSUPPORTED
+
+
+FAKE = 0x10000  # an aligned non-null address that is never dereferenced
+
+
+def test_route_validation_before_launch():
+    L = _lib()
+    s = _shape()
+    # T == 0 is an OK no-op, even with NULL tensors
+    assert L.moe_route(ctypes.byref(s), 0, None, None, None, None, None, None, None, None, None, 0, None) == N.MOE_OK
+    # missing x
+    assert L.moe_route(ctypes.byref(s), 4, None, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    # misaligned x
+    assert L.moe_route(ctypes.byref(s), 4, FAKE + 2, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
+    # shared_gate without shared_w
+    assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    # workspace too small / missing
+    assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 16, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, None, None, FAKE, FAKE, None, None, 0, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert b"workspace" in L.moe_last_error()
+
+
+def _experts(**kw):
+    d = dict(w13=FAKE, w13_scale=FAKE, w13_min=None, w2=FAKE, w2_scale=FAKE, w2_min=None,
+             s13=None, s13_scale=None, s13_min=None, s2=None, s2_scale=None, s2_min=None)
+    d.update(kw)
+    return N.MoeExperts(**d)
+
+
+def test_layer_forward_validation_before_launch():
+    L = _lib()
+    s = _shape()
+    st, need = _ws(s, 4)
+    args = lambda e, ws_bytes=need, sg=None, shape=s: L.moe_layer_forward(
+        ctypes.byref(shape), 4, FAKE, FAKE, None, sg, ctypes.byref(e), None, FAKE, FAKE, ws_bytes, None)
+    assert args(_experts(w13=None)) == N.MOE_ERR_INVALID_ARGUMENT
+    assert args(_experts(w13_min=FAKE)) == N.MOE_ERR_INVALID_ARGUMENT       # min with SYM
+    assert args(_experts(s13=FAKE)) == N.MOE_ERR_INVALID_ARGUMENT           # shared without shared_inter
+    assert args(_experts(), ws_bytes=need - 1) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert args(_experts(), sg=FAKE) == N.MOE_ERR_INVALID_ARGUMENT          # gate without shared expert
+    sa = _shape(quant=1)
+    assert args(_experts(), shape=sa) == N.MOE_ERR_INVALID_ARGUMENT         # ASYM needs mins
+    ss = _shape(shared_inter=512)
+    st, need_s = _ws(ss, 4)
+    ex = _experts(s13=FAKE, s13_scale=FAKE, s2=FAKE, s2_scale=FAKE)
+    assert L.moe_layer_forward(ctypes.byref(ss), 4, FAKE, FAKE, None, None, ctypes.byref(ex), None,
+                               FAKE, FAKE, need_s, None) == N.MOE_ERR_INVALID_ARGUMENT  # shared_gate missing
+    assert L.moe_layer_forward(ctypes.byref(s), 0, None, None, None, None, None, None, None, None, 0, None) == N.MOE_OK
+
+
+def test_other_entry_points_validation():
+    L = _lib()
+    s = _shape()
+    e = _experts()
+    assert L.moe_expert_ffn(ctypes.byref(s), 4, FAKE, ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_expert_ffn(ctypes.byref(s), 4, FAKE, ctypes.byref(e), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_ffn(ctypes.byref(s), 4, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(s), 4, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(s), 4, None, FAKE, FAKE, None, None, None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_permute(ctypes.byref(s), 4, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_rmsnorm(4, 2048, FAKE, FAKE, ctypes.c_float(1e-6), FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT  # aliasing
+    assert L.moe_rmsnorm(4, 2047, FAKE, FAKE, ctypes.c_float(1e-6), FAKE + 64, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_rmsnorm(0, 2048, None, None, ctypes.c_float(1e-6), None, None) == N.MOE_OK
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0)
+    assert L.moe_profile_read(None, ctypes.byref(n), ctypes.byref(ms)) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_profile_read(b"combine", ctypes.byref(n), ctypes.byref(ms)) == N.MOE_OK and n.value == 0
