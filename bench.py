@@ -29,6 +29,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer prefill tokens/sec at T=8192; % of bf16 MFMA peak and HBM GB/s"
 
+# Kernel names the library reports timings under (one layer forward).
+KERNELS = ("router_split", "router_gemm", "router_topk", "permute_count", "permute_scatter",
+           "x_to_f16", "gateup_gemm", "down_gemm", "shared_gateup_gemm", "shared_down_gemm",
+           "combine")
+
 # HBM bytes per gate/up launch on the a3b_pp8192 workload, from rocprofv3
 # FETCH_SIZE + WRITE_SIZE (scaled by the copy-kernel calibration factor);
 # None until measured on the current kernel.
@@ -121,8 +126,7 @@ def main():
         layer.forward(x, out=out)
     torch.cuda.synchronize()
     kernels = {}
-    for name in ("router_split", "router_topk", "permute_count", "permute_scatter",
-                 "gateup_gemm", "down_gemm", "shared_gateup_gemm", "shared_down_gemm", "combine"):
+    for name in KERNELS:
         n, tot = qm.profile_read(name)
         if n:
             kernels[name] = round(tot / n * 1000.0, 2)  # microseconds per launch

@@ -37,9 +37,9 @@
  *
  * Supported shapes (MOE_ERR_UNSUPPORTED otherwise):
  *    hidden H % 128 == 0, 128 <= H <= 16384;  1 <= E <= 256;  1 <= k <= min(E, 8);
- *    group_size G in {32, 64, 128};  H % G == 0;  inter I % 64 == 0 and I % G == 0;
- *    shared_inter == 0 or (shared_inter % 64 == 0 and shared_inter % G == 0);
- *    T * k < 2^31.
+ *    group_size G in {32, 64, 128};  inter I % 128 == 0;
+ *    shared_inter == 0 or shared_inter % 128 == 0;
+ *    T * k < 2^31;  T * H and T * k * I below 2^34.
  */
 #ifndef QMOE_MOE_H
 #define QMOE_MOE_H

@@ -92,15 +92,16 @@ static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
   if (s->hidden % 128 != 0 || s->hidden > 16384)
     return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of 128 and <= 16384");
   if (s->hidden % G != 0) return fail(MOE_ERR_UNSUPPORTED, "hidden must be a multiple of G");
-  if (s->inter % 64 != 0 || s->inter % G != 0 || s->inter > 65536)
-    return fail(MOE_ERR_UNSUPPORTED, "inter must be a multiple of 64 and of G");
-  if (s->shared_inter != 0 && (s->shared_inter % 64 != 0 || s->shared_inter % G != 0 ||
-                               s->shared_inter > 65536))
-    return fail(MOE_ERR_UNSUPPORTED, "shared_inter must be 0 or a multiple of 64 and of G");
+  if (s->inter % 128 != 0 || s->inter > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "inter must be a multiple of 128");
+  if (s->shared_inter != 0 && (s->shared_inter % 128 != 0 || s->shared_inter > 65536))
+    return fail(MOE_ERR_UNSUPPORTED, "shared_inter must be 0 or a multiple of 128");
   if (s->num_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "num_experts must be <= 256");
   if (s->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 8");
   if (T * s->top_k >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T * top_k must be < 2^31");
+  if (T * s->hidden / 8 >= (int64_t(1) << 31) || T * s->top_k * s->inter / 8 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "activation tensors must hold fewer than 2^34 elements");
   out->H = (int)s->hidden;
   out->E = (int)s->num_experts;
   out->k = (int)s->top_k;
