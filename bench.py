@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer prefill tokens/sec at T=8192; % of bf16 MFMA peak and HBM GB/s"
 
 # Kernel names the library reports timings under (one layer forward).
-KERNELS = ("router_split", "router_gemm", "router_topk", "permute_count", "permute_scatter",
+KERNELS = ("router_split", "router_gemm", "router_select", "permute_rank", "permute_scatter",
            "x_to_f16", "gateup_gemm", "down_gemm", "shared_gateup_gemm", "shared_down_gemm",
            "combine")
 
@@ -154,7 +154,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: one MoE FFN layer, T={T}, hidden={cfg.H}, experts={cfg.E}, "

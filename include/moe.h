@@ -130,7 +130,8 @@ moe_status_t moe_workspace_size(const moe_shape_t *shape, int64_t T, int32_t kin
  *   logits      [T][E] fp32 or NULL: receives the (biased) logits used for selection
  *   topk_ids    [T][k] int32         topk_w [T][k] fp32
  *   shared_w    [T] fp32, required iff shared_gate != NULL
- *   ws          >= moe_workspace_size(MOE_WS_ROUTE) bytes of scratch        */
+ *   ws          >= moe_workspace_size(MOE_WS_ROUTE, T) bytes of scratch (the
+ *               split router matrix and fp32 partial logits; grows with T)   */
 moe_status_t moe_route(const moe_shape_t *shape, int64_t T, const uint16_t *x,
                        const float *w_router, const float *router_bias,
                        const float *shared_gate, float *logits, int32_t *topk_ids,
@@ -142,8 +143,12 @@ moe_status_t moe_route(const moe_shape_t *shape, int64_t T, const uint16_t *x,
  *   offsets[e]     exclusive prefix sum of counts                [E+1] int32
  *   sorted_pairs   expert by expert, that expert's pairs in ascending p  [P] int32
  *   inv[p]         position of pair p in sorted_pairs            [P] int32
- * topk_ids entries must lie in [0, E). Deterministic (no atomics). ws may be
- * NULL when moe_workspace_size(MOE_WS_PERMUTE) is 0. */
+ * topk_ids entries must lie in [0, E); a pair with an id outside that range
+ * is a caller error: it is left out of counts and sorted_pairs and its inv
+ * entry is 0. Deterministic (no atomics). T == 0 writes zero counts/offsets
+ * (topk_ids, sorted_pairs and inv may then be NULL).
+ *   ws  >= moe_workspace_size(MOE_WS_PERMUTE, T) bytes (per-chunk expert
+ *          histograms, 4 * E * ceil(T*k / 2048) bytes)                     */
 moe_status_t moe_permute(const moe_shape_t *shape, int64_t T, const int32_t *topk_ids,
                          int32_t *counts, int32_t *offsets, int32_t *sorted_pairs,
                          int32_t *inv, void *ws, size_t ws_bytes, hipStream_t stream);

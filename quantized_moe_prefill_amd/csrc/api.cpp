@@ -115,7 +115,7 @@ static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
 static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t split, ids, tw, sw, counts, offsets, sorted, inv, x16, h, hs, yperm, ysh, total;
+  size_t split, partial, hist, ids, tw, sw, counts, offsets, sorted, inv, x16, h, hs, yperm, ysh, total;
 };
 
 // Carve-up of the layer workspace. Each region is 256-byte aligned.
@@ -124,6 +124,8 @@ static Layout layer_layout(const Shape& s, int64_t T) {
   const size_t P = (size_t)T * s.k;
   size_t o = 0;
   L.split = o;   o = al(o + router_split_bytes(s.E, s.Is > 0, s.H));
+  L.partial = o; o = al(o + router_partial_bytes((int)T, s.E, s.Is > 0, s.H));
+  L.hist = o;    o = al(o + permute_ws_bytes((int)P, s.E));
   L.ids = o;     o = al(o + P * 4);
   L.tw = o;      o = al(o + P * 4);
   L.sw = o;      o = al(o + (size_t)T * 4);
@@ -140,7 +142,11 @@ static Layout layer_layout(const Shape& s, int64_t T) {
   return L;
 }
 
-static size_t route_ws(const Shape& s) { return al(router_split_bytes(s.E, s.Is > 0, s.H)); }
+// moe_route scratch: the split router matrix, then the fp32 partial logits.
+static size_t route_ws(const Shape& s, int64_t T) {
+  return al(router_split_bytes(s.E, s.Is > 0, s.H)) +
+         al(router_partial_bytes((int)T, s.E, s.Is > 0, s.H));
+}
 // moe_expert_ffn scratch: fp16 activations, h, shared h.
 static size_t ffn_ws(const Shape& s, int64_t T) {
   const size_t P = (size_t)T * s.k;
@@ -207,11 +213,11 @@ static moe_status_t check_experts(const Shape& s, const moe_experts_t* w) {
 static moe_status_t route_impl(const Shape& s, int64_t T, const uint16_t* x, const float* wr,
                                const float* bias, const float* sg, float* logits,
                                int32_t* ids, float* tw, float* sw, uint16_t* split,
-                               hipStream_t st) {
+                               float* partial, hipStream_t st) {
   QMOE_HIP(launch_router_split(wr, sg, s.E, s.H, split, st), "router_split launch");
-  QMOE_HIP(launch_router_topk(x, split, bias, (int)T, s.H, s.E, s.k, sg != nullptr, logits, ids,
-                              tw, sw, st),
-           "router_topk launch");
+  QMOE_HIP(launch_router_topk(x, split, partial, bias, (int)T, s.H, s.E, s.k, sg != nullptr,
+                              logits, ids, tw, sw, st),
+           "router launch");
   return MOE_OK;
 }
 
@@ -307,8 +313,8 @@ moe_status_t moe_workspace_size(const moe_shape_t* shape, int64_t T, int32_t kin
   if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
   switch (kind) {
     case MOE_WS_LAYER: *bytes = layer_layout(s, T).total; break;
-    case MOE_WS_ROUTE: *bytes = route_ws(s); break;
-    case MOE_WS_PERMUTE: *bytes = 0; break;
+    case MOE_WS_ROUTE: *bytes = route_ws(s, T); break;
+    case MOE_WS_PERMUTE: *bytes = al(permute_ws_bytes((int)(T * s.k), s.E)); break;
     case MOE_WS_EXPERT_FFN: *bytes = ffn_ws(s, T); break;
     default: return fail(MOE_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", kind);
   }
@@ -337,34 +343,35 @@ moe_status_t moe_route(const moe_shape_t* shape, int64_t T, const uint16_t* x,
   // the router pads for a shared-gate row whenever the shape has a shared expert
   Shape sr = s;
   sr.Is = shared_gate != nullptr ? 1 : 0;
-  st = check_ws(ws, ws_bytes, route_ws(sr));
+  st = check_ws(ws, ws_bytes, route_ws(sr, T));
   if (st != MOE_OK) return st;
+  auto* wsb = static_cast<uint8_t*>(ws);
   return route_impl(s, T, x, w_router, router_bias, shared_gate, logits, topk_ids, topk_w,
-                    shared_w, static_cast<uint16_t*>(ws), stream);
+                    shared_w, reinterpret_cast<uint16_t*>(wsb),
+                    reinterpret_cast<float*>(wsb + al(router_split_bytes(s.E, sr.Is > 0, s.H))),
+                    stream);
 }
 
 moe_status_t moe_permute(const moe_shape_t* shape, int64_t T, const int32_t* topk_ids,
                          int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
                          int32_t* inv, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   Shape s;
   moe_status_t st = check_shape(shape, T, &s);
   if (st != MOE_OK) return st;
   QMOE_REQUIRE(counts, "counts");
   QMOE_REQUIRE(offsets, "offsets");
-  if (T == 0) {
-    // counts/offsets of an empty batch are all zero; written by a kernel so
-    // that the call stays asynchronous
-    QMOE_HIP(launch_permute(topk_ids, 0, s.E, counts, offsets, sorted_pairs, inv, stream),
-             "permute launch");
-    return MOE_OK;
+  const int P = (int)(T * s.k);
+  st = check_ws(ws, ws_bytes, al(permute_ws_bytes(P, s.E)));
+  if (st != MOE_OK) return st;
+  if (P > 0) {
+    QMOE_REQUIRE(topk_ids, "topk_ids");
+    QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
+    QMOE_REQUIRE(inv, "inv");
   }
-  QMOE_REQUIRE(topk_ids, "topk_ids");
-  QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
-  QMOE_REQUIRE(inv, "inv");
-  QMOE_HIP(launch_permute(topk_ids, (int)(T * s.k), s.E, counts, offsets, sorted_pairs, inv,
-                          stream),
+  // an empty batch still launches, so that zero counts/offsets are written
+  // asynchronously like every other result
+  QMOE_HIP(launch_permute(topk_ids, P, s.E, counts, offsets, sorted_pairs, inv,
+                          static_cast<int32_t*>(ws), stream),
            "permute launch");
   return MOE_OK;
 }
@@ -449,6 +456,8 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
   if (st != MOE_OK) return st;
   uint8_t* b = static_cast<uint8_t*>(ws);
   auto* split = reinterpret_cast<uint16_t*>(b + L.split);
+  auto* partial = reinterpret_cast<float*>(b + L.partial);
+  auto* hist = reinterpret_cast<int32_t*>(b + L.hist);
   auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
   auto* tw = reinterpret_cast<float*>(b + L.tw);
   auto* sw = s.Is > 0 ? reinterpret_cast<float*>(b + L.sw) : nullptr;
@@ -463,9 +472,9 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
   auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
 
   st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
-                  stream);
+                  partial, stream);
   if (st != MOE_OK) return st;
-  QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, stream),
+  QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
            "permute launch");
   st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs, stream);
   if (st != MOE_OK) return st;

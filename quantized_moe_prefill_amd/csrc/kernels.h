@@ -22,15 +22,21 @@ struct LaunchScope {
 // the shared-gate row (if any), then zeros.
 int router_padded_rows(int E, bool has_shared);
 size_t router_split_bytes(int E, bool has_shared, int H);
+// fp32 partial logits of the router GEMM (one plane per K slice)
+size_t router_partial_bytes(int T, int E, bool has_shared, int H);
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
                                uint16_t* split, hipStream_t s);
-hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, const float* bias, int T,
-                              int H, int E, int k, bool has_shared, float* logits, int32_t* ids,
-                              float* topk_w, float* shared_w, hipStream_t s);
+// router GEMM into `partial`, then per-token logits, top-k and softmax
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, float* partial,
+                              const float* bias, int T, int H, int E, int k, bool has_shared,
+                              float* logits, int32_t* ids, float* topk_w, float* shared_w,
+                              hipStream_t s);
 
 // ---- permutation ------------------------------------------------------
+// scratch: per-chunk expert histograms, permute_ws_bytes(P, E) bytes
+size_t permute_ws_bytes(int P, int E);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_pairs, int32_t* inv, hipStream_t s);
+                          int32_t* sorted_pairs, int32_t* inv, int32_t* hist, hipStream_t s);
 
 // ---- grouped expert GEMMs --------------------------------------------
 // bf16 [n] (n % 8 == 0) -> fp16 in the kperm chunk order of the expert GEMMs.

@@ -2,10 +2,16 @@
 // histogram, prefix scan and a stable scatter into expert-sorted row blocks
 // (the "per-expert buffers" arrangement of the MoE prefill route).
 //
-// One workgroup per expert scans the whole id list, so the result is
-// deterministic and stable (ascending pair index inside each expert) without
-// atomics: pass 1 counts, pass 2 derives the expert's offset from all counts
-// and compacts its pairs with a block-wide scan of match flags.
+// Deterministic and stable (ascending pair index inside each expert), with
+// no global atomics, in two passes over the id list:
+//  permute_rank   : each workgroup takes a chunk of PCH consecutive pairs and
+//                   gives every pair its rank among the chunk's pairs of the
+//                   same expert (wavefront match with one ballot per id bit,
+//                   then a prefix over the waves); writes the rank to inv[p]
+//                   and the chunk's per-expert histogram
+//  permute_scatter: each workgroup sums the histograms (all chunks: counts
+//                   and offsets; earlier chunks: its own base per expert) and
+//                   writes sorted_pairs[base + rank] = p, inv[p] = that position
 #include "common.h"
 #include "kernels.h"
 
@@ -13,106 +19,152 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPer = 4;  // ids per thread per sweep (one 16-byte load)
+constexpr int PT = 256;              // threads per workgroup (4 waves)
+constexpr int PSEG = 8;              // 64-pair segments per wave
+constexpr int PCH = 4 * PSEG * 64;   // pairs per workgroup (2048)
+constexpr int PMAXE = 256;
 
-__device__ __forceinline__ void load4(const int32_t* ids, int p, int P, int v[4]) {
-  if (p + 3 < P) {
-    const u32x4 q = ld16(ids + p);
-    v[0] = (int)q[0]; v[1] = (int)q[1]; v[2] = (int)q[2]; v[3] = (int)q[3];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (p + i < P) ? ids[p + i] : -1;
-  }
+// number of lanes below this one whose bit is set in m
+__device__ __forceinline__ int count_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ int block_sum(int v, int* s_red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_i(v);
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  const int tot = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-  __syncthreads();
-  return tot;
-}
-
-__global__ __launch_bounds__(kThreads) void permute_count_kernel(const int32_t* __restrict__ ids,
-                                                                  int P,
-                                                                  int32_t* __restrict__ counts) {
-  __shared__ int s_red[4];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int p = threadIdx.x * kPer; p < P; p += kThreads * kPer) {
-    int v[4];
-    load4(ids, p, P, v);
-    c += (v[0] == e) + (v[1] == e) + (v[2] == e) + (v[3] == e);
-  }
-  const int tot = block_sum(c, s_red);
-  if (threadIdx.x == 0) counts[e] = tot;
-}
-
-__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ inv) {
-  __shared__ int s_red[4];
-  __shared__ int s_wave[4];
-  const int e = blockIdx.x;
+__global__ __launch_bounds__(PT) void permute_rank_kernel(const int32_t* __restrict__ ids, int P,
+                                                          int E, int nbits,
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ rank_out) {
+  __shared__ int cnt[4][PMAXE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * PMAXE; i += PT) (&cnt[0][0])[i] = 0;
+  __syncthreads();
 
-  int part = 0;
-  for (int i = tid; i < e; i += kThreads) part += counts[i];
-  const int base = block_sum(part, s_red);
-  if (tid == 0) {
-    offsets[e] = base;
-    if (e == E - 1) offsets[E] = base + counts[e];
-  }
-
-  int running = 0;
-  for (int p0 = 0; p0 < P; p0 += kThreads * kPer) {
-    const int p = p0 + tid * kPer;
-    int v[4];
-    load4(ids, p, P, v);
-    const int f0 = v[0] == e, f1 = v[1] == e, f2 = v[2] == e, f3 = v[3] == e;
-    const int n = f0 + f1 + f2 + f3;
-    // inclusive scan of n across the wave
-    int incl = n;
+  const int p0 = blockIdx.x * PCH + wave * PSEG * 64 + lane;
+  int ev[PSEG], rk[PSEG];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
+  for (int s = 0; s < PSEG; ++s) {
+    const int p = p0 + s * 64;
+    int e = p < P ? ids[p] : -1;
+    if ((unsigned)e >= (unsigned)E) e = -1;
+    ev[s] = e;
+  }
+  // Segments in pair order. The lanes holding the same expert are found by
+  // one ballot per id bit: a lane keeps the lanes that agree with it on
+  // every bit. Its rank is the running count of its expert in this wave plus
+  // the number of matching lanes below it.
+#pragma unroll
+  for (int s = 0; s < PSEG; ++s) {
+    const int e = ev[s];
+    const bool valid = e >= 0;
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t bb = __ballot(set);
+      m &= set ? bb : ~bb;
     }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int wbase = 0, tot = 0;
+    const int below = count_below(m);
+    int c = 0;
+    if (valid) c = cnt[wave][e];
+    // every lane has read before the group's lowest lane writes (LDS
+    // operations of one wave complete in order)
+    if (valid && below == 0) cnt[wave][e] = c + __popcll(m);
+    rk[s] = c + below;
+  }
+  __syncthreads();
+  // exclusive prefix over the waves per expert; the chunk's histogram
+  for (int e = tid; e < E; e += PT) {
+    int run = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int c = s_wave[w];
-      if (w < wave) wbase += c;
-      tot += c;
+      const int c = cnt[w][e];
+      cnt[w][e] = run;
+      run += c;
     }
-    __syncthreads();
-    int pos = base + running + wbase + incl - n;
-    if (f0) { sorted_pairs[pos] = p;     inv[p] = pos;     ++pos; }
-    if (f1) { sorted_pairs[pos] = p + 1; inv[p + 1] = pos; ++pos; }
-    if (f2) { sorted_pairs[pos] = p + 2; inv[p + 2] = pos; ++pos; }
-    if (f3) { sorted_pairs[pos] = p + 3; inv[p + 3] = pos; ++pos; }
-    running += tot;
+    hist[(int64_t)blockIdx.x * E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < PSEG; ++s) {
+    const int p = p0 + s * 64;
+    if (p < P) rank_out[p] = ev[s] >= 0 ? rk[s] + cnt[wave][ev[s]] : 0;
+  }
+}
+
+__global__ __launch_bounds__(PT) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv) {
+  __shared__ int s_base[PMAXE];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = gridDim.x, b = blockIdx.x;
+
+  // one thread per expert (E <= 256 = PT)
+  int total = 0, before = 0;
+  if (tid < E) {
+#pragma unroll 8
+    for (int j = 0; j < nb; ++j) {
+      const int h = hist[(int64_t)j * E + tid];
+      total += h;
+      before += j < b ? h : 0;
+    }
+  }
+  // exclusive scan of total over the experts
+  int incl = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (w < wave) wbase += s_wave[w];
+  const int off = wbase + incl - total;
+  if (tid < E) {
+    s_base[tid] = off + before;
+    if (b == 0) {
+      counts[tid] = total;
+      offsets[tid] = off;
+      if (tid == E - 1) offsets[E] = off + total;
+    }
+  }
+  __syncthreads();
+
+  const int end = min(P, (b + 1) * PCH);
+  for (int p = b * PCH + tid; p < end; p += PT) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) {
+      const int pos = s_base[e] + inv[p];
+      sorted_pairs[pos] = p;
+      inv[p] = pos;
+    } else {
+      inv[p] = 0;
+    }
   }
 }
 
 }  // namespace
 
+int permute_chunks(int P) { return P > 0 ? cdiv(P, PCH) : 1; }
+
+size_t permute_ws_bytes(int P, int E) { return (size_t)permute_chunks(P) * E * sizeof(int32_t); }
+
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_pairs, int32_t* inv, hipStream_t s) {
+                          int32_t* sorted_pairs, int32_t* inv, int32_t* hist, hipStream_t s) {
+  const int nb = permute_chunks(P);
   {
-    LaunchScope ls("permute_count", s);
-    hipLaunchKernelGGL(permute_count_kernel, dim3(E), dim3(kThreads), 0, s, ids, P, counts);
+    LaunchScope ls("permute_rank", s);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(PT), 0, s, ids, P, E, nbits, hist, inv);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   LaunchScope ls("permute_scatter", s);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(E), dim3(kThreads), 0, s, ids, P, E, counts,
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(PT), 0, s, ids, P, E, hist, counts,
                      offsets, sorted_pairs, inv);
   return hipGetLastError();
 }

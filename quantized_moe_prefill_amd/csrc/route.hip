@@ -5,8 +5,16 @@
 // router weight is split exactly into three bf16 terms (w = w1 + w2 + w3,
 // truncating the significand 8 bits at a time), so every bf16 x bf16 product
 // on the matrix cores is exact and only the fp32 accumulation rounds - the
-// same error class as an fp32 GEMM, at bf16 matrix-core speed. The split is a
-// tiny pre-pass over E*H weights.
+// same error class as an fp32 GEMM, at bf16 matrix-core speed.
+//
+//  router_split : Wr (+ shared gate row) -> Wsplit [3*Epad][H] bf16 (the three
+//                 terms are separate rows, so the product is one dense GEMM)
+//  router_gemm  : P[ks][t][n] = sum over the ks-th K slice of x[t] . Wsplit[n],
+//                 fp32; 128 x 256 tiles, 8 waves, a three-stage ring of
+//                 direct global->LDS loads; the K dimension is split across
+//                 workgroups when there are too few token tiles to fill the GPU
+//  router_select: L[t,e] = sum_ks ((P[e] + P[Epad+e]) + P[2Epad+e]) + b[e] in a
+//                 fixed order, then top-k and softmax (16 lanes per token)
 #include "common.h"
 #include "kernels.h"
 
@@ -14,7 +22,14 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kRouteRows = 32;  // tokens per workgroup
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int RBM = 128;   // tokens per GEMM tile
+constexpr int RBN = 256;   // output columns (split rows) per tile
+constexpr int RBK = 64;    // K per stage
+constexpr int RSTAGES = 3;
+constexpr int RTHREADS = 512;
 
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
                                                           const float* __restrict__ sg, int E,
@@ -42,6 +57,114 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
+// Dense bf16 GEMM P = x * Wsplit^T over one K slice. LDS rows are 64 bf16
+// (128 B, eight 16-byte chunks); chunk c of row r sits in slot c ^ (r & 7),
+// which keeps the 16-row fragment reads conflict-free and lets one direct
+// load fill eight whole rows.
+__global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ P,
+    int T, int H, int N, int n_mt, int n_nt, int ksplit) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[RSTAGES][RBM][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[RSTAGES][RBN][RBK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 x 64 each
+  const int r16 = lane & 15, lg = lane >> 4;
+
+  int b = blockIdx.x;
+  const int ks = b % ksplit;
+  b /= ksplit;
+  const int nt = b % n_nt;
+  const int mt = b / n_nt;
+  const int row0 = mt * RBM, col0 = nt * RBN;
+  const int klen = H / ksplit;
+  const int kbeg = ks * klen;
+  const int nst = klen / RBK;
+
+  // direct loads: A 128 rows = 16 loads of 8 rows, B 256 rows = 32 loads;
+  // wave w issues A loads 2w, 2w+1 and B loads 4w .. 4w+3 each stage
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const uint16_t* a_src[2];
+  const uint16_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * wave + i) * 8 + lrow;
+    const int t = min(row0 + r, T - 1);
+    a_src[i] = x + (int64_t)t * H + kbeg + 8 * (lslot ^ (r & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (4 * wave + i) * 8 + lrow;
+    const int n = min(col0 + r, N - 1);
+    b_src[i] = w + (int64_t)n * H + kbeg + 8 * (lslot ^ (r & 7));
+  }
+  auto load_stage = [&](int s, int buf) {
+    const int k0 = s * RBK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[i] + k0),
+                                       (lds_void_t*)&As[buf][(2 * wave + i) * 8][0], 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[i] + k0),
+                                       (lds_void_t*)&Bs[buf][(4 * wave + i) * 8][0], 16, 0, 0);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // three-stage ring: stages s+1 and s+2 are in flight while s is computed;
+  // each stage is six direct loads per wave, so "at most 6 outstanding"
+  // means stage s+1 has landed
+  load_stage(0, 0);
+  if (nst > 1) load_stage(1, 1);
+  if (nst > 1)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s % RSTAGES;
+    if (s + 2 < nst) load_stage(s + 2, (s + 2) % RSTAGES);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 64 + i * 16 + r16;
+        a[i] = __builtin_bit_cast(bf16x8, ld16(&As[buf][ra][((j * 4 + lg) ^ (ra & 7)) * 8]));
+        const int rb = wn * 64 + i * 16 + r16;
+        bb[i] = __builtin_bit_cast(bf16x8, ld16(&Bs[buf][rb][((j * 4 + lg) ^ (rb & 7)) * 8]));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_16x16x32(a[mi], bb[ni], acc[mi][ni]);
+    }
+    if (s + 2 < nst)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  float* Pk = P + (int64_t)ks * T * N;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int col = col0 + wn * 64 + ni * 16 + r16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wm * 64 + mi * 16 + 4 * lg + v;
+        if (row < T && col < N) Pk[(int64_t)row * N + col] = acc[mi][ni][v];
+      }
+    }
+}
+
 // (value, index) order used by the selection: larger value first, then the
 // lower index. idx < 0 marks "nothing".
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
@@ -50,132 +173,120 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-template <int MAXN>
-__global__ __launch_bounds__(256) void router_topk_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ split,
-    const float* __restrict__ bias, int T, int H, int E, int Epad, int k, int has_shared,
-    float* __restrict__ logits_out, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
-    float* __restrict__ sw_out) {
-  constexpr int MSUB = kRouteRows / 16;
-  __shared__ float s_log[kRouteRows][272 + 1];
+// DPP row patterns: after xor-1, xor-2 (quad_perm), half-mirror and mirror
+// exchanges every lane of a 16-lane row has combined all 16 lanes.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int NT = Epad / 16;
-  const int t0 = blockIdx.x * kRouteRows;
-  const int64_t plane = (int64_t)Epad * H;
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
 
-  f32x4 acc[MSUB][MAXN];
-#pragma unroll
-  for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-    for (int i = 0; i < MAXN; ++i) acc[m][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& bv, int& bi) {
+  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(bv)));
+  const int oi = dpp<CTRL>(bi);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
 
-  const int kq = 8 * (lane >> 4);  // this lane's 8-wide K slot within a 32-step
-  const int r16 = lane & 15;
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float x) {
+  return x + __int_as_float(dpp<CTRL>(__float_as_int(x)));
+}
 
-  for (int kb = 0; kb < H; kb += 32) {
-    bf16x8 a[MSUB];
+// 16 lanes per token (16 tokens per 256-thread workgroup). Lane r holds the
+// logits of experts 64*i + 4*r + c (i < Q/4, c < 4). Each of the k rounds
+// takes the lane-local best, reduces it over the row with DPP exchanges and
+// retires the winner; lane j keeps round j's winner for the softmax.
+template <int Q>
+__global__ __launch_bounds__(256) void router_select_kernel(
+    const float* __restrict__ P, int ksplit, int T, int E, int Epad, int k,
+    const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out) {
+  const int r = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = t < T;
+  const int tt = live ? t : T - 1;
+  const int N = 3 * Epad;
+
+  float v[Q];
 #pragma unroll
-    for (int m = 0; m < MSUB; ++m) {
-      const int row = t0 + m * 16 + r16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < T) v = ld16(x + (int64_t)row * H + kb + kq);
-      a[m] = __builtin_bit_cast(bf16x8, v);
-    }
-#pragma unroll
-    for (int i = 0; i < MAXN; ++i) {
-      const int n = wave + 4 * i;
-      if (n < NT) {
-        const uint16_t* bp = split + (int64_t)(n * 16 + r16) * H + kb + kq;
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, ld16(bp + s * plane));
-#pragma unroll
-          for (int m = 0; m < MSUB; ++m) acc[m][i] = mfma_16x16x32(a[m], b, acc[m][i]);
-        }
+  for (int i = 0; i < Q / 4; ++i) {
+    const int e0 = 64 * i + 4 * r;
+    f32x4 l = {0.f, 0.f, 0.f, 0.f};
+    if (e0 < Epad) {
+      for (int s = 0; s < ksplit; ++s) {
+        const float* p = P + ((int64_t)s * T + tt) * N + e0;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + Epad);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(p + 2 * Epad);
+        l += (a + b) + c;
       }
     }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = e0 + c;
+      float x = l[c];
+      if (e < E) {
+        if (bias != nullptr) x += bias[e];
+        if (logits_out != nullptr && live) logits_out[(int64_t)t * E + e] = x;
+      } else if (e == E && has_shared && live) {
+        sw_out[t] = 1.f / (1.f + expf(-x));
+      }
+      v[4 * i + c] = x;
+    }
+  }
+  // the shared-gate column past the last lane's range (E a multiple of 64)
+  if (has_shared && E >= 16 * Q && r == 0 && live) {
+    float x = 0.f;
+    for (int s = 0; s < ksplit; ++s) {
+      const float* p = P + ((int64_t)s * T + tt) * N + E;
+      x += (p[0] + p[Epad]) + p[2 * Epad];
+    }
+    sw_out[t] = 1.f / (1.f + expf(-x));
   }
 
-  // logits tile -> LDS (biased)
+  uint32_t avail = 0;  // bit q: v[q] is a candidate
 #pragma unroll
-  for (int i = 0; i < MAXN; ++i) {
-    const int n = wave + 4 * i;
-    if (n < NT) {
-      const int col = n * 16 + r16;
-      const float b = (bias != nullptr && col < E) ? bias[col] : 0.f;
-#pragma unroll
-      for (int m = 0; m < MSUB; ++m)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s_log[m * 16 + 4 * (lane >> 4) + v][col] = acc[m][i][v] + b;
-    }
-  }
-  __syncthreads();
+  for (int q = 0; q < Q; ++q)
+    if (64 * (q >> 2) + 4 * r + (q & 3) < E) avail |= 1u << q;
 
-  if (logits_out != nullptr) {
-    for (int i = tid; i < kRouteRows * E; i += 256) {
-      const int r = i / E, c = i - (i / E) * E;
-      if (t0 + r < T) logits_out[(int64_t)(t0 + r) * E + c] = s_log[r][c];
+  float m0 = 0.f, selv = 0.f;
+  int seli = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.f;
+    int bi = -1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = 64 * (q >> 2) + 4 * r + (q & 3);
+      if (((avail >> q) & 1) && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
     }
+    best_step<kDppXor1>(bv, bi);
+    best_step<kDppXor2>(bv, bi);
+    best_step<kDppHalfMirror>(bv, bi);
+    best_step<kDppMirror>(bv, bi);
+    if (j == 0) m0 = bv;
+    if (r == j) { selv = bv; seli = bi; }
+    if (((bi & 63) >> 2) == r) avail &= ~(1u << (4 * (bi >> 6) + (bi & 3)));
   }
+  // softmax over the k winners (the largest is round 0's)
+  const float ex = r < k ? expf(selv - m0) : 0.f;
+  float sum = sum_step<kDppXor1>(ex);
+  sum = sum_step<kDppXor2>(sum);
+  sum = sum_step<kDppHalfMirror>(sum);
+  sum = sum_step<kDppMirror>(sum);
+  if (live && r < k) {
+    ids_out[(int64_t)t * k + r] = seli;
+    w_out[(int64_t)t * k + r] = ex * (1.f / sum);
+  }
+}
 
-  // top-k + softmax: one wave per token, E/64 candidates per lane
-  for (int r = wave; r < kRouteRows; r += 4) {
-    const int t = t0 + r;
-    if (t >= T) break;
-    float v[4];
-    int id[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      id[q] = e < E ? e : -1;
-      v[q] = e < E ? s_log[r][e] : 0.f;
-    }
-    float sel_v[8];
-    int sel_i[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      float bv = 0.f;
-      int bi = -1;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (better(v[q], id[q], bv, bi)) { bv = v[q]; bi = id[q]; }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      sel_v[j] = bv;
-      sel_i[j] = bi;
-      // retire the winner from its owner lane
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (id[q] == bi) id[q] = -1;
-    }
-    if (lane == 0) {
-      const float m = sel_v[0];
-      float ex[8];
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        ex[j] = expf(sel_v[j] - m);
-        sum += ex[j];
-      }
-      const float inv = 1.f / sum;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        ids_out[(int64_t)t * k + j] = sel_i[j];
-        w_out[(int64_t)t * k + j] = ex[j] * inv;
-      }
-      if (has_shared) sw_out[t] = 1.f / (1.f + expf(-s_log[r][E]));
-    }
-  }
+int router_ksplit(int T, int E, bool has_shared, int H) {
+  const int N = 3 * router_padded_rows(E, has_shared);
+  const int tiles = cdiv(T, RBM) * cdiv(N, RBN);
+  int ks = 1;
+  while (ks < 16 && tiles * ks * 2 <= 256 && (H / RBK) % (ks * 2) == 0) ks *= 2;
+  return ks;
 }
 
 }  // namespace
@@ -184,6 +295,11 @@ int router_padded_rows(int E, bool has_shared) { return cdiv(E + (has_shared ? 1
 
 size_t router_split_bytes(int E, bool has_shared, int H) {
   return (size_t)3 * router_padded_rows(E, has_shared) * H * sizeof(uint16_t);
+}
+
+size_t router_partial_bytes(int T, int E, bool has_shared, int H) {
+  const int N = 3 * router_padded_rows(E, has_shared);
+  return (size_t)router_ksplit(T, E, has_shared, H) * T * N * sizeof(float);
 }
 
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
@@ -198,29 +314,33 @@ hipError_t launch_router_split(const float* w_router, const float* shared_gate, 
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, const float* bias, int T,
-                              int H, int E, int k, bool has_shared, float* logits, int32_t* ids,
-                              float* topk_w, float* shared_w, hipStream_t s) {
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, float* partial,
+                              const float* bias, int T, int H, int E, int k, bool has_shared,
+                              float* logits, int32_t* ids, float* topk_w, float* shared_w,
+                              hipStream_t s) {
   const int Epad = router_padded_rows(E, has_shared);
-  const int NT = Epad / 16;
-  const int maxn = cdiv(NT, 4);
-  const dim3 grid(cdiv(T, kRouteRows)), block(256);
-  LaunchScope ls("router_topk", s);
-#define QMOE_ROUTE_CASE(NN)                                                                    \
-  case NN:                                                                                     \
-    hipLaunchKernelGGL(router_topk_kernel<NN>, grid, block, 0, s, x, split, bias, T, H, E, Epad, \
-                       k, has_shared ? 1 : 0, logits, ids, topk_w, shared_w);                  \
-    break;
-  switch (maxn) {
-    QMOE_ROUTE_CASE(1)
-    QMOE_ROUTE_CASE(2)
-    QMOE_ROUTE_CASE(3)
-    QMOE_ROUTE_CASE(4)
-    QMOE_ROUTE_CASE(5)
-    default:
-      return hipErrorInvalidValue;
+  const int N = 3 * Epad;
+  const int n_mt = cdiv(T, RBM), n_nt = cdiv(N, RBN);
+  const int ks = router_ksplit(T, E, has_shared, H);
+  {
+    LaunchScope ls("router_gemm", s);
+    hipLaunchKernelGGL(router_gemm_kernel, dim3(n_mt * n_nt * ks), dim3(RTHREADS), 0, s, x,
+                       split, partial, T, H, N, n_mt, n_nt, ks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-#undef QMOE_ROUTE_CASE
+  LaunchScope ls("router_select", s);
+  const dim3 grid(cdiv(T, 16)), block(256);
+  const int hs = has_shared ? 1 : 0;
+  if (E <= 64)
+    hipLaunchKernelGGL(router_select_kernel<4>, grid, block, 0, s, partial, ks, T, E, Epad, k,
+                       bias, hs, logits, ids, topk_w, shared_w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(router_select_kernel<8>, grid, block, 0, s, partial, ks, T, E, Epad, k,
+                       bias, hs, logits, ids, topk_w, shared_w);
+  else
+    hipLaunchKernelGGL(router_select_kernel<16>, grid, block, 0, s, partial, ks, T, E, Epad, k,
+                       bias, hs, logits, ids, topk_w, shared_w);
   return hipGetLastError();
 }
 

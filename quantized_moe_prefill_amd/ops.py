@@ -99,7 +99,7 @@ def moe_route(shape, x, w_router, router_bias=None, shared_gate=None, want_logit
     return logits, ids, tw, sw
 
 
-def moe_permute(shape, topk_ids):
+def moe_permute(shape, topk_ids, ws=None):
     T = topk_ids.shape[0]
     dev = topk_ids.device
     E, k = shape.num_experts, shape.top_k
@@ -108,9 +108,12 @@ def moe_permute(shape, topk_ids):
     offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     sp = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
     inv = torch.empty((max(P, 1),), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_PERMUTE)
     N.check(N.lib().moe_permute(
         ctypes.byref(shape), T, _ptr(topk_ids, "topk_ids", (torch.int32,), dev), _ptr(counts, "counts"),
-        _ptr(offsets, "offsets"), _ptr(sp, "sorted_pairs"), _ptr(inv, "inv"), None, 0, _stream(dev)))
+        _ptr(offsets, "offsets"), _ptr(sp, "sorted_pairs"), _ptr(inv, "inv"), _ptr(ws, "ws"),
+        ws.numel(), _stream(dev)))
     return counts, offsets, sp[:P], inv[:P]
 
 

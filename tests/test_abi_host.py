@@ -60,10 +60,10 @@ def test_workspace_sizes():
     st, r = _ws(_shape(), 8192, N.MOE_WS_ROUTE)
     assert st == N.MOE_OK and r >= 3 * 128 * 2048 * 2
     st, p = _ws(_shape(), 8192, N.MOE_WS_PERMUTE)
-    assert st == N.MOE_OK and p == 0
+    assert st == N.MOE_OK and p >= 128 * 4
     st, f = _ws(_shape(), 8192, N.MOE_WS_EXPERT_FFN)
     assert st == N.MOE_OK and f >= P * 768 * 2
-    assert n >= max(r, f)
+    assert n >= max(r, f, p)
     st, z = _ws(_shape(), 0)
     assert st == N.MOE_OK
 

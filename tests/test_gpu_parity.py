@@ -203,6 +203,45 @@ def test_permute_edge_cases():
         check_permute(cfg, ids, g)
 
 
+@pytest.mark.parametrize("E,k,shared,bias", [
+    (1, 1, False, False), (3, 2, True, True), (64, 6, True, False), (100, 8, True, True),
+    (128, 4, True, True), (200, 8, False, True), (256, 8, True, False)])
+def test_route_expert_counts(E, k, shared, bias):
+    """Router alone over expert counts that exercise every per-lane width of
+    the selection and both places of the shared-gate column."""
+    cfg = replace(CONFIGS["a3b_pp512"], T=333, H=512, E=E, k=k, I=128,
+                  shared_I=128 if shared else 0, zipf_bias=bias)
+    li, cpu, x = setup(cfg)
+    shape = qm.shape_of(cfg)
+    logits, ids, tw, sw = qm.moe_route(shape, x, li.w_router, li.router_bias, li.shared_gate,
+                                       want_logits=True)
+    torch.cuda.synchronize()
+    check_route(cfg, cpu, x, dict(logits=logits, ids=ids, tw=tw, sw=sw))
+
+
+def test_permute_large_and_duplicates():
+    """Several 2048-pair chunks with a ragged tail, all 256 experts, skewed
+    and repeated ids (moe_permute does not need distinct ids per token)."""
+    rng = np.random.default_rng(11)
+    for E, k, T, kind in [(256, 8, 1000, "zipf"), (200, 7, 3001, "uniform"), (1, 1, 4097, "one"),
+                          (32, 8, 513, "dup")]:
+        cfg = replace(CONFIGS["tiny"], E=E, k=k)
+        if kind == "zipf":
+            p = 1.0 / np.arange(1, E + 1)
+            ids = rng.choice(E, size=(T, k), p=p / p.sum())
+        elif kind == "uniform":
+            ids = rng.integers(0, E, size=(T, k))
+        elif kind == "one":
+            ids = np.zeros((T, k))
+        else:
+            ids = np.repeat(rng.integers(0, 3, size=(T, 1)), k, axis=1)
+        ids = ids.astype(np.int32)
+        g = dict(zip(["counts", "offsets", "sp", "inv"],
+                     qm.moe_permute(qm.shape_of(cfg), torch.from_numpy(ids).to(DEV))))
+        torch.cuda.synchronize()
+        check_permute(cfg, ids, g)
+
+
 def test_combine_with_residual_in_place():
     cfg = CONFIGS["skew_shared"]
     T, k, H = 300, cfg.k, cfg.H
