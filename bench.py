@@ -1,6 +1,10 @@
 """MoE-layer prefill benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload a3b_pp8192] [--no-cpu]
+    python bench.py --calib-copy ...      also run a 1 GiB device copy (counter scale)
+    python bench.py --pmc-summary FETCH.csv WRITE.csv
+                                          HBM bytes per launch from two rocprofv3
+                                          --pmc runs (FETCH_SIZE, WRITE_SIZE)
 
 One step = one moe_layer_forward (route, permute, gate/up + SwiGLU, down,
 combine) over the workload's batch, with all inputs resident in HBM. Prints
@@ -35,24 +39,85 @@ KERNELS = ("router_split", "router_gemm", "router_select", "permute_rank", "perm
            "combine")
 
 # HBM bytes per gate/up launch on the a3b_pp8192 workload, from rocprofv3
-# FETCH_SIZE + WRITE_SIZE (scaled by the copy-kernel calibration factor);
-# None until measured on the current kernel.
-GATEUP_TRAFFIC_BYTES = None
+# FETCH_SIZE + WRITE_SIZE (each scaled by the copy-kernel calibration factor),
+# keyed by the hash of the expert-GEMM sources they were measured on: a
+# changed kernel reports null until it is measured again.
+GATEUP_TRAFFIC = {"7ed618c2dca75173": 663292907}   # {source sha256[:16]: bytes per launch}
+GEMM_SOURCES = ("quantized_moe_prefill_amd/csrc/ffn.hip", "quantized_moe_prefill_amd/csrc/common.h")
+CALIB_BYTES = 1 << 30
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="a3b_pp8192")
     ap.add_argument("--T", type=int, default=0, help="rows (default: the workload's T)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one elementwise kernel that reads and writes 1 GiB "
+                         "(counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize two rocprofv3 counter_collection.csv files and exit")
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, li, x):
-    """The oracle as it stands, on the whole batch, once."""
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary(fetch_csv: str, write_csv: str) -> None:
+    """Per-kernel KiB per dispatch of FETCH_SIZE and WRITE_SIZE, and each
+    scaled by the ratio of the known copy size to what the counter reads for
+    the calibration copy."""
+    import collections
+    import csv
+    import re
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                name = re.sub(r"\(.*", "", name).replace("void ", "").strip()
+                per[name].append(float(r["Counter_Value"]))
+        return per
+
+    pf = load(fetch_csv, "FETCH_SIZE")
+    pw = load(write_csv, "WRITE_SIZE")
+    # the calibration copy is by far the largest multiply-by-scalar dispatch
+    copy_f = [max(v) for k, v in pf.items() if "MulFunctor" in k]
+    copy_w = [max(v) for k, v in pw.items() if "MulFunctor" in k]
+    fetch = {k: sum(v) / len(v) for k, v in pf.items() if "MulFunctor" not in k}
+    write = {k: sum(v) / len(v) for k, v in pw.items() if "MulFunctor" not in k}
+    nf = {k: len(v) for k, v in pf.items()}
+    kib = CALIB_BYTES / 1024.0
+    sf = kib / max(copy_f) if copy_f else None
+    sw = kib / max(copy_w) if copy_w else None
+    print(f"copy calibration ({CALIB_BYTES} B): FETCH_SIZE {max(copy_f) if copy_f else None} KiB, "
+          f"WRITE_SIZE {max(copy_w) if copy_w else None} KiB -> scale fetch {sf}, write {sw}")
+    print(f"{'kernel':55s} {'n':>4s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'scaled bytes':>14s}")
+    for k in sorted(set(fetch) | set(write)):
+        f, w = fetch.get(k), write.get(k)
+        tot = None
+        if f is not None and w is not None and sf and sw:
+            tot = (f * sf + w * sw) * 1024.0
+        print(f"{k[:55]:55s} {nf.get(k, 0):4d} {f if f is not None else float('nan'):12.1f} "
+              f"{w if w is not None else float('nan'):12.1f} {tot if tot else float('nan'):14.4g}")
+    print(f"gemm source hash {gemm_source_hash()}")
+
+
+def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8):
+    """The oracle as it stands, on the whole batch, repeated until about
+    min_seconds of CPU work (at most max_passes passes)."""
     import numpy as np
     import torch
 
@@ -66,22 +131,28 @@ def cpu_baseline(cfg, li, x):
     cores = len(os.sched_getaffinity(0))
     cpu = li.to("cpu")
     xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
-    dt = time.perf_counter() - t0
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
+        dt += time.perf_counter() - t0
+        passes += 1
     return {
-        "value": round(x.shape[0] / dt, 2),
+        "value": round(passes * x.shape[0] / dt, 2),
         "unit": "tokens/s",
         "cores": blas_threads or cores,
         "kind": "oracle",
-        "sample": f"whole {x.shape[0]}-token batch, one pass of the float64 numpy oracle "
-                  f"(dequantize + route + experts + combine), {dt:.1f} s; "
-                  f"{cores} cores visible, BLAS threads {blas_threads}",
+        "sample": f"the whole {x.shape[0]}-token batch, {passes} passes of the float64 numpy "
+                  f"oracle (dequantize all experts + route + experts + combine), {dt:.1f} s in "
+                  f"total; {cores} cores visible, BLAS threads {blas_threads}",
     }
 
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the MoE layer is "
               "benchmarked on a single MI355X.", file=sys.stderr)
@@ -176,11 +247,20 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-            "traffic": GATEUP_TRAFFIC_BYTES if T == cfg.T else None,
+            "traffic": (GATEUP_TRAFFIC.get(gemm_source_hash())
+                        if (cfg.name, T) == ("a3b_pp8192", 8192) else None),
             "flops_per_launch": gu_flops,
         },
         "cpu_baseline": None,
     }
+    if a.calib_copy:
+        # a copy kernel of known size: y = x * 1 over 1 GiB of fp32 (a memcpy
+        # would go to the DMA engine, which the counters do not see)
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     if not a.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(cfg, li, x)
     print(json.dumps(rec), flush=True)
