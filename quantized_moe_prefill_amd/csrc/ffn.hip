@@ -29,6 +29,8 @@
 // its XCD (workgroups are dealt to the 8 XCDs round-robin), and walks it, so
 // the N tiles of one row block and the row blocks of one expert run on the
 // same XCD and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,17 +39,26 @@ namespace qmoe {
 namespace {
 
 constexpr int BM = 128;          // rows per tile
-#ifndef QMOE_NWAVES
-#define QMOE_NWAVES 8
-#endif
-constexpr int NWAVES = QMOE_NWAVES;  // waves per workgroup, 64 weight rows each
+constexpr int NWAVES = 8;        // waves per workgroup, 64 weight rows each
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int BN = 64 * NWAVES;  // weight rows per tile
 constexpr int BK = 128;          // K per pipeline stage
 constexpr int NXCD = 8;
 constexpr int MSUB = BM / 16;    // 16-row sub-tiles
 constexpr int NFRAG = 4;         // 16-column fragments per wave
-constexpr int WGS_PER_CU = 1;    // persistent workgroups per CU (one wave per SIMD)
+constexpr int WGS_PER_CU = 1;    // persistent workgroups per CU (two waves per SIMD)
+constexpr int ASTAGES = 3;       // activation stages in the LDS ring
+constexpr int ALD = 32 / NWAVES; // direct activation loads per wave and stage (4 rows each)
+constexpr int A_STAGE_BYTES = BM * BK * 2;
+constexpr int SUB_BYTES = BM * 128;  // one wave's epilogue sub-tile (128 rows x 64 fp16)
+// two sub-tiles fit in each activation stage; Ex holds the rest
+constexpr int EX_BYTES = (NWAVES - 2 * ASTAGES) * SUB_BYTES;
+static_assert(A_STAGE_BYTES == 2 * SUB_BYTES && NWAVES > 2 * ASTAGES, "epilogue LDS layout");
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
+// operations are outstanding, leaving the LDS and export counters alone.
+// The builtin form keeps the compiler's own wait bookkeeping exact.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 // Eight consecutive 4-bit weights (one 32-bit word) of one row -> eight fp16
 // weights in the kperm chunk order. OR-ing a nibble n into the fp16 pattern
@@ -92,27 +103,49 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
 
+// Workgroup barrier for LDS hand-offs only. __syncthreads() also orders
+// global memory, which on this target means waiting for every outstanding
+// vector memory operation (loads included) first and would drain the load
+// pipeline at every K stage; here the callers wait for exactly the loads
+// they need (s_waitcnt vmcnt) before this barrier. It completes this wave's
+// own LDS operations, and the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <bool GATEUP, bool ASYM>
+// NK > 0: the number of K stages is known at compile time and the K loop is
+// unrolled completely; NK == 0: any K (a multiple of BK), rolled by three.
+template <bool GATEUP, bool ASYM, int NK>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
-  // A tile, two stages, 128 rows x 128 fp16 each, no padding: the 16-byte
-  // chunk c of row r sits in slot c ^ (r & 15) of its row, which keeps the
-  // 16-row fragment reads free of bank conflicts and lets every wave fill
-  // four whole rows per direct global->LDS load.
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][BK];
-  // packed weights of the stage, per wave: 64 rows x 64 bytes (128 K
-  // nibbles); the 16-byte chunk c of row r sits at position c ^ ((r >> 1) & 3),
-  // so the 16-row fragment reads are free of bank conflicts
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][NWAVES][64][64];
+  // LDS, two uses:
+  //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
+  //    fp16 each, no padding; the 16-byte chunk c of row r sits in slot
+  //    c ^ (r & 15), which keeps the 16-row fragment reads free of bank
+  //    conflicts and lets a direct global->LDS load fill four whole rows.
+  //    Separate arrays (and a K loop unrolled by three) let the compiler see
+  //    that a stage's LDS reads never touch the tiles still being loaded, so
+  //    it does not wait for those loads before reading;
+  //  - epilogue: each wave's output sub-tile (128 rows x 64 B for h, x 128 B
+  //    for y) in As0..As2 and Ex, so the results leave in whole 16-byte row
+  //    pieces.
+  __shared__ __attribute__((aligned(16))) uint8_t As0[A_STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
   __shared__ int s_scan[257];
   __shared__ int s_wave[NWAVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = g.K, N = g.N;
   const int KG = K / g.G;
-  const int nk = K / BK;
+  const int nk = NK > 0 ? NK : K / BK;
 
   // ---- tile list: per-expert tile prefix (tiles of BM rows) ----
   int n_mtiles;
@@ -177,7 +210,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // Rows past the expert's end read row 0 of the tile's source (finite
     // data whose outputs are never stored).
     // offsets are in 16-byte chunks (the host guarantees rows * K / 8 < 2^31)
-    constexpr int ALD = 32 / NWAVES;
     int a_off[ALD];
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
@@ -187,7 +219,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       a_off[i] = src * (K / 8) + (r16 ^ (r & 15));
     }
 
-    // ---- this wave's weight rows ----
+    // ---- this wave's weight rows: fragment f covers 16 of them; lane
+    // (r16, lg) reads row r16 of each fragment, K values [32 lg, 32 lg + 32)
+    // of every stage (16 bytes), which is also the K range its A fragments
+    // cover, so the two operands agree without any reordering.
     int wrow[NFRAG];
     bool fvalid[NFRAG];
 #pragma unroll
@@ -208,42 +243,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) wr_base[f] = e * N + (fvalid[f] ? wrow[f] : 0);
 
-    // B staging: load f of this wave fills fragment f's 16 rows; lane l
-    // covers row l/4 and LDS position l%4, i.e. source chunk (l%4) ^ ((row>>1)&3)
-    const int b_row = lane >> 2;
-    const int b_chunk = (lane & 3) ^ ((b_row >> 1) & 3);
-    int b_src[NFRAG];  // this lane's source row (global weight row index)
-#pragma unroll
-    for (int f = 0; f < NFRAG; ++f) {
-      int wr;
-      if (GATEUP) {
-        const int I = N / 2;
-        const int c = ntile * (BN / 2) + wave * 32 + (f & 1) * 16;
-        wr = (c < I) ? (f < 2 ? c : I + c) + b_row : 0;
-      } else {
-        const int c = ntile * BN + wave * 64 + f * 16;
-        wr = (c < N) ? c + b_row : 0;
-      }
-      b_src[f] = e * N + wr;
-    }
-
-    uint32_t rs[NFRAG], rm[NFRAG];
-    auto load_stage = [&](int kt, int buf) {
+    auto load_a = [&](int kt, uint8_t* dst) {
       const int k0 = kt * BK;
 #pragma unroll
       for (int i = 0; i < ALD; ++i)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(g.A + (int64_t)a_off[i] * 8 + k0),
-                                         (lds_void_t*)&As[buf][4 * (ALD * wave + i)][0], 16, 0, 0);
-#pragma unroll
-      for (int f = 0; f < NFRAG; ++f)
-        __builtin_amdgcn_global_load_lds(
-            (glb_void_t*)(g.W + (int64_t)b_src[f] * (K / 2) + k0 / 2 + b_chunk * 16),
-            (lds_void_t*)&Bs[buf][wave][f * 16][0], 16, 0, 0);
+                                         (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16,
+                                         0, 0);
+    };
+    // weights and the group's scale (and min) of stage kt into registers
+    auto load_b = [&](int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
+      const int k0 = kt * BK;
       const int grp = (k0 + lg * 32) / g.G;
 #pragma unroll
+      for (int f = 0; f < NFRAG; ++f)
+        cb[f] = ld16(g.W + (int64_t)wr_base[f] * (K / 2) + k0 / 2 + lg * 16);
+#pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
-        rs[f] = (uint32_t)g.Wscale[(int64_t)wr_base[f] * KG + grp] * 0x10001u;
-        rm[f] = ASYM ? (uint32_t)g.Wmin[(int64_t)wr_base[f] * KG + grp] * 0x10001u : 0u;
+        rs[f] = g.Wscale[(int64_t)wr_base[f] * KG + grp];
+        rm[f] = ASYM ? (uint32_t)g.Wmin[(int64_t)wr_base[f] * KG + grp] : 0u;
       }
     };
 
@@ -253,143 +271,160 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One K stage on LDS buffer `buf`: four 32-wide K steps x eight 16-row
-    // sub-tiles, flattened into 32 (step, sub-tile) slots of four MFMAs each.
-    // A fragments are read two slots ahead through a three-deep rotation; the
-    // next step's weights are dequantized while the current step's MFMAs run.
-    // The scheduling groups pin one LDS read and four MFMAs per slot with two
-    // VALU ops between MFMAs, so neither LDS latency nor dequant work sits on
-    // the matrix core's critical path. Every sub-tile is computed; rows past
-    // the end of an expert hold finite data whose results are never stored.
-    auto compute_stage = [&](int buf, const f16x2* cs, const f16x2* cm) {
-      // Per-lane LDS byte addresses; every other term of an address is a
-      // compile-time offset (sub-tile, stage buffer, fragment), which keeps
-      // the address state to five registers.
-      const uint8_t* as_base = reinterpret_cast<const uint8_t*>(&As[buf][0][0]);
-      const uint8_t* bs_base = reinterpret_cast<const uint8_t*>(&Bs[buf][wave][0][0]);
-      u32x4 cb[NFRAG];  // this lane's packed weights of the stage (32 K values per fragment)
-      {
-        const uint8_t* bp = bs_base + r16 * 64 + ((lg ^ ((r16 >> 1) & 3)) * 16);
+    // One K stage from ring slot `buf`: four 32-wide K steps x eight 16-row
+    // sub-tiles. Two waves share each SIMD, so the hardware interleaves one
+    // wave's dequant and LDS reads with the other's MFMAs: keep the live set
+    // small (weights dequantized just in time, A read one sub-tile ahead).
+    // Every sub-tile is computed; rows past the end of an expert hold finite
+    // data whose results are never stored. The down GEMM swaps the operands
+    // (C^T = W A^T), so each lane ends up with four consecutive output
+    // columns of one row.
+    auto compute_stage = [&](const uint8_t* as_base, const u32x4* cb, const uint32_t* rs,
+                             const uint32_t* rm) {
+      f16x2 cs[NFRAG], cm[NFRAG];
 #pragma unroll
-        for (int f = 0; f < NFRAG; ++f) cb[f] = ld16(bp + f * 16 * 64);
+      for (int f = 0; f < NFRAG; ++f) {
+        cs[f] = __builtin_bit_cast(f16x2, rs[f] * 0x10001u);
+        cm[f] = __builtin_bit_cast(f16x2, rm[f] * 0x10001u);
       }
       const uint8_t* ap[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) ap[j] = as_base + r16 * (BK * 2) + ((((lg * 4) ^ r16) ^ j) * 16);
-      auto read_a = [&](int p) {
-        const int j = p >> 3, mi = p & 7;
+      auto read_a = [&](int j, int mi) {
         return __builtin_bit_cast(f16x8, ld16(ap[j] + mi * 16 * BK * 2));
       };
-      if constexpr (NWAVES >= 8) {
-        // Two waves share each SIMD, so the hardware interleaves one wave's
-        // dequant and LDS reads with the other's MFMAs: keep the live set
-        // small (weights dequantized just in time, A read one sub-tile ahead).
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f16x8 b[NFRAG];
+      for (int j = 0; j < 4; ++j) {
+        f16x8 b[NFRAG];
 #pragma unroll
-          for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][j], cs[f], cm[f]);
-          f16x8 a = read_a(j * 8);
+        for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][j], cs[f], cm[f]);
+        f16x8 a = read_a(j, 0);
 #pragma unroll
-          for (int mi = 0; mi < MSUB; ++mi) {
-            f16x8 an;
-            if (mi + 1 < MSUB) an = read_a(j * 8 + mi + 1);
+        for (int mi = 0; mi < MSUB; ++mi) {
+          f16x8 an;
+          if (mi + 1 < MSUB) an = read_a(j, mi + 1);
 #pragma unroll
-            for (int f = 0; f < NFRAG; ++f) acc[mi][f] = mfma_16x16x32_f16(a, b[f], acc[mi][f]);
-            if (mi + 1 < MSUB) a = an;
-          }
+          for (int f = 0; f < NFRAG; ++f)
+            acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
+                                : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
+          if (mi + 1 < MSUB) a = an;
         }
-        return;
-      }
-      f16x8 abuf[3], b_cur[NFRAG], b_nxt[NFRAG];
-      abuf[0] = read_a(0);
-      abuf[1] = read_a(1);
-#pragma unroll
-      for (int f = 0; f < NFRAG; ++f) b_cur[f] = dequant8_f16<ASYM>(cb[f][0], cs[f], cm[f]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int j = p >> 3, mi = p & 7;
-        if (p + 2 < 32) abuf[(p + 2) % 3] = read_a(p + 2);
-        if (mi == 0 && j + 1 < 4) {
-#pragma unroll
-          for (int f = 0; f < NFRAG; ++f) b_nxt[f] = dequant8_f16<ASYM>(cb[f][j + 1], cs[f], cm[f]);
-        }
-#pragma unroll
-        for (int f = 0; f < NFRAG; ++f)
-          acc[mi][f] = mfma_16x16x32_f16(abuf[p % 3], b_cur[f], acc[mi][f]);
-        if (p + 2 < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // 2 VALU
-        }
-        if (mi == 7 && j + 1 < 4) {
-#pragma unroll
-          for (int f = 0; f < NFRAG; ++f) b_cur[f] = b_nxt[f];
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto k_loop = [&]() {
-      load_stage(0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        // this stage's scales move to registers; the next stage's loads fly
-        f16x2 cs[NFRAG], cm[NFRAG];
-#pragma unroll
-        for (int f = 0; f < NFRAG; ++f) {
-          cs[f] = __builtin_bit_cast(f16x2, rs[f]);
-          cm[f] = __builtin_bit_cast(f16x2, rm[f]);
-        }
-        if (kt + 1 < nk) load_stage(kt + 1, buf ^ 1);
-        compute_stage(buf, cs, cm);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
       }
     };
-    k_loop();
 
-    // ---- epilogue ----
-    // Opaque redefinitions of the per-lane row offsets: they are constants
-    // per lane, and without this the compiler computes all 32 row indices
-    // once at kernel start and holds them in registers through the K loop.
-    int rq = 4 * lg;
-    asm volatile("" : "+v"(rq), "+v"(row0), "+v"(rows));
-    if (GATEUP) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!fvalid[j]) continue;
-        // h is the A operand of the down GEMM: stored in kperm chunk order
-        const int col = wrow[j];
-        const int pcol = (col & ~7) | kpos(col & 7);
-#pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rl = mi * 16 + rq + v;
-            if (rl < rows) {
-              const float h = silu(acc[mi][j][v]) * acc[mi][j + 2][v];
-              g.C[(int64_t)(row0 + rl) * g.ldc + pcol] = (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
-            }
-          }
-      }
-    } else {
+    // ---- K loop: activations two stages ahead in the LDS ring, weights one
+    // stage ahead in registers. Within a stage the weight loads are issued
+    // before the activation loads, so "at most ALD loads outstanding" at the
+    // end of stage s means: stage s+1's activations and weights have landed
+    // (loads complete in issue order). Every stage issues the same loads (past
+    // the last stage they repeat it, into a slot nobody reads), so the waits
+    // are the same at every stage and the compiler's own wait bookkeeping
+    // stays exact.
+    lds_barrier();  // the previous tile's epilogue is done with the LDS
+    const int klast = nk - 1;
+    u32x4 cb[NFRAG];
+    uint32_t rs[NFRAG], rm[NFRAG];
+    load_b(0, cb, rs, rm);
+    load_a(0, As0);
+    load_a(min(1, klast), As1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
+    lds_barrier();
+    // stage kt reads ring slot kt % 3 and loads stage kt + 2 into slot (kt + 2) % 3
+    auto stage = [&](int kt, const uint8_t* cur, uint8_t* nxt2) {
+      u32x4 cbn[NFRAG];
+      uint32_t rsn[NFRAG], rmn[NFRAG];
+      load_b(min(kt + 1, klast), cbn, rsn, rmn);
+      load_a(min(kt + 2, klast), nxt2);
+      compute_stage(cur, cb, rs, rm);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
+      lds_barrier();
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
-        if (!fvalid[f]) continue;
-        const int col = wrow[f];
+        cb[f] = cbn[f];
+        rs[f] = rsn[f];
+        rm[f] = rmn[f];
+      }
+    };
+    if constexpr (NK > 0) {
+#pragma unroll
+      for (int kt = 0; kt < NK; kt += 3) {
+        stage(kt, As0, As2);
+        if (kt + 1 < NK) stage(kt + 1, As1, As0);
+        if (kt + 2 < NK) stage(kt + 2, As2, As1);
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += 3) {
+        stage(kt, As0, As2);
+        if (kt + 1 < nk) stage(kt + 1, As1, As0);
+        if (kt + 2 < nk) stage(kt + 2, As2, As1);
+      }
+    }
+    // the repeated loads of the last stages must land before the epilogue
+    // reuses the ring
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+    // ---- epilogue: results to this wave's LDS sub-tile, then whole row
+    // pieces to global memory. The last barrier of the K loop has released
+    // the activation ring.
+    // Opaque redefinitions of the per-lane row offsets: they are constants
+    // per lane, and without this the compiler computes all row indices once
+    // at kernel start and holds them in registers through the K loop.
+    int rq = 4 * lg, rr = r16;
+    asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
+    uint8_t* sub = (wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? As2 : Ex) + (wave & 1) * SUB_BYTES;
+    if (GATEUP) {
+      // h (128 rows x 32 columns) in kperm chunk order, 64 bytes per row; the
+      // 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four row
+      // groups of one write land in different banks
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pc = 8 * (r16 >> 3) + kpos(r16 & 7);  // column in its 16-wide pair of pieces
 #pragma unroll
         for (int mi = 0; mi < MSUB; ++mi)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int rl = mi * 16 + rq + v;
-            if (rl < rows)
-              g.C[(int64_t)(row0 + rl) * g.ldc + col] =
-                  (uint16_t)(pack_f16x2(acc[mi][f][v], 0.f) & 0xffffu);
+            const float h = silu(acc[mi][j][v]) * acc[mi][j + 2][v];
+            const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
+            *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
+                (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
           }
+      }
+      // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
+      const int col0 = ntile * (BN / 2) + wave * 32;
+      const bool cvalid = col0 < N / 2;
+#pragma unroll
+      for (int q = 0; q < BM / 16; ++q) {
+        const int rl = q * 16 + (lane_o >> 2);
+        const int p = lane_o & 3;
+        const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
+        if (cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + col0 + p * 8, d);
+      }
+    } else {
+      // y (128 rows x 64 columns), 128 bytes per row; lane (r16, lg) holds
+      // columns 16 f + 4 lg .. +3 of row 16 mi + r16. The 16-byte piece p of
+      // row r sits at p ^ (r & 7), so the 16 rows of one write spread over
+      // all banks.
+#pragma unroll
+      for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) {
+          const int rl = mi * 16 + rr;
+          uint2 d;
+          d.x = pack_f16x2(acc[mi][f][0], acc[mi][f][1]);
+          d.y = pack_f16x2(acc[mi][f][2], acc[mi][f][3]);
+          const int piece = (2 * f + (lg >> 1)) ^ (rl & 7);
+          *reinterpret_cast<uint2*>(sub + rl * 128 + piece * 16 + (lg & 1) * 8) = d;
+        }
+      const int col0 = ntile * BN + wave * 64;
+      const bool cvalid = col0 < N;
+      // 8 rows x 128 bytes per wave-wide read: lane -> row lane/8, piece lane%8
+#pragma unroll
+      for (int q = 0; q < BM / 8; ++q) {
+        const int rl = q * 8 + (lane_o >> 3);
+        const int p = lane_o & 7;
+        const u32x4 d = ld16(sub + rl * 128 + (p ^ (rl & 7)) * 16);
+        if (cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + col0 + p * 8, d);
       }
     }
   }
@@ -418,10 +453,23 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   wgs = cdiv(wgs, NXCD) * NXCD;
   const dim3 grid(wgs), block(NTHREADS);
   LaunchScope ls(name, s);
+  const int nk = g.K / BK;
+  // the down projection of the common I = 768 runs fully unrolled (six
+  // stages); everything else uses the loop rolled by three
+  auto go = [&](auto asym) {
+    constexpr bool A = decltype(asym)::value;
+    if constexpr (!GATEUP) {
+      if (nk == 6) {
+        hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, 6>), grid, block, 0, s, g, n_ntiles);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, 0>), grid, block, 0, s, g, n_ntiles);
+  };
   if (g.Wmin != nullptr)
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, true>), grid, block, 0, s, g, n_ntiles);
+    go(std::true_type{});
   else
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, false>), grid, block, 0, s, g, n_ntiles);
+    go(std::false_type{});
   return hipGetLastError();
 }
 
