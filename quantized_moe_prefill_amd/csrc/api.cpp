@@ -236,6 +236,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   g.offsets = offsets;
   g.E = s.E;
   g.max_rows = P;
+  g.a_rows = (int)T;
   g.W = w->w13;
   g.Wscale = w->w13_scale;
   g.Wmin = s.asym ? w->w13_min : nullptr;
@@ -248,6 +249,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
 
   GroupedGemm d = g;
   d.A = h;
+  d.a_rows = P;
   d.gather = nullptr;
   d.W = w->w2;
   d.Wscale = w->w2_scale;
@@ -268,6 +270,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
     gs.rows_single = (int)T;
     gs.E = 1;
     gs.max_rows = (int)T;
+    gs.a_rows = (int)T;
     gs.W = w->s13;
     gs.Wscale = w->s13_scale;
     gs.Wmin = s.asym ? w->s13_min : nullptr;

@@ -6,14 +6,16 @@
 // an fp16 scale (and min) per group of G elements along K, as in that page's
 // symmetric and asymmetric expert files ("Known limits").
 //
-// Tile: BM = 128 rows of one expert x BN = 256 weight rows, K in stages of
-// 128. The gathered activation rows go through LDS (double buffered) and are
-// read by all four waves; each wave owns 64 weight rows (four 16-column
-// fragments) across all 128 rows, loads its packed weights straight from
-// global memory (16 bytes = 32 K values per lane per fragment and stage) and
+// Tile: BM = 128 rows of one expert x BN = 512 weight rows, K in stages of
+// 128, one 512-thread workgroup per CU (eight waves, two per SIMD). The
+// gathered activation rows go through a three-stage LDS ring (direct
+// global->LDS loads, two stages ahead) and are read by all eight waves; each
+// wave owns 64 weight rows (four 16-column fragments) across all 128 rows,
+// loads its packed weights straight from global memory into registers (16
+// bytes = 32 K values per lane per fragment and stage, one stage ahead) and
 // dequantizes them in registers, so no weight is dequantized twice and no
-// dequantized weight touches LDS. v_mfma_f32_16x16x32_f16 with fp32
-// accumulators.
+// weight touches LDS. v_mfma_f32_16x16x32_f16 with fp32 accumulators; the
+// results leave through a per-wave LDS sub-tile as 16-byte row pieces.
 //
 // The gate/up kernel pairs gate and up rows of the same intermediate columns
 // in one wave, so h = silu(g) * u is formed in registers and written once.
@@ -55,6 +57,10 @@ constexpr int SUB_BYTES = BM * 128;  // one wave's epilogue sub-tile (128 rows x
 constexpr int EX_BYTES = (NWAVES - 2 * ASTAGES) * SUB_BYTES;
 static_assert(A_STAGE_BYTES == 2 * SUB_BYTES && NWAVES > 2 * ASTAGES, "epilogue LDS layout");
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, offset
+// mode).
+constexpr int kRsrcWord3 = 0x00020000;
+
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
 // operations are outstanding, leaving the LDS and export counters alone.
 // The builtin form keeps the compiler's own wait bookkeeping exact.
@@ -70,14 +76,15 @@ __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s2, f16x2 m2) {
   const f16x2 off = ASYM ? f16x2{(_Float16)1024.0f, (_Float16)1024.0f}
                          : f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
   // the two constants live in registers so that mask-and-or is a single
-  // v_and_or_b32 (VOP3 takes no literal and at most one scalar operand on gfx9)
+  // v_and_or_b32 (VOP3 takes no literal and at most one scalar operand on
+  // gfx9): the mask in a scalar register, the fp16 pattern in a vector one
   const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
-  const uint32_t magic = 0x64006400u;
+  uint32_t magic = 0x64006400u;
+  asm("" : "+v"(magic));
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t t;  // (1024 + n_i, 1024 + n_{i+4}) as an fp16 pair
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(t) : "v"(w >> (4 * i)), "s"(mask), "v"(magic));
+    const uint32_t t = ((w >> (4 * i)) & mask) | magic;  // (1024 + n_i, 1024 + n_{i+4})
     const f16x2 n = __builtin_bit_cast(f16x2, t) - off;
     const f16x2 v = ASYM ? __builtin_elementwise_fma(n, s2, m2) : n * s2;
     o[i] = __builtin_bit_cast(uint32_t, v);
@@ -117,18 +124,54 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The LDS writes of this wave are complete and visible to its own later
+// reads (a wave's LDS operations complete in order; the wait also keeps the
+// compiler from reordering across it).
+__device__ __forceinline__ void lds_wave_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
+// Slot swizzle of the activation tiles: chunk c of row r sits in slot
+// c ^ rowswz(r), the row's low four bits with their two halves swapped. A
+// fragment read has 16 lanes on 16 consecutive rows and, per group of 16
+// lanes, chunk 4*group + step; a plain c ^ (r & 15) leaves it two-way bank
+// conflicted on gfx950 (measured with the LDS conflict counter), the swapped
+// form is conflict-free.
+__device__ __forceinline__ int rowswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Source rows of n activation rows starting at local row r_first (stride
+// r_step) of a tile: rows past the expert's end read the tile's first row
+// (finite data whose outputs are never stored). All gathers are issued
+// before any is used, so their latencies overlap.
+template <int NL>
+__device__ __forceinline__ void gather_rows(const GroupedGemm& g, int row0, int rows, int r_first,
+                                            int r_step, int* src) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int r = r_first + i * r_step;
+    src[i] = row0 + (r < rows ? r : 0);
+  }
+  if (g.gather != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) src[i] = g.gather[src[i]];
+    const int div = g.gather_div;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) src[i] /= div;
+  }
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// NK > 0: the number of K stages is known at compile time and the K loop is
-// unrolled completely; NK == 0: any K (a multiple of BK), rolled by three.
-template <bool GATEUP, bool ASYM, int NK>
+template <bool GATEUP, bool ASYM>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
   //    fp16 each, no padding; the 16-byte chunk c of row r sits in slot
-  //    c ^ (r & 15), which keeps the 16-row fragment reads free of bank
-  //    conflicts and lets a direct global->LDS load fill four whole rows.
+  //    c ^ rowswz(r) (see rowswz), which keeps the fragment reads free of
+  //    bank conflicts and lets a direct global->LDS load fill four whole rows.
   //    Separate arrays (and a K loop unrolled by three) let the compiler see
   //    that a stage's LDS reads never touch the tiles still being loaded, so
   //    it does not wait for those loads before reading;
@@ -145,7 +188,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = g.K, N = g.N;
   const int KG = K / g.G;
-  const int nk = NK > 0 ? NK : K / BK;
+  const int nk = K / BK;
 
   // ---- tile list: per-expert tile prefix (tiles of BM rows) ----
   int n_mtiles;
@@ -174,6 +217,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const int wgs_per_xcd = gridDim.x / NXCD;
   const int t_begin = (int)((int64_t)total * xcd / NXCD);
   const int t_end = (int)((int64_t)total * (xcd + 1) / NXCD);
+
+  // buffer resources: 32-bit offsets instead of 64-bit addresses (the host
+  // guarantees every byte size below fits in 31 bits); a read past the end
+  // of a buffer returns zero
+  const int n_groups = g.counts != nullptr ? g.E : 1;
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, g.a_rows * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rW =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, 0, n_groups * N * (K / 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rS =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale, 0, n_groups * N * KG * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3);
+  const int s_step = (BK / g.G) * 2;  // scale bytes per stage along a row
 
   for (int tile = t_begin + wg_in_xcd; tile < t_end; tile += wgs_per_xcd) {
     // per-lane constants are derived from an opaque copy of the lane index in
@@ -210,58 +267,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // Rows past the expert's end read row 0 of the tile's source (finite
     // data whose outputs are never stored).
     // offsets are in 16-byte chunks (the host guarantees rows * K / 8 < 2^31)
-    int a_off[ALD];
+    uint32_t a_off[ALD];  // byte offsets into A
+    {
+      int src[ALD];
+      gather_rows<ALD>(g, row0, rows, 4 * ALD * wave + lg, 4, src);
 #pragma unroll
-    for (int i = 0; i < ALD; ++i) {
-      const int r = 4 * (ALD * wave + i) + lg;
-      const int ar = row0 + (r < rows ? r : 0);
-      const int src = g.gather != nullptr ? g.gather[ar] / g.gather_div : ar;
-      a_off[i] = src * (K / 8) + (r16 ^ (r & 15));
-    }
-
-    // ---- this wave's weight rows: fragment f covers 16 of them; lane
-    // (r16, lg) reads row r16 of each fragment, K values [32 lg, 32 lg + 32)
-    // of every stage (16 bytes), which is also the K range its A fragments
-    // cover, so the two operands agree without any reordering.
-    int wrow[NFRAG];
-    bool fvalid[NFRAG];
-#pragma unroll
-    for (int f = 0; f < NFRAG; ++f) {
-      if (GATEUP) {
-        // fragments 0,1: gate columns c0 + 0..31 ; 2,3: up rows of the same columns
-        const int I = N / 2;
-        const int c = ntile * (BN / 2) + wave * 32 + (f & 1) * 16;
-        fvalid[f] = c < I;
-        wrow[f] = (f < 2 ? c : I + c) + r16;
-      } else {
-        const int c = ntile * BN + wave * 64 + f * 16;
-        fvalid[f] = c < N;
-        wrow[f] = c + r16;
+      for (int i = 0; i < ALD; ++i) {
+        const int r = 4 * (ALD * wave + i) + lg;
+        a_off[i] = (uint32_t)(src[i] * (K / 8) + (r16 ^ rowswz(r))) * 16u;
       }
     }
-    int wr_base[NFRAG];  // global weight row index (E * N < 2^24)
-#pragma unroll
-    for (int f = 0; f < NFRAG; ++f) wr_base[f] = e * N + (fvalid[f] ? wrow[f] : 0);
+
+    // ---- this wave's weight rows: fragment f covers rows c0 + frow(f) +
+    // 0..15 of the expert (gate/up: fragments 0, 1 are gate columns c0 + 16 f,
+    // 2, 3 the up rows of the same columns). Lane (r16, lg) reads row r16 of
+    // each fragment, K values [32 lg, 32 lg + 32) of every stage (16 bytes),
+    // which is also the K range its A fragments cover, so the two operands
+    // agree without any reordering: one per-lane offset plus a uniform offset
+    // per fragment and stage.
+    const int c0 = GATEUP ? ntile * (BN / 2) + wave * 32 : ntile * BN + wave * 64;
+    const bool cvalid = c0 < (GATEUP ? N / 2 : N);
+    const int wrow0 = e * N + (cvalid ? c0 : 0) + r16;
+    const uint32_t b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
+    const uint32_t s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
+    auto frow = [&](int f) { return GATEUP ? 16 * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f; };
 
     auto load_a = [&](int kt, uint8_t* dst) {
-      const int k0 = kt * BK;
 #pragma unroll
       for (int i = 0; i < ALD; ++i)
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(g.A + (int64_t)a_off[i] * 8 + k0),
-                                         (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, a_off[i], kt * BK * 2, 0, 0);
     };
     // weights and the group's scale (and min) of stage kt into registers
     auto load_b = [&](int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
-      const int k0 = kt * BK;
-      const int grp = (k0 + lg * 32) / g.G;
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f)
-        cb[f] = ld16(g.W + (int64_t)wr_base[f] * (K / 2) + k0 / 2 + lg * 16);
+        cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rW, b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
-        rs[f] = g.Wscale[(int64_t)wr_base[f] * KG + grp];
-        rm[f] = ASYM ? (uint32_t)g.Wmin[(int64_t)wr_base[f] * KG + grp] : 0u;
+        const int so = frow(f) * KG * 2 + kt * s_step;
+        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_lane, so, 0);
+        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, s_lane, so, 0) : 0u;
       }
     };
 
@@ -289,15 +336,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       }
       const uint8_t* ap[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ap[j] = as_base + r16 * (BK * 2) + ((((lg * 4) ^ r16) ^ j) * 16);
+      for (int j = 0; j < 4; ++j) ap[j] = as_base + r16 * (BK * 2) + (((lg * 4 + j) ^ rowswz(r16)) * 16);
       auto read_a = [&](int j, int mi) {
         return __builtin_bit_cast(f16x8, ld16(ap[j] + mi * 16 * BK * 2));
       };
+      // weights of step 0 now; those of step j+1 are dequantized while step
+      // j's MFMAs run (one fragment behind each of the first sub-tiles)
+      f16x8 b[NFRAG];
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][0], cs[f], cm[f]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f16x8 b[NFRAG];
-#pragma unroll
-        for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][j], cs[f], cm[f]);
+        f16x8 bn[NFRAG];
         f16x8 a = read_a(j, 0);
 #pragma unroll
         for (int mi = 0; mi < MSUB; ++mi) {
@@ -307,7 +357,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           for (int f = 0; f < NFRAG; ++f)
             acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
                                 : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
+          if (j < 3 && mi < NFRAG) bn[mi] = dequant8_f16<ASYM>(cb[mi][j + 1], cs[mi], cm[mi]);
           if (mi + 1 < MSUB) a = an;
+        }
+        if (j < 3) {
+#pragma unroll
+          for (int f = 0; f < NFRAG; ++f) b[f] = bn[f];
         }
       }
     };
@@ -335,6 +390,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       uint32_t rsn[NFRAG], rmn[NFRAG];
       load_b(min(kt + 1, klast), cbn, rsn, rmn);
       load_a(min(kt + 2, klast), nxt2);
+      // issue the loads here, a whole stage before they are needed: left to
+      // itself the scheduler sinks them to the end of the stage (to shorten
+      // register lifetimes), right before the wait for them
+      __builtin_amdgcn_sched_barrier(0);
       compute_stage(cur, cb, rs, rm);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       lds_barrier();
@@ -345,19 +404,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         rm[f] = rmn[f];
       }
     };
-    if constexpr (NK > 0) {
-#pragma unroll
-      for (int kt = 0; kt < NK; kt += 3) {
-        stage(kt, As0, As2);
-        if (kt + 1 < NK) stage(kt + 1, As1, As0);
-        if (kt + 2 < NK) stage(kt + 2, As2, As1);
-      }
-    } else {
-      for (int kt = 0; kt < nk; kt += 3) {
-        stage(kt, As0, As2);
-        if (kt + 1 < nk) stage(kt + 1, As1, As0);
-        if (kt + 2 < nk) stage(kt + 2, As2, As1);
-      }
+    for (int kt = 0; kt < nk; kt += 3) {
+      stage(kt, As0, As2);
+      if (kt + 1 < nk) stage(kt + 1, As1, As0);
+      if (kt + 2 < nk) stage(kt + 2, As2, As1);
     }
     // the repeated loads of the last stages must land before the epilogue
     // reuses the ring
@@ -391,8 +441,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           }
       }
       // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
-      const int col0 = ntile * (BN / 2) + wave * 32;
-      const bool cvalid = col0 < N / 2;
+      const int col0 = c0;
 #pragma unroll
       for (int q = 0; q < BM / 16; ++q) {
         const int rl = q * 16 + (lane_o >> 2);
@@ -416,8 +465,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           const int piece = (2 * f + (lg >> 1)) ^ (rl & 7);
           *reinterpret_cast<uint2*>(sub + rl * 128 + piece * 16 + (lg & 1) * 8) = d;
         }
-      const int col0 = ntile * BN + wave * 64;
-      const bool cvalid = col0 < N;
+      const int col0 = c0;
       // 8 rows x 128 bytes per wave-wide read: lane -> row lane/8, piece lane%8
 #pragma unroll
       for (int q = 0; q < BM / 8; ++q) {
@@ -453,18 +501,9 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   wgs = cdiv(wgs, NXCD) * NXCD;
   const dim3 grid(wgs), block(NTHREADS);
   LaunchScope ls(name, s);
-  const int nk = g.K / BK;
-  // the down projection of the common I = 768 runs fully unrolled (six
-  // stages); everything else uses the loop rolled by three
   auto go = [&](auto asym) {
     constexpr bool A = decltype(asym)::value;
-    if constexpr (!GATEUP) {
-      if (nk == 6) {
-        hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, 6>), grid, block, 0, s, g, n_ntiles);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, 0>), grid, block, 0, s, g, n_ntiles);
+    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A>), grid, block, 0, s, g, n_ntiles);
   };
   if (g.Wmin != nullptr)
     go(std::true_type{});

@@ -51,6 +51,7 @@ struct GroupedGemm {
   int rows_single;
   int E;
   int max_rows;            // upper bound of all rows (sizes the grid)
+  int a_rows;              // rows of A (bounds the activation reads)
   const uint8_t* W;        // [E][N][K/2] packed nibbles
   const uint16_t* Wscale;  // fp16 [E][N][K/G]
   const uint16_t* Wmin;    // fp16 [E][N][K/G] or NULL (symmetric)
