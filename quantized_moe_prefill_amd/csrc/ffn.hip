@@ -165,6 +165,17 @@ __device__ __forceinline__ void gather_rows(const GroupedGemm& g, int row0, int 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// What one tile of the expert GEMM needs besides the shared setup: its
+// rows, this lane's activation sources and weight offsets. (At namespace
+// scope: a class local to a kernel template keeps the compiler from emitting
+// the kernel's host-side launch stub.)
+struct GemmTile {
+  int row0, rows, c0;
+  bool cvalid;
+  uint32_t a_off[ALD];  // byte offsets of this lane's activation loads
+  uint32_t b_lane, s_lane;
+};
+
 template <bool GATEUP, bool ASYM>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
@@ -232,18 +243,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3);
   const int s_step = (BK / g.G) * 2;  // scale bytes per stage along a row
 
-  for (int tile = t_begin + wg_in_xcd; tile < t_end; tile += wgs_per_xcd) {
-    // per-lane constants are derived from an opaque copy of the lane index in
-    // every tile, so the compiler cannot compute them once up front and hold
-    // them in registers across the whole persistent loop
-    int lane_o = lane;
+  // Per-lane constants are derived from an opaque copy of the lane index, so
+  // the compiler cannot compute them once up front and hold them in
+  // registers across the whole persistent loop.
+  int lane_o = lane, r16, lg;
+  auto refresh_lane = [&]() {
     asm volatile("" : "+v"(lane_o));
-    const int r16 = lane_o & 15, lg = lane_o >> 4;
+    r16 = lane_o & 15;
+    lg = lane_o >> 4;
+  };
+  refresh_lane();
+  auto frow = [&](int f) { return GATEUP ? 16 * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f; };
+
+  // Fragment f of a wave covers weight rows c0 + frow(f) + 0..15 of
+  // the expert (gate/up: fragments 0, 1 are gate columns c0 + 16 f, 2, 3 the
+  // up rows of the same columns). Lane (r16, lg) reads row r16 of each
+  // fragment, K values [32 lg, 32 lg + 32) of every stage (16 bytes), which
+  // is also the K range its A fragments cover, so the two operands agree
+  // without any reordering: one per-lane offset plus a uniform offset per
+  // fragment and stage.
+  auto setup = [&](int tile, GemmTile& ts) {
     const int mtile = tile / n_ntiles;
     const int ntile = tile - mtile * n_ntiles;
-
-    // ---- which expert / rows ----
-    int e, row0, rows;
+    int e;
     if (g.counts != nullptr) {
       // largest e with s_scan[e] <= mtile (binary search over the E+1 prefixes)
       int lo = 0, hi = g.E;  // s_scan[lo] <= mtile < s_scan[hi]
@@ -253,150 +275,212 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       }
       e = lo;
       const int local = mtile - s_scan[e];
-      row0 = g.offsets[e] + local * BM;
-      rows = min(BM, g.counts[e] - local * BM);
+      ts.row0 = g.offsets[e] + local * BM;
+      ts.rows = min(BM, g.counts[e] - local * BM);
     } else {
       e = 0;
-      row0 = mtile * BM;
-      rows = min(BM, g.rows_single - row0);
+      ts.row0 = mtile * BM;
+      ts.rows = min(BM, g.rows_single - ts.row0);
     }
-
-    // ---- A: this lane's source offsets for its direct loads per stage.
-    // Load i of wave w fills rows 4*(ALD*w+i) .. +3; lane l covers row
-    // 4*(ALD*w+i) + l/16, LDS slot l%16, i.e. source chunk (l%16) ^ (row & 15).
-    // Rows past the expert's end read row 0 of the tile's source (finite
-    // data whose outputs are never stored).
-    // offsets are in 16-byte chunks (the host guarantees rows * K / 8 < 2^31)
-    uint32_t a_off[ALD];  // byte offsets into A
-    {
-      int src[ALD];
-      gather_rows<ALD>(g, row0, rows, 4 * ALD * wave + lg, 4, src);
+    // load i of wave w fills rows 4 (ALD w + i) .. +3; lane l covers row
+    // 4 (ALD w + i) + l/16, LDS slot l%16, i.e. source chunk (l%16) ^ rowswz(row)
+    int src[ALD];
+    gather_rows<ALD>(g, ts.row0, ts.rows, 4 * ALD * wave + lg, 4, src);
 #pragma unroll
-      for (int i = 0; i < ALD; ++i) {
-        const int r = 4 * (ALD * wave + i) + lg;
-        a_off[i] = (uint32_t)(src[i] * (K / 8) + (r16 ^ rowswz(r))) * 16u;
+    for (int i = 0; i < ALD; ++i) {
+      const int r = 4 * (ALD * wave + i) + lg;
+      ts.a_off[i] = (uint32_t)(src[i] * (K / 8) + (r16 ^ rowswz(r))) * 16u;
+    }
+    ts.c0 = GATEUP ? ntile * (BN / 2) + wave * 32 : ntile * BN + wave * 64;
+    ts.cvalid = ts.c0 < (GATEUP ? N / 2 : N);
+    const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
+    ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
+    ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
+  };
+  auto load_a = [&](const GemmTile& ts, int kt, uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < ALD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, ts.a_off[i], kt * BK * 2, 0, 0);
+  };
+  // weights and the group's scale (and min) of stage kt into registers
+  auto load_b = [&](const GemmTile& ts, int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f)
+      cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+      const int so = frow(f) * KG * 2 + kt * s_step;
+      rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, so, 0);
+      rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, ts.s_lane, so, 0) : 0u;
+    }
+  };
+
+  f32x4 acc[MSUB][NFRAG];
+
+  // One K stage from ring slot `as_base`: four 32-wide K steps x eight
+  // 16-row sub-tiles. Two waves share each SIMD, so the hardware interleaves
+  // one wave's dequant and LDS reads with the other's MFMAs. Every sub-tile
+  // is computed; rows past the end of an expert hold finite data whose
+  // results are never stored. The down GEMM swaps the operands
+  // (C^T = W A^T), so each lane ends up with four consecutive output
+  // columns of one row.
+  auto compute_stage = [&](const uint8_t* as_base, const u32x4* cb, const uint32_t* rs,
+                           const uint32_t* rm) {
+    f16x2 cs[NFRAG], cm[NFRAG];
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+      cs[f] = __builtin_bit_cast(f16x2, rs[f] * 0x10001u);
+      cm[f] = __builtin_bit_cast(f16x2, rm[f] * 0x10001u);
+    }
+    const uint8_t* ap[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ap[j] = as_base + r16 * (BK * 2) + (((lg * 4 + j) ^ rowswz(r16)) * 16);
+    auto read_a = [&](int j, int mi) {
+      return __builtin_bit_cast(f16x8, ld16(ap[j] + mi * 16 * BK * 2));
+    };
+    // weights of step 0 now; those of step j+1 are dequantized while step
+    // j's MFMAs run (one fragment behind each of the first sub-tiles)
+    f16x8 b[NFRAG];
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][0], cs[f], cm[f]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 bn[NFRAG];
+      f16x8 a = read_a(j, 0);
+#pragma unroll
+      for (int mi = 0; mi < MSUB; ++mi) {
+        f16x8 an;
+        if (mi + 1 < MSUB) an = read_a(j, mi + 1);
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f)
+          acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
+                              : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
+        if (j < 3 && mi < NFRAG) bn[mi] = dequant8_f16<ASYM>(cb[mi][j + 1], cs[mi], cm[mi]);
+        if (mi + 1 < MSUB) a = an;
+      }
+      if (j < 3) {
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) b[f] = bn[f];
       }
     }
+  };
 
-    // ---- this wave's weight rows: fragment f covers rows c0 + frow(f) +
-    // 0..15 of the expert (gate/up: fragments 0, 1 are gate columns c0 + 16 f,
-    // 2, 3 the up rows of the same columns). Lane (r16, lg) reads row r16 of
-    // each fragment, K values [32 lg, 32 lg + 32) of every stage (16 bytes),
-    // which is also the K range its A fragments cover, so the two operands
-    // agree without any reordering: one per-lane offset plus a uniform offset
-    // per fragment and stage.
-    const int c0 = GATEUP ? ntile * (BN / 2) + wave * 32 : ntile * BN + wave * 64;
-    const bool cvalid = c0 < (GATEUP ? N / 2 : N);
-    const int wrow0 = e * N + (cvalid ? c0 : 0) + r16;
-    const uint32_t b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
-    const uint32_t s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
-    auto frow = [&](int f) { return GATEUP ? 16 * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f; };
-
-    auto load_a = [&](int kt, uint8_t* dst) {
+  // Epilogue. Gate/up: h = silu(g) * u, stored as fp16 in kperm chunk order
+  // through this wave's LDS sub-tile (128 rows x 64 B, in As2 or Ex, which
+  // the next tile's first two stages leave alone) so that it leaves as
+  // 16-byte row pieces. Down: the same, in two halves of 64 rows.
+  auto epilogue = [&](const GemmTile& ts) {
+    int rq = 4 * lg, rr = r16, row0 = ts.row0, rows = ts.rows;
+    asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
+    if (GATEUP) {
+      uint8_t* sub = (wave < 4 ? As2 : Ex) + (wave & 3) * (BM * 64);
+      // the 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four
+      // row groups of one write land in different banks
 #pragma unroll
-      for (int i = 0; i < ALD; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, a_off[i], kt * BK * 2, 0, 0);
-    };
-    // weights and the group's scale (and min) of stage kt into registers
-    auto load_b = [&](int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
+      for (int j = 0; j < 2; ++j) {
+        const int pc = 8 * (r16 >> 3) + kpos(r16 & 7);  // column in its pair of pieces
 #pragma unroll
-      for (int f = 0; f < NFRAG; ++f)
-        cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rW, b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+        for (int mi = 0; mi < MSUB; ++mi)
 #pragma unroll
-      for (int f = 0; f < NFRAG; ++f) {
-        const int so = frow(f) * KG * 2 + kt * s_step;
-        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, s_lane, so, 0);
-        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, s_lane, so, 0) : 0u;
+          for (int v = 0; v < 4; ++v) {
+            const int rl = mi * 16 + rq + v;
+            const float h = silu(acc[mi][j][v]) * acc[mi][j + 2][v];
+            const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
+            *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
+                (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
+          }
       }
-    };
+      lds_wave_sync();
+      // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
+#pragma unroll
+      for (int q = 0; q < BM / 16; ++q) {
+        const int rl = q * 16 + (lane_o >> 2);
+        const int p = lane_o & 3;
+        const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
+        if (ts.cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + ts.c0 + p * 8, d);
+      }
+    } else {
+      // y in two halves of 64 rows: this wave's half sub-tile is 64 rows x
+      // 128 B (its 64 columns) in As2 or Ex; lane (r16, lg) holds columns
+      // 16 f + 4 lg .. +3 of row 16 mi + r16, and the 16-byte piece p of row
+      // r sits at p ^ (r & 7)
+      uint8_t* sub = (wave < 4 ? As2 : Ex) + (wave & 3) * (64 * 128);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int mh = 0; mh < MSUB / 2; ++mh) {
+          const int mi = half * (MSUB / 2) + mh;
+          const int rl = mh * 16 + rr;  // row within the half
+#pragma unroll
+          for (int f = 0; f < NFRAG; ++f) {
+            uint2 d;
+            d.x = pack_f16x2(acc[mi][f][0], acc[mi][f][1]);
+            d.y = pack_f16x2(acc[mi][f][2], acc[mi][f][3]);
+            const int piece = (2 * f + (lg >> 1)) ^ (rl & 7);
+            *reinterpret_cast<uint2*>(sub + rl * 128 + piece * 16 + (lg & 1) * 8) = d;
+          }
+        }
+        lds_wave_sync();
+        // 8 rows x 128 bytes per wave-wide read: lane -> row lane/8, piece lane%8
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int rl = q * 8 + (lane_o >> 3);
+          const int p = lane_o & 7;
+          const u32x4 d = ld16(sub + rl * 128 + (p ^ (rl & 7)) * 16);
+          const int row = half * 64 + rl;
+          if (ts.cvalid && row < rows) st16(g.C + (int64_t)(row0 + row) * g.ldc + ts.c0 + p * 8, d);
+        }
+      }
+    }
+  };
 
-    f32x4 acc[MSUB][NFRAG];
+  // ---- persistent loop. K loop: activations two stages ahead in the LDS
+  // ring, weights one stage ahead in registers. Within a stage the weight
+  // loads are issued before the activation loads, so "at most ALD loads
+  // outstanding" at the end of stage s means: stage s+1's activations and
+  // weights have landed (loads complete in issue order). Every stage issues
+  // the same loads (past the last stage they repeat it, into a slot nobody
+  // reads), so the waits are the same at every stage and the compiler's own
+  // wait bookkeeping stays exact. The next tile's first two stages are loaded
+  // while this tile's epilogue runs: weights and stage 0 before it, stage 1
+  // after its stores, so that "at most ALD outstanding" again means stage 0
+  // has landed.
+  int tile = t_begin + wg_in_xcd;
+  if (tile >= t_end) return;
+  const int klast = nk - 1;
+  GemmTile cur;
+  setup(tile, cur);
+  u32x4 cb[NFRAG];
+  uint32_t rs[NFRAG], rm[NFRAG];
+  load_b(cur, 0, cb, rs, rm);
+  load_a(cur, 0, As0);
+  load_a(cur, min(1, klast), As1);
+  while (true) {
+    refresh_lane();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
+    lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // One K stage from ring slot `buf`: four 32-wide K steps x eight 16-row
-    // sub-tiles. Two waves share each SIMD, so the hardware interleaves one
-    // wave's dequant and LDS reads with the other's MFMAs: keep the live set
-    // small (weights dequantized just in time, A read one sub-tile ahead).
-    // Every sub-tile is computed; rows past the end of an expert hold finite
-    // data whose results are never stored. The down GEMM swaps the operands
-    // (C^T = W A^T), so each lane ends up with four consecutive output
-    // columns of one row.
-    auto compute_stage = [&](const uint8_t* as_base, const u32x4* cb, const uint32_t* rs,
-                             const uint32_t* rm) {
-      f16x2 cs[NFRAG], cm[NFRAG];
-#pragma unroll
-      for (int f = 0; f < NFRAG; ++f) {
-        cs[f] = __builtin_bit_cast(f16x2, rs[f] * 0x10001u);
-        cm[f] = __builtin_bit_cast(f16x2, rm[f] * 0x10001u);
-      }
-      const uint8_t* ap[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ap[j] = as_base + r16 * (BK * 2) + (((lg * 4 + j) ^ rowswz(r16)) * 16);
-      auto read_a = [&](int j, int mi) {
-        return __builtin_bit_cast(f16x8, ld16(ap[j] + mi * 16 * BK * 2));
-      };
-      // weights of step 0 now; those of step j+1 are dequantized while step
-      // j's MFMAs run (one fragment behind each of the first sub-tiles)
-      f16x8 b[NFRAG];
-#pragma unroll
-      for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][0], cs[f], cm[f]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f16x8 bn[NFRAG];
-        f16x8 a = read_a(j, 0);
-#pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi) {
-          f16x8 an;
-          if (mi + 1 < MSUB) an = read_a(j, mi + 1);
-#pragma unroll
-          for (int f = 0; f < NFRAG; ++f)
-            acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
-                                : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
-          if (j < 3 && mi < NFRAG) bn[mi] = dequant8_f16<ASYM>(cb[mi][j + 1], cs[mi], cm[mi]);
-          if (mi + 1 < MSUB) a = an;
-        }
-        if (j < 3) {
-#pragma unroll
-          for (int f = 0; f < NFRAG; ++f) b[f] = bn[f];
-        }
-      }
-    };
-
-    // ---- K loop: activations two stages ahead in the LDS ring, weights one
-    // stage ahead in registers. Within a stage the weight loads are issued
-    // before the activation loads, so "at most ALD loads outstanding" at the
-    // end of stage s means: stage s+1's activations and weights have landed
-    // (loads complete in issue order). Every stage issues the same loads (past
-    // the last stage they repeat it, into a slot nobody reads), so the waits
-    // are the same at every stage and the compiler's own wait bookkeeping
-    // stays exact.
-    lds_barrier();  // the previous tile's epilogue is done with the LDS
-    const int klast = nk - 1;
-    u32x4 cb[NFRAG];
-    uint32_t rs[NFRAG], rm[NFRAG];
-    load_b(0, cb, rs, rm);
-    load_a(0, As0);
-    load_a(min(1, klast), As1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
-    lds_barrier();
     // stage kt reads ring slot kt % 3 and loads stage kt + 2 into slot (kt + 2) % 3
-    auto stage = [&](int kt, const uint8_t* cur, uint8_t* nxt2) {
+    auto stage = [&](int kt, const uint8_t* curs, uint8_t* nxt2) {
       u32x4 cbn[NFRAG];
       uint32_t rsn[NFRAG], rmn[NFRAG];
-      load_b(min(kt + 1, klast), cbn, rsn, rmn);
-      load_a(min(kt + 2, klast), nxt2);
+      load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
+      load_a(cur, min(kt + 2, klast), nxt2);
       // issue the loads here, a whole stage before they are needed: left to
       // itself the scheduler sinks them to the end of the stage (to shorten
       // register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(cur, cb, rs, rm);
+      compute_stage(curs, cb, rs, rm);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       lds_barrier();
+      // the hand-over of the next stage's registers stays here: moved up into
+      // the stage it would wait for loads that were just issued
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
         cb[f] = cbn[f];
@@ -409,72 +493,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       if (kt + 1 < nk) stage(kt + 1, As1, As0);
       if (kt + 2 < nk) stage(kt + 2, As2, As1);
     }
-    // the repeated loads of the last stages must land before the epilogue
-    // reuses the ring
+    // the repeated loads of the last stages land before the ring is reused
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-    // ---- epilogue: results to this wave's LDS sub-tile, then whole row
-    // pieces to global memory. The last barrier of the K loop has released
-    // the activation ring.
-    // Opaque redefinitions of the per-lane row offsets: they are constants
-    // per lane, and without this the compiler computes all row indices once
-    // at kernel start and holds them in registers through the K loop.
-    int rq = 4 * lg, rr = r16;
-    asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
-    uint8_t* sub = (wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? As2 : Ex) + (wave & 1) * SUB_BYTES;
-    if (GATEUP) {
-      // h (128 rows x 32 columns) in kperm chunk order, 64 bytes per row; the
-      // 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four row
-      // groups of one write land in different banks
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pc = 8 * (r16 >> 3) + kpos(r16 & 7);  // column in its 16-wide pair of pieces
-#pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rl = mi * 16 + rq + v;
-            const float h = silu(acc[mi][j][v]) * acc[mi][j + 2][v];
-            const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
-            *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
-                (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
-          }
-      }
-      // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
-      const int col0 = c0;
-#pragma unroll
-      for (int q = 0; q < BM / 16; ++q) {
-        const int rl = q * 16 + (lane_o >> 2);
-        const int p = lane_o & 3;
-        const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
-        if (cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + col0 + p * 8, d);
-      }
-    } else {
-      // y (128 rows x 64 columns), 128 bytes per row; lane (r16, lg) holds
-      // columns 16 f + 4 lg .. +3 of row 16 mi + r16. The 16-byte piece p of
-      // row r sits at p ^ (r & 7), so the 16 rows of one write spread over
-      // all banks.
-#pragma unroll
-      for (int mi = 0; mi < MSUB; ++mi)
-#pragma unroll
-        for (int f = 0; f < NFRAG; ++f) {
-          const int rl = mi * 16 + rr;
-          uint2 d;
-          d.x = pack_f16x2(acc[mi][f][0], acc[mi][f][1]);
-          d.y = pack_f16x2(acc[mi][f][2], acc[mi][f][3]);
-          const int piece = (2 * f + (lg >> 1)) ^ (rl & 7);
-          *reinterpret_cast<uint2*>(sub + rl * 128 + piece * 16 + (lg & 1) * 8) = d;
-        }
-      const int col0 = c0;
-      // 8 rows x 128 bytes per wave-wide read: lane -> row lane/8, piece lane%8
-#pragma unroll
-      for (int q = 0; q < BM / 8; ++q) {
-        const int rl = q * 8 + (lane_o >> 3);
-        const int p = lane_o & 7;
-        const u32x4 d = ld16(sub + rl * 128 + (p ^ (rl & 7)) * 16);
-        if (cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + col0 + p * 8, d);
-      }
+    const int next = tile + wgs_per_xcd;
+    const bool has_next = next < t_end;
+    GemmTile nts;
+    refresh_lane();
+    if (has_next) {
+      setup(next, nts);
+      load_b(nts, 0, cb, rs, rm);
+      load_a(nts, 0, As0);
     }
+    epilogue(cur);
+    if (!has_next) break;
+    load_a(nts, min(1, klast), As1);
+    cur = nts;
+    tile = next;
   }
 }
 
