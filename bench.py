@@ -148,6 +148,38 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8):
     }
 
 
+def stack_cpu_baseline(cfg, layers_cpu, x, rows=32, layers=2):
+    """Stacked workload: the oracle on a bounded sample (`rows` tokens through
+    `layers` layers, the experts those tokens need dequantized per layer),
+    scaled to tokens/s of the whole stack (tokens interact only within a
+    row, so the work per token is the same for every row)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    xb = x[:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    for li in layers_cpu[:layers]:
+        w = li.norm_weight.numpy()
+        xn = oracle.round_to_bf16(oracle.rmsnorm(xb, w, cfg.rms_eps))
+        res = oracle.moe_layer_rows(xn, np.arange(rows), li, cfg.k, cfg.G, cfg.quant,
+                                    residual_bits=xb)
+        xb = oracle.round_to_bf16(res["out"])
+    dt = time.perf_counter() - t0
+    per_token_stack = dt / rows * (cfg.n_layers / layers)
+    return {
+        "value": round(1.0 / per_token_stack, 3),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{rows} tokens through {layers} of the {cfg.n_layers} layers (RMSNorm + "
+                  f"routed experts + shared expert + residual, the needed experts dequantized "
+                  f"per layer) in {dt:.1f} s, scaled to the whole stack",
+    }
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -160,20 +192,34 @@ def main():
     import torch
 
     import quantized_moe_prefill_amd as qm
-    from synth import get_config, make_layer, make_tokens
+    from synth import get_config, make_layer, make_stack_layer, make_tokens
 
     cfg = get_config(a.workload)
     T = a.T or cfg.T
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    li = make_layer(cfg, device=dev)
+    stacked = cfg.n_layers > 1
     x = make_tokens(cfg, device=dev, rows=T)
-    layer = qm.MoELayer(cfg, li, dev, T)
-    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    if stacked:
+        layers = [make_stack_layer(cfg, l, device=dev) for l in range(cfg.n_layers)]
+        stack = qm.MoEStack(cfg, layers, dev, eps=cfg.rms_eps, chunk=min(cfg.chunk or T, T))
+        xs = torch.empty_like(x)
+
+        def step():
+            xs.copy_(x)
+            stack.forward(xs)
+        li = layers[0]
+    else:
+        li = make_layer(cfg, device=dev)
+        layer = qm.MoELayer(cfg, li, dev, T)
+        out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            layer.forward(x, out=out)
     torch.cuda.synchronize()
 
     for _ in range(a.warmup):
-        layer.forward(x, out=out)
+        step()
     torch.cuda.synchronize()
 
     # timed region: K steps, bracketed by synchronizations
@@ -183,7 +229,7 @@ def main():
     t_wall = time.perf_counter()
     e0.record(st)
     for _ in range(a.steps):
-        layer.forward(x, out=out)
+        step()
     e1.record(st)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -191,29 +237,47 @@ def main():
 
     # per-kernel durations: the same K steps again with HIP events around
     # every kernel launch (recorded on the launch stream by the library)
-    n_kernels = 16
-    qm.profile_enable(a.steps * n_kernels)
+    launches_per_step = 16 * max(1, cfg.n_layers) * max(1, -(-T // (cfg.chunk or T)))
+    qm.profile_enable(a.steps * launches_per_step)
     for _ in range(a.steps):
-        layer.forward(x, out=out)
+        step()
     torch.cuda.synchronize()
     kernels = {}
-    for name in KERNELS:
+    for name in KERNELS + ("rmsnorm",):
         n, tot = qm.profile_read(name)
         if n:
             kernels[name] = round(tot / n * 1000.0, 2)  # microseconds per launch
     qm.profile_enable(0)
 
+    # the work of one layer application over n rows
+    def layer_flops(n):
+        return cfg.mfma_flops(n)
+
+    n_apps = cfg.n_layers if stacked else 1
     P = T * cfg.k
-    gu_flops = 4.0 * cfg.H * cfg.I * P
+    chunk_rows = min(cfg.chunk or T, T)
+    gu_launch_rows = chunk_rows if stacked else T
+    gu_flops = 4.0 * cfg.H * cfg.I * gu_launch_rows * cfg.k
     gu_us = kernels.get("gateup_gemm")
     achieved = gu_flops / (gu_us * 1e-6) / 1e12 if gu_us else None
-    layer_tflops = cfg.mfma_flops(T) / (ms * 1e-3) / 1e12
-    # algorithmic HBM bytes of the layer: every active expert's packed weights
-    # (all experts are active at this T) + router + x in + out
-    weight_bytes = cfg.E * cfg.expert_bytes() + cfg.shared_bytes()
-    io_bytes = cfg.E * cfg.H * 4 + 2 * T * cfg.H * 2
+    total_flops = layer_flops(T) * n_apps
+    layer_tflops = total_flops / (ms * 1e-3) / 1e12
+    # algorithmic HBM bytes: the packed weights of every expert that received
+    # tokens (all of them at large T), router, shared expert, x in, out
+    with torch.no_grad():
+        logits, ids, _, _ = qm.moe_route(qm.shape_of(cfg), x, li.w_router, li.router_bias,
+                                         li.shared_gate)
+        active = int(torch.unique(ids).numel())
+    weight_bytes = (active * cfg.expert_bytes() + cfg.shared_bytes()) * n_apps
+    io_bytes = (cfg.E * cfg.H * 4) * n_apps + 2 * T * cfg.H * 2
     hbm_gbs = (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9
 
+    desc = (f"{cfg.name}: {'a stack of %d ' % cfg.n_layers if stacked else 'one '}MoE FFN "
+            f"layer{'s with RMSNorm + residual, in %d-row chunks' % chunk_rows if stacked else ''}"
+            f", T={T}, hidden={cfg.H}, experts={cfg.E}, top-{cfg.k}, inter={cfg.I}, "
+            f"{cfg.quant} int4 group {cfg.G}"
+            + (f", shared expert {cfg.shared_I}" if cfg.shared_I else "")
+            + (", Zipf router bias" if cfg.zipf_bias else ""))
     rec = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -228,14 +292,14 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: one MoE FFN layer, T={T}, hidden={cfg.H}, experts={cfg.E}, "
-                        f"top-{cfg.k}, inter={cfg.I}, {cfg.quant} int4 group {cfg.G}"
-                        + (f", shared expert {cfg.shared_I}" if cfg.shared_I else ""),
+            "workload": desc,
             "T": T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I,
             "group": cfg.G, "quant": cfg.quant, "shared_inter": cfg.shared_I,
+            "layers": cfg.n_layers,
         },
         "layer_tflops": round(layer_tflops, 1),
         "layer_mfma_frac": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "active_experts": active,
         "layer_hbm_gbs": round(hbm_gbs, 1),
         "layer_hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "kernel_us": kernels,
@@ -262,7 +326,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not a.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(cfg, li, x)
+        if stacked:
+            rec["cpu_baseline"] = stack_cpu_baseline(cfg, [l.to("cpu") for l in layers[:2]], x)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(cfg, li, x)
     print(json.dumps(rec), flush=True)
 
 

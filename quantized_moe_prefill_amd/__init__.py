@@ -7,14 +7,14 @@ library; the first call does, and fails loudly if it has not been built.
 from ._native import (MOE_OK, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
                       MOE_ERR_WORKSPACE_TOO_SMALL, MOE_WS_EXPERT_FFN, MOE_WS_LAYER,
                       MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeError, lib)
-from .ops import (Experts, MoELayer, make_shape, moe_combine, moe_expert_ffn, moe_layer_forward,
+from .ops import (Experts, MoELayer, MoEStack, make_shape, moe_combine, moe_expert_ffn, moe_layer_forward,
                   moe_permute, moe_rmsnorm, moe_route, moe_workspace_size, profile_enable,
                   profile_read, profile_reset, shape_of, workspace)
 
 __all__ = [
     "MOE_OK", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
     "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_WS_EXPERT_FFN", "MOE_WS_LAYER", "MOE_WS_PERMUTE",
-    "MOE_WS_ROUTE", "MoeError", "lib", "Experts", "MoELayer", "make_shape", "moe_combine",
+    "MOE_WS_ROUTE", "MoeError", "lib", "Experts", "MoELayer", "MoEStack", "make_shape", "moe_combine",
     "moe_expert_ffn", "moe_layer_forward", "moe_permute", "moe_rmsnorm", "moe_route",
     "moe_workspace_size", "profile_enable", "profile_read", "profile_reset", "shape_of",
     "workspace",

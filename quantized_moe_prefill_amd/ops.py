@@ -194,16 +194,55 @@ def profile_read(kernel: str):
 
 class MoELayer:
     """One layer's weights resident on the device, with a reusable
-    workspace, for repeated moe_layer_forward calls."""
+    workspace (its own, or one shared with other layers of the same shape),
+    for repeated moe_layer_forward calls."""
 
-    def __init__(self, cfg, li, device, T_max: int):
+    def __init__(self, cfg, li, device, T_max: int, ws=None):
         self.cfg = cfg
         self.shape = shape_of(cfg)
         self.li = li
         self.experts = Experts(li)
-        self.ws = workspace(self.shape, T_max, device)
+        self.ws = ws if ws is not None else workspace(self.shape, T_max, device)
 
     def forward(self, x, residual=None, out=None):
         return moe_layer_forward(self.shape, x, self.li.w_router, self.li.router_bias,
                                  self.li.shared_gate, self.experts, residual=residual, out=out,
                                  ws=self.ws)
+
+
+class MoEStack:
+    """A pre-norm stack of MoE FFN layers resident on the device (the
+    attention blocks of the model are not part of it):
+
+        for each chunk of `chunk` rows, for each layer l:
+            xn = moe_rmsnorm(x, g_l)
+            x  = moe_layer_forward(xn, ..., residual=x, out=x)
+
+    i.e. x <- x + MoE_l(RMSNorm_l(x)) with a bf16 residual stream, chunk by
+    chunk as a prefill engine processes a long prompt. Orchestration only:
+    every step runs in the library's kernels; the layers share one
+    workspace."""
+
+    def __init__(self, cfg, layers, device, eps: float = 1e-6, chunk: int = 0):
+        self.cfg = cfg
+        self.eps = eps
+        self.chunk = chunk if chunk > 0 else cfg.T
+        shape = shape_of(cfg)
+        self.ws = workspace(shape, self.chunk, device)
+        self.layers = [MoELayer(cfg, li, device, self.chunk, ws=self.ws) for li in layers]
+        self.xn = torch.empty((self.chunk, cfg.H), dtype=torch.bfloat16, device=device)
+
+    def layer_step(self, layer: "MoELayer", xc: torch.Tensor) -> torch.Tensor:
+        """One layer on one chunk, in place: xc <- xc + MoE(RMSNorm(xc))."""
+        xn = self.xn[: xc.shape[0]]
+        moe_rmsnorm(xc, layer.li.norm_weight, self.eps, out=xn)
+        layer.forward(xn, residual=xc, out=xc)
+        return xc
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        """x [T][H] bf16, updated in place and returned."""
+        for r0 in range(0, x.shape[0], self.chunk):
+            xc = x[r0:r0 + self.chunk]
+            for layer in self.layers:
+                self.layer_step(layer, xc)
+        return x
