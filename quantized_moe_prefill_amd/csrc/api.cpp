@@ -214,9 +214,10 @@ static moe_status_t route_impl(const Shape& s, int64_t T, const uint16_t* x, con
                                const float* bias, const float* sg, float* logits,
                                int32_t* ids, float* tw, float* sw, uint16_t* split,
                                float* partial, hipStream_t st) {
-  QMOE_HIP(launch_router_split(wr, sg, s.E, s.H, split, st), "router_split launch");
-  QMOE_HIP(launch_router_topk(x, split, partial, bias, (int)T, s.H, s.E, s.k, sg != nullptr,
-                              logits, ids, tw, sw, st),
+  if (!router_uses_gemv((int)T))
+    QMOE_HIP(launch_router_split(wr, sg, s.E, s.H, split, st), "router_split launch");
+  QMOE_HIP(launch_router_topk(x, wr, sg, split, partial, bias, (int)T, s.H, s.E, s.k, logits, ids,
+                              tw, sw, st),
            "router launch");
   return MOE_OK;
 }
@@ -227,7 +228,6 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
                              uint16_t* ysh, uint16_t* x16, uint16_t* h, uint16_t* hs,
                              hipStream_t st) {
   const int P = (int)(T * s.k);
-  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
   GroupedGemm g{};
   g.A = x16;
   g.gather = sorted;
@@ -245,10 +245,21 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   g.G = s.G;
   g.C = h;
   g.ldc = s.I;
+  g.expect_rows = (int)T;
+  // the weight-streaming gate/up reads the bf16 activations itself; the tiled
+  // one wants them as fp16 in kperm order
+  const bool x_direct = gateup_streams(g);
+  if (x_direct) {
+    g.A = x;
+    g.a_bf16 = true;
+  } else {
+    QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+  }
   QMOE_HIP(launch_gateup(g, st), "gateup launch");
 
   GroupedGemm d = g;
   d.A = h;
+  d.a_bf16 = false;
   d.a_rows = P;
   d.gather = nullptr;
   d.W = w->w2;
@@ -262,7 +273,8 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
 
   if (s.Is > 0) {
     GroupedGemm gs{};
-    gs.A = x16;
+    gs.A = x_direct ? x : x16;
+    gs.a_bf16 = x_direct;
     gs.gather = nullptr;
     gs.gather_div = 1;
     gs.counts = nullptr;
@@ -279,9 +291,16 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
     gs.G = s.G;
     gs.C = hs;
     gs.ldc = s.Is;
+    gs.expect_rows = (int)T;
+    if (gs.a_bf16 && !gateup_streams(gs)) {
+      QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+      gs.A = x16;
+      gs.a_bf16 = false;
+    }
     QMOE_HIP(launch_gateup(gs, st, "shared_gateup_gemm"), "shared gateup launch");
     GroupedGemm ds = gs;
     ds.A = hs;
+    ds.a_bf16 = false;
     ds.W = w->s2;
     ds.Wscale = w->s2_scale;
     ds.Wmin = s.asym ? w->s2_min : nullptr;

@@ -89,4 +89,27 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier for LDS hand-offs only. __syncthreads() also orders
+// global memory, which on this target means waiting for every outstanding
+// vector memory operation (loads included) first and would drain the load
+// pipeline; the callers wait for exactly the loads
+// they need (s_waitcnt vmcnt) before this barrier. It completes this wave's
+// own LDS operations, and the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The LDS writes of this wave are complete and visible to its own later
+// reads (a wave's LDS operations complete in order; the wait also keeps the
+// compiler from reordering across it).
+__device__ __forceinline__ void lds_wave_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace qmoe

@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dequant.h"
 #include "kernels.h"
 
 namespace qmoe {
@@ -66,32 +67,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 // The builtin form keeps the compiler's own wait bookkeeping exact.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
-// Eight consecutive 4-bit weights (one 32-bit word) of one row -> eight fp16
-// weights in the kperm chunk order. OR-ing a nibble n into the fp16 pattern
-// 0x6400 gives exactly 1024 + n; subtracting 1032 (symmetric) or 1024
-// (asymmetric) is exact, and the final multiply (or fused multiply-add with
-// the min) rounds once.
-template <bool ASYM>
-__device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s2, f16x2 m2) {
-  const f16x2 off = ASYM ? f16x2{(_Float16)1024.0f, (_Float16)1024.0f}
-                         : f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
-  // the two constants live in registers so that mask-and-or is a single
-  // v_and_or_b32 (VOP3 takes no literal and at most one scalar operand on
-  // gfx9): the mask in a scalar register, the fp16 pattern in a vector one
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
-  uint32_t magic = 0x64006400u;
-  asm("" : "+v"(magic));
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((w >> (4 * i)) & mask) | magic;  // (1024 + n_i, 1024 + n_{i+4})
-    const f16x2 n = __builtin_bit_cast(f16x2, t) - off;
-    const f16x2 v = ASYM ? __builtin_elementwise_fma(n, s2, m2) : n * s2;
-    o[i] = __builtin_bit_cast(uint32_t, v);
-  }
-  return __builtin_bit_cast(f16x8, o);
-}
-
 // bf16 activations -> fp16 in kperm chunk order (exact for |x| < 65504).
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ out,
@@ -109,29 +84,6 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
-
-// Workgroup barrier for LDS hand-offs only. __syncthreads() also orders
-// global memory, which on this target means waiting for every outstanding
-// vector memory operation (loads included) first and would drain the load
-// pipeline at every K stage; here the callers wait for exactly the loads
-// they need (s_waitcnt vmcnt) before this barrier. It completes this wave's
-// own LDS operations, and the empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// The LDS writes of this wave are complete and visible to its own later
-// reads (a wave's LDS operations complete in order; the wait also keeps the
-// compiler from reordering across it).
-__device__ __forceinline__ void lds_wave_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-}
 
 // Slot swizzle of the activation tiles: chunk c of row r sits in slot
 // c ^ rowswz(r), the row's low four bits with their two halves swapped. A
@@ -559,10 +511,20 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, int64_t n, hipStrea
   return hipGetLastError();
 }
 
+// A few rows per group: the layer is bound by reading the weights once, and
+// the weight-streaming kernel spreads them over the whole chip.
+static bool use_stream(const GroupedGemm& g, bool gateup) {
+  return g.expect_rows > 0 && g.expect_rows <= kStreamMaxRows && stream_supported(g, gateup);
+}
+
+bool gateup_streams(const GroupedGemm& g) { return use_stream(g, true); }
+
 hipError_t launch_gateup(const GroupedGemm& g, hipStream_t s, const char* name) {
+  if (use_stream(g, true)) return launch_stream(g, true, s, name);
   return launch_grouped<true>(g, s, name);
 }
 hipError_t launch_down(const GroupedGemm& g, hipStream_t s, const char* name) {
+  if (use_stream(g, false)) return launch_stream(g, false, s, name);
   return launch_grouped<false>(g, s, name);
 }
 

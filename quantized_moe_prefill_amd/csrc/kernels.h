@@ -26,11 +26,16 @@ size_t router_split_bytes(int E, bool has_shared, int H);
 size_t router_partial_bytes(int T, int E, bool has_shared, int H);
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
                                uint16_t* split, hipStream_t s);
-// router GEMM into `partial`, then per-token logits, top-k and softmax
-hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, float* partial,
-                              const float* bias, int T, int H, int E, int k, bool has_shared,
-                              float* logits, int32_t* ids, float* topk_w, float* shared_w,
-                              hipStream_t s);
+// At most this many tokens: the router logits are an fp32 matrix-vector
+// product straight from the fp32 router rows (no split matrix needed).
+constexpr int kRouterGemvT = 16;
+bool router_uses_gemv(int T);
+// router GEMM (or matrix-vector product) into `partial`, then per-token
+// logits, top-k and softmax; `split` is only read when !router_uses_gemv(T)
+hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const float* shared_gate,
+                              const uint16_t* split, float* partial, const float* bias, int T,
+                              int H, int E, int k, float* logits, int32_t* ids, float* topk_w,
+                              float* shared_w, hipStream_t s);
 
 // ---- permutation ------------------------------------------------------
 // scratch: per-chunk expert histograms, permute_ws_bytes(P, E) bytes
@@ -58,12 +63,26 @@ struct GroupedGemm {
   int N, K, G;
   uint16_t* C;             // output rows, fp16, leading dimension ldc
   int ldc;
+  // Rows per group the caller expects at most (the token count for routed
+  // groups and for the shared expert). At most kStreamMaxRows selects the
+  // weight-streaming kernel; any actual count is still computed correctly.
+  int expect_rows;
+  // A holds bf16 rows in natural order (the weight-streaming gate/up kernel
+  // converts them itself); otherwise fp16 in kperm chunk order
+  bool a_bf16;
 };
+constexpr int kStreamMaxRows = 16;
 // gate/up with fused SwiGLU: N = 2I weight rows, writes h = silu(g)*u
 // (fp16, kperm chunk order), ldc = I.
 hipError_t launch_gateup(const GroupedGemm& g, hipStream_t s, const char* name = "gateup_gemm");
 // down projection: N = H weight rows, writes y (fp16, natural order), ldc = H.
 hipError_t launch_down(const GroupedGemm& g, hipStream_t s, const char* name = "down_gemm");
+// Weight-streaming form of the two GEMMs above for a few rows per group.
+bool stream_supported(const GroupedGemm& g, bool gateup);
+// launch_gateup(g) would run the weight-streaming kernel (which can read bf16
+// activations directly: a_bf16)
+bool gateup_streams(const GroupedGemm& g);
+hipError_t launch_stream(const GroupedGemm& g, bool gateup, hipStream_t s, const char* name);
 
 // ---- combine / norm ---------------------------------------------------
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const float* topk_w,

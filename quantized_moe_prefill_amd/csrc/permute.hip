@@ -12,6 +12,9 @@
 //  permute_scatter: each workgroup sums the histograms (all chunks: counts
 //                   and offsets; earlier chunks: its own base per expert) and
 //                   writes sorted_pairs[base + rank] = p, inv[p] = that position
+//  permute_small  : at most one chunk of pairs: both passes in one workgroup
+//                   (the ranks stay in registers, the scan over the experts in
+//                   LDS), one launch
 #include "common.h"
 #include "kernels.h"
 
@@ -30,17 +33,18 @@ __device__ __forceinline__ int count_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ __launch_bounds__(PT) void permute_rank_kernel(const int32_t* __restrict__ ids, int P,
-                                                          int E, int nbits,
-                                                          int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ rank_out) {
-  __shared__ int cnt[4][PMAXE];
+// Ranks of this workgroup's chunk of PCH pairs (chunk c): ev[s] = expert of
+// pair p0 + 64 s (-1 if none or out of range), rk[s] = its rank among the
+// chunk's pairs of that expert; afterwards cnt[w][e] holds the number of
+// pairs of e in the waves before w and the return value, for thread e < E,
+// the chunk's total of e. Ends with the workgroup synchronized.
+__device__ __forceinline__ int chunk_ranks(const int32_t* __restrict__ ids, int P, int E, int nbits,
+                                           int chunk, int (*cnt)[PMAXE], int* ev, int* rk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < 4 * PMAXE; i += PT) (&cnt[0][0])[i] = 0;
   __syncthreads();
 
-  const int p0 = blockIdx.x * PCH + wave * PSEG * 64 + lane;
-  int ev[PSEG], rk[PSEG];
+  const int p0 = chunk * PCH + wave * PSEG * 64 + lane;
 #pragma unroll
   for (int s = 0; s < PSEG; ++s) {
     const int p = p0 + s * 64;
@@ -71,18 +75,30 @@ __global__ __launch_bounds__(PT) void permute_rank_kernel(const int32_t* __restr
     rk[s] = c + below;
   }
   __syncthreads();
-  // exclusive prefix over the waves per expert; the chunk's histogram
-  for (int e = tid; e < E; e += PT) {
-    int run = 0;
+  // exclusive prefix over the waves per expert (E <= PT: one expert per thread)
+  int run = 0;
+  if (tid < E) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int c = cnt[w][e];
-      cnt[w][e] = run;
+      const int c = cnt[w][tid];
+      cnt[w][tid] = run;
       run += c;
     }
-    hist[(int64_t)blockIdx.x * E + e] = run;
   }
   __syncthreads();
+  return run;
+}
+
+__global__ __launch_bounds__(PT) void permute_rank_kernel(const int32_t* __restrict__ ids, int P,
+                                                          int E, int nbits,
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ rank_out) {
+  __shared__ int cnt[4][PMAXE];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int ev[PSEG], rk[PSEG];
+  const int total = chunk_ranks(ids, P, E, nbits, blockIdx.x, cnt, ev, rk);
+  if (tid < E) hist[(int64_t)blockIdx.x * E + tid] = total;
+  const int p0 = blockIdx.x * PCH + wave * PSEG * 64 + (tid & 63);
 #pragma unroll
   for (int s = 0; s < PSEG; ++s) {
     const int p = p0 + s * 64;
@@ -90,26 +106,10 @@ __global__ __launch_bounds__(PT) void permute_rank_kernel(const int32_t* __restr
   }
 }
 
-__global__ __launch_bounds__(PT) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ hist,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv) {
-  __shared__ int s_base[PMAXE];
-  __shared__ int s_wave[4];
+// Exclusive scan over the experts of `total` (thread e holds expert e's
+// total, E <= PT); returns thread e's offset.
+__device__ __forceinline__ int expert_scan(int total, int* s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb = gridDim.x, b = blockIdx.x;
-
-  // one thread per expert (E <= 256 = PT)
-  int total = 0, before = 0;
-  if (tid < E) {
-#pragma unroll 8
-    for (int j = 0; j < nb; ++j) {
-      const int h = hist[(int64_t)j * E + tid];
-      total += h;
-      before += j < b ? h : 0;
-    }
-  }
-  // exclusive scan of total over the experts
   int incl = total;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -122,7 +122,63 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(
 #pragma unroll
   for (int w = 0; w < 4; ++w)
     if (w < wave) wbase += s_wave[w];
-  const int off = wbase + incl - total;
+  return wbase + incl - total;
+}
+
+__global__ __launch_bounds__(PT) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int nbits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv) {
+  __shared__ int cnt[4][PMAXE];
+  __shared__ int s_off[PMAXE];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int ev[PSEG], rk[PSEG];
+  const int total = chunk_ranks(ids, P, E, nbits, 0, cnt, ev, rk);
+  const int off = expert_scan(total, s_wave);
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = off;
+    s_off[tid] = off;
+    if (tid == E - 1) offsets[E] = off + total;
+  }
+  __syncthreads();
+  const int p0 = wave * PSEG * 64 + (tid & 63);
+#pragma unroll
+  for (int s = 0; s < PSEG; ++s) {
+    const int p = p0 + s * 64;
+    if (p < P) {
+      const int e = ev[s];
+      if (e >= 0) {
+        const int pos = s_off[e] + cnt[wave][e] + rk[s];
+        sorted_pairs[pos] = p;
+        inv[p] = pos;
+      } else {
+        inv[p] = 0;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(PT) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv) {
+  __shared__ int s_base[PMAXE];
+  __shared__ int s_wave[4];
+  const int tid = threadIdx.x;
+  const int nb = gridDim.x, b = blockIdx.x;
+
+  // one thread per expert (E <= 256 = PT)
+  int total = 0, before = 0;
+  if (tid < E) {
+#pragma unroll 8
+    for (int j = 0; j < nb; ++j) {
+      const int h = hist[(int64_t)j * E + tid];
+      total += h;
+      before += j < b ? h : 0;
+    }
+  }
+  const int off = expert_scan(total, s_wave);
   if (tid < E) {
     s_base[tid] = off + before;
     if (b == 0) {
@@ -155,10 +211,16 @@ size_t permute_ws_bytes(int P, int E) { return (size_t)permute_chunks(P) * E * s
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* inv, int32_t* hist, hipStream_t s) {
   const int nb = permute_chunks(P);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  if (nb == 1) {
+    LaunchScope ls("permute_rank", s);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PT), 0, s, ids, P, E, nbits, counts,
+                       offsets, sorted_pairs, inv);
+    return hipGetLastError();
+  }
   {
     LaunchScope ls("permute_rank", s);
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
     hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(PT), 0, s, ids, P, E, nbits, hist, inv);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

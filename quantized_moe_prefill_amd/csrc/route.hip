@@ -15,6 +15,12 @@
 //                 workgroups when there are too few token tiles to fill the GPU
 //  router_select: L[t,e] = sum_ks ((P[e] + P[Epad+e]) + P[2Epad+e]) + b[e] in a
 //                 fixed order, then top-k and softmax (16 lanes per token)
+//
+// For a few tokens (at most kRouterGemvT) the product is a plain fp32
+// matrix-vector product instead, router_gemv: one workgroup per router row
+// reads the fp32 row once and takes its dot product with every token (fp32
+// multiply-add, same error class), writing the finished logits as the single
+// plane router_select then reads; the split and the K slices are skipped.
 #include "common.h"
 #include "kernels.h"
 
@@ -200,14 +206,14 @@ __device__ __forceinline__ float sum_step(float x) {
 // retires the winner; lane j keeps round j's winner for the softmax.
 template <int Q>
 __global__ __launch_bounds__(256) void router_select_kernel(
-    const float* __restrict__ P, int ksplit, int T, int E, int Epad, int k,
+    const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
     const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out) {
   const int r = threadIdx.x & 15;
   const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   const bool live = t < T;
   const int tt = live ? t : T - 1;
-  const int N = 3 * Epad;
+  const int N = planes * Epad;
 
   float v[Q];
 #pragma unroll
@@ -215,12 +221,16 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const int e0 = 64 * i + 4 * r;
     f32x4 l = {0.f, 0.f, 0.f, 0.f};
     if (e0 < Epad) {
-      for (int s = 0; s < ksplit; ++s) {
-        const float* p = P + ((int64_t)s * T + tt) * N + e0;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(p + Epad);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(p + 2 * Epad);
-        l += (a + b) + c;
+      if (planes == 1) {
+        l = *reinterpret_cast<const f32x4*>(P + (int64_t)tt * N + e0);
+      } else {
+        for (int s = 0; s < ksplit; ++s) {
+          const float* p = P + ((int64_t)s * T + tt) * N + e0;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(p + Epad);
+          const f32x4 c = *reinterpret_cast<const f32x4*>(p + 2 * Epad);
+          l += (a + b) + c;
+        }
       }
     }
 #pragma unroll
@@ -239,9 +249,13 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   // the shared-gate column past the last lane's range (E a multiple of 64)
   if (has_shared && E >= 16 * Q && r == 0 && live) {
     float x = 0.f;
-    for (int s = 0; s < ksplit; ++s) {
-      const float* p = P + ((int64_t)s * T + tt) * N + E;
-      x += (p[0] + p[Epad]) + p[2 * Epad];
+    if (planes == 1) {
+      x = P[(int64_t)tt * N + E];
+    } else {
+      for (int s = 0; s < ksplit; ++s) {
+        const float* p = P + ((int64_t)s * T + tt) * N + E;
+        x += (p[0] + p[Epad]) + p[2 * Epad];
+      }
     }
     sw_out[t] = 1.f / (1.f + expf(-x));
   }
@@ -281,6 +295,67 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 }
 
+// L[t][n] = sum_h f32(x[t][h]) * w[n][h] for the E router rows and the
+// shared-gate row (n = E), T <= kRouterGemvT tokens. One workgroup per row
+// n; wave w takes the K quarter [w H/4, (w + 1) H/4), lane l the values 8 l
+// .. 8 l + 7 of every 512-wide piece of it, reading the fp32 row and every
+// token's bf16 values straight from memory. The per-lane sums are reduced
+// across the wave, then across the four waves, in a fixed order.
+__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          const float* __restrict__ sg, int T,
+                                                          int H, int E, int Epad,
+                                                          float* __restrict__ out) {
+  __shared__ float part[4][kRouterGemvT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = blockIdx.x;
+  const int rows = E + (sg != nullptr ? 1 : 0);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, 0x00020000);
+  float acc[kRouterGemvT];
+#pragma unroll
+  for (int t = 0; t < kRouterGemvT; ++t) acc[t] = 0.f;
+  if (n < rows) {
+    const float* wrow = n < E ? wr + (int64_t)n * H : sg;  // n == E: the shared gate
+    const int kq = H / 4;
+    for (int c = 0; c < kq; c += 512) {
+      const int k = wave * kq + c + 8 * lane;
+      if (c + 8 * lane < kq) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + k);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + k + 4);
+        u32x4 xv[kRouterGemvT];
+#pragma unroll
+        for (int t = 0; t < kRouterGemvT; ++t) {
+          // past the last token: past the end of x, which reads zero
+          const uint32_t off = t < T ? (uint32_t)(t * H + k) * 2u : 0x7ffffff0u;
+          xv[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        }
+#pragma unroll
+        for (int t = 0; t < kRouterGemvT; ++t) {
+          float a = acc[t];
+          a = fmaf(bf16lo(xv[t][0]), w0[0], a);
+          a = fmaf(bf16hi(xv[t][0]), w0[1], a);
+          a = fmaf(bf16lo(xv[t][1]), w0[2], a);
+          a = fmaf(bf16hi(xv[t][1]), w0[3], a);
+          a = fmaf(bf16lo(xv[t][2]), w1[0], a);
+          a = fmaf(bf16hi(xv[t][2]), w1[1], a);
+          a = fmaf(bf16lo(xv[t][3]), w1[2], a);
+          a = fmaf(bf16hi(xv[t][3]), w1[3], a);
+          acc[t] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouterGemvT; ++t) acc[t] = wave_sum(acc[t]);
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < kRouterGemvT; ++t) part[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (tid < T) out[(int64_t)tid * Epad + n] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
 int router_ksplit(int T, int E, bool has_shared, int H) {
   const int N = 3 * router_padded_rows(E, has_shared);
   const int tiles = cdiv(T, RBM) * cdiv(N, RBN);
@@ -290,6 +365,8 @@ int router_ksplit(int T, int E, bool has_shared, int H) {
 }
 
 }  // namespace
+
+bool router_uses_gemv(int T) { return T <= kRouterGemvT; }
 
 int router_padded_rows(int E, bool has_shared) { return cdiv(E + (has_shared ? 1 : 0), 16) * 16; }
 
@@ -314,15 +391,25 @@ hipError_t launch_router_split(const float* w_router, const float* shared_gate, 
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, float* partial,
-                              const float* bias, int T, int H, int E, int k, bool has_shared,
-                              float* logits, int32_t* ids, float* topk_w, float* shared_w,
-                              hipStream_t s) {
+hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const float* shared_gate,
+                              const uint16_t* split, float* partial, const float* bias, int T,
+                              int H, int E, int k, float* logits, int32_t* ids, float* topk_w,
+                              float* shared_w, hipStream_t s) {
+  const bool has_shared = shared_gate != nullptr;
   const int Epad = router_padded_rows(E, has_shared);
-  const int N = 3 * Epad;
-  const int n_mt = cdiv(T, RBM), n_nt = cdiv(N, RBN);
-  const int ks = router_ksplit(T, E, has_shared, H);
-  {
+  int ks = 1, planes = 1;
+  if (router_uses_gemv(T)) {
+    // the finished fp32 logits, one plane [T][Epad]
+    LaunchScope ls("router_gemm", s);
+    hipLaunchKernelGGL(router_gemv_kernel, dim3(Epad), dim3(256), 0, s, x, w_router, shared_gate,
+                       T, H, E, Epad, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const int N = 3 * Epad;
+    const int n_mt = cdiv(T, RBM), n_nt = cdiv(N, RBN);
+    ks = router_ksplit(T, E, has_shared, H);
+    planes = 3;
     LaunchScope ls("router_gemm", s);
     hipLaunchKernelGGL(router_gemm_kernel, dim3(n_mt * n_nt * ks), dim3(RTHREADS), 0, s, x,
                        split, partial, T, H, N, n_mt, n_nt, ks);
@@ -333,14 +420,14 @@ hipError_t launch_router_topk(const uint16_t* x, const uint16_t* split, float* p
   const dim3 grid(cdiv(T, 16)), block(256);
   const int hs = has_shared ? 1 : 0;
   if (E <= 64)
-    hipLaunchKernelGGL(router_select_kernel<4>, grid, block, 0, s, partial, ks, T, E, Epad, k,
-                       bias, hs, logits, ids, topk_w, shared_w);
+    hipLaunchKernelGGL(router_select_kernel<4>, grid, block, 0, s, partial, ks, planes, T, E, Epad,
+                       k, bias, hs, logits, ids, topk_w, shared_w);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_select_kernel<8>, grid, block, 0, s, partial, ks, T, E, Epad, k,
-                       bias, hs, logits, ids, topk_w, shared_w);
+    hipLaunchKernelGGL(router_select_kernel<8>, grid, block, 0, s, partial, ks, planes, T, E, Epad,
+                       k, bias, hs, logits, ids, topk_w, shared_w);
   else
-    hipLaunchKernelGGL(router_select_kernel<16>, grid, block, 0, s, partial, ks, T, E, Epad, k,
-                       bias, hs, logits, ids, topk_w, shared_w);
+    hipLaunchKernelGGL(router_select_kernel<16>, grid, block, 0, s, partial, ks, planes, T, E,
+                       Epad, k, bias, hs, logits, ids, topk_w, shared_w);
   return hipGetLastError();
 }
 

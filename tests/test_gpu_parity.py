@@ -123,6 +123,49 @@ def test_weight_streaming_sweep(T):
     full_check(replace(cfg, T=T), li, cpu, x)
 
 
+@pytest.mark.parametrize("name,T,over", [
+    ("skew_shared", 1, {}),
+    ("skew_shared", 5, {}),
+    ("skew_shared", 16, {}),
+    ("tiny", 1, {}),
+    ("tiny", 3, {}),
+    # gate/up K = 768: six 128-wide stages over four waves (two waves repeat
+    # a stage whose products are skipped); down K = 384: three stages, one
+    # wave without work
+    ("a3b_pp512", 7, dict(H=768, I=384, E=16, G=64)),
+    # every expert takes every token: exactly one full 16-row block each
+    ("a3b_pp512", 16, dict(H=1024, I=256, E=8, G=32, quant="asym")),
+])
+def test_small_T_weight_streaming(name, T, over):
+    """At most 16 tokens: the expert GEMMs run as the weight-streaming
+    kernel (asymmetric and symmetric, shared expert, 1/2/4 stages per wave)."""
+    cfg = replace(CONFIGS[name], T=T, **over)
+    li, cpu, x = setup(cfg)
+    full_check(cfg, li, cpu, x)
+
+
+def test_streaming_more_rows_than_a_block():
+    """Few tokens, but each sends three of its four rows to expert 0 (the
+    entry points accept repeated ids): 36 rows of one expert, walked by the
+    weight-streaming kernel in 16-row blocks with its weights held."""
+    cfg = replace(CONFIGS["skew_shared"], T=12, E=16, k=4, I=256, shared_I=128, G=32)
+    li, cpu, x = setup(cfg)
+    rng = np.random.default_rng(5)
+    ids = np.array([[0, 0, 0, rng.integers(1, 16)] for _ in range(cfg.T)], np.int32)
+    shape = qm.shape_of(cfg)
+    counts, offsets, sp, inv = qm.moe_permute(shape, torch.from_numpy(ids).to(DEV))
+    y_perm, y_sh = qm.moe_expert_ffn(shape, x, qm.Experts(li), counts, offsets, sp)
+    torch.cuda.synchronize()
+    c, o, s, _ = oracle.permute(ids, cfg.E)
+    assert c[0] == 36
+    w = oracle.moe_oracle._weights_dict(cpu)
+    xf = f64_of_bf16(x)
+    _, y_ref = oracle.expert_ffn(xf, s, o, cfg.k, w, cfg.G, cfg.quant)
+    gate(f64_of_f16(y_perm), y_ref, "y_perm", fmt="fp16")
+    _, ys_ref = oracle.moe_oracle.shared_expert(xf, w, cfg.G, cfg.quant)
+    gate(f64_of_f16(y_sh), ys_ref, "y_shared", fmt="fp16")
+
+
 def test_ragged_and_k1():
     # T not a multiple of any tile, k = 1, odd expert count
     cfg = replace(CONFIGS["tiny"], T=37, E=5, k=1)
