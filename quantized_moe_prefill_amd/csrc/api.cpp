@@ -493,11 +493,19 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
   auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
   auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
 
-  st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
-                  partial, stream);
-  if (st != MOE_OK) return st;
-  QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
-           "permute launch");
+  if (router_uses_gemv((int)T)) {
+    // a few tokens: the router product, then top-k and grouping in one workgroup
+    QMOE_HIP(launch_route_permute_small(x, w_router, shared_gate, partial, router_bias, (int)T,
+                                        s.H, s.E, s.k, ids, tw, sw, counts, offsets, sorted, inv,
+                                        stream),
+             "router launch");
+  } else {
+    st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
+                    partial, stream);
+    if (st != MOE_OK) return st;
+    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
+             "permute launch");
+  }
   st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs, stream);
   if (st != MOE_OK) return st;
   QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),

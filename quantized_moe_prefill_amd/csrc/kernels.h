@@ -37,6 +37,14 @@ hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const fl
                               int H, int E, int k, float* logits, int32_t* ids, float* topk_w,
                               float* shared_w, hipStream_t s);
 
+// At most kRouterGemvT tokens: router logits, top-k and softmax, and the
+// grouping by expert (as launch_permute), in two launches.
+hipError_t launch_route_permute_small(const uint16_t* x, const float* w_router,
+                                      const float* shared_gate, float* partial, const float* bias,
+                                      int T, int H, int E, int k, int32_t* ids, float* topk_w,
+                                      float* shared_w, int32_t* counts, int32_t* offsets,
+                                      int32_t* sorted_pairs, int32_t* inv, hipStream_t s);
+
 // ---- permutation ------------------------------------------------------
 // scratch: per-chunk expert histograms, permute_ws_bytes(P, E) bytes
 size_t permute_ws_bytes(int P, int E);

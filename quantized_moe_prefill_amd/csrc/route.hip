@@ -23,6 +23,7 @@
 // plane router_select then reads; the split and the K slices are skipped.
 #include "common.h"
 #include "kernels.h"
+#include "permute_impl.h"
 
 namespace qmoe {
 
@@ -204,13 +205,15 @@ __device__ __forceinline__ float sum_step(float x) {
 // logits of experts 64*i + 4*r + c (i < Q/4, c < 4). Each of the k rounds
 // takes the lane-local best, reduces it over the row with DPP exchanges and
 // retires the winner; lane j keeps round j's winner for the softmax.
+// Logits, top-k and softmax of token t (16 lanes per token: lane r of the
+// group); the selected ids also go to lds_ids[t * k + j] if it is given.
 template <int Q>
-__global__ __launch_bounds__(256) void router_select_kernel(
+__device__ __forceinline__ void select_token(
     const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
     const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out, int t,
+    int32_t* lds_ids) {
   const int r = threadIdx.x & 15;
-  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   const bool live = t < T;
   const int tt = live ? t : T - 1;
   const int N = planes * Epad;
@@ -292,6 +295,63 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   if (live && r < k) {
     ids_out[(int64_t)t * k + r] = seli;
     w_out[(int64_t)t * k + r] = ex * (1.f / sum);
+    if (lds_ids != nullptr) lds_ids[t * k + r] = seli;
+  }
+}
+
+template <int Q>
+__global__ __launch_bounds__(256) void router_select_kernel(
+    const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
+    const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out) {
+  select_token<Q>(P, ksplit, planes, T, E, Epad, k, bias, has_shared, logits_out, ids_out, w_out,
+                  sw_out, blockIdx.x * 16 + (threadIdx.x >> 4), nullptr);
+}
+
+// At most 16 tokens: top-k and softmax of every token (one workgroup, 16
+// lanes per token) and then, in the same workgroup, the grouping of the
+// (token, slot) pairs by expert (counts, offsets, sorted_pairs, inv, as
+// permute computes them), the ids handed over in LDS.
+template <int Q>
+__global__ __launch_bounds__(PT) void router_select_permute_kernel(
+    const float* __restrict__ P, int T, int E, int Epad, int k, int nbits,
+    const float* __restrict__ bias, int has_shared, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, float* __restrict__ sw_out, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ inv) {
+  __shared__ int32_t s_ids[16 * 8];
+  __shared__ int cnt[4][PMAXE];
+  __shared__ int s_off[PMAXE];
+  __shared__ int s_wave[4];
+  select_token<Q>(P, 1, 1, T, E, Epad, k, bias, has_shared, nullptr, ids_out, w_out, sw_out,
+                  threadIdx.x >> 4, s_ids);
+  __syncthreads();
+  const int Pn = T * k;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int ev[PSEG], rk[PSEG];
+  const int total = chunk_ranks(s_ids, Pn, E, nbits, 0, cnt, ev, rk);
+  const int off = expert_scan(total, s_wave);
+  if (tid < E) {
+    counts[tid] = total;
+    offsets[tid] = off;
+    s_off[tid] = off;
+    if (tid == E - 1) offsets[E] = off + total;
+  }
+  __syncthreads();
+  const int p0 = wave * PSEG * 64 + (tid & 63);
+#pragma unroll
+  for (int s = 0; s < PSEG; ++s) {
+    const int p = p0 + s * 64;
+    if (p < Pn) {
+      const int e = ev[s];
+      if (e >= 0) {
+        const int pos = s_off[e] + cnt[wave][e] + rk[s];
+        sorted_pairs[pos] = p;
+        inv[p] = pos;
+      } else {
+        inv[p] = 0;
+      }
+    }
   }
 }
 
@@ -367,6 +427,37 @@ int router_ksplit(int T, int E, bool has_shared, int H) {
 }  // namespace
 
 bool router_uses_gemv(int T) { return T <= kRouterGemvT; }
+
+hipError_t launch_route_permute_small(const uint16_t* x, const float* w_router,
+                                      const float* shared_gate, float* partial, const float* bias,
+                                      int T, int H, int E, int k, int32_t* ids, float* topk_w,
+                                      float* shared_w, int32_t* counts, int32_t* offsets,
+                                      int32_t* sorted_pairs, int32_t* inv, hipStream_t s) {
+  const bool has_shared = shared_gate != nullptr;
+  const int Epad = router_padded_rows(E, has_shared);
+  {
+    LaunchScope ls("router_gemm", s);
+    hipLaunchKernelGGL(router_gemv_kernel, dim3(Epad), dim3(256), 0, s, x, w_router, shared_gate,
+                       T, H, E, Epad, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int hs = has_shared ? 1 : 0;
+  LaunchScope ls("router_select", s);
+  if (E <= 64)
+    hipLaunchKernelGGL(router_select_permute_kernel<4>, dim3(1), dim3(PT), 0, s, partial, T, E, Epad,
+                       k, nbits, bias, hs, ids, topk_w, shared_w, counts, offsets, sorted_pairs, inv);
+  else if (E <= 128)
+    hipLaunchKernelGGL(router_select_permute_kernel<8>, dim3(1), dim3(PT), 0, s, partial, T, E, Epad,
+                       k, nbits, bias, hs, ids, topk_w, shared_w, counts, offsets, sorted_pairs, inv);
+  else
+    hipLaunchKernelGGL(router_select_permute_kernel<16>, dim3(1), dim3(PT), 0, s, partial, T, E,
+                       Epad, k, nbits, bias, hs, ids, topk_w, shared_w, counts, offsets,
+                       sorted_pairs, inv);
+  return hipGetLastError();
+}
 
 int router_padded_rows(int E, bool has_shared) { return cdiv(E + (has_shared ? 1 : 0), 16) * 16; }
 
