@@ -42,7 +42,7 @@ KERNELS = ("router_split", "router_gemm", "router_select", "permute_rank", "perm
 # FETCH_SIZE + WRITE_SIZE (each scaled by the copy-kernel calibration factor),
 # keyed by the hash of the expert-GEMM sources they were measured on: a
 # changed kernel reports null until it is measured again.
-GATEUP_TRAFFIC = {"8192fae07451da4b": 661247413}   # {source sha256[:16]: bytes per launch}
+GATEUP_TRAFFIC = {"bcad9b561b323f77": 662103896}   # {source sha256[:16]: bytes per launch}
 GEMM_SOURCES = ("quantized_moe_prefill_amd/csrc/ffn.hip", "quantized_moe_prefill_amd/csrc/common.h",
                 "quantized_moe_prefill_amd/csrc/dequant.h")
 CALIB_BYTES = 1 << 30

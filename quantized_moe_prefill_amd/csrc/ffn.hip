@@ -126,9 +126,19 @@ struct GemmTile {
   bool cvalid;
   uint32_t a_off[ALD];  // byte offsets of this lane's activation loads
   uint32_t b_lane, s_lane;
+  uint32_t sc_src[2];  // scale tiles in LDS: byte offsets of the two 1 KB sources
 };
 
-template <bool GATEUP, bool ASYM>
+// Scales (and mins) of a tile in LDS: each wave's rows take two 1 KB slots,
+// filled by two direct loads per tile instead of one 2-byte load per
+// fragment and K stage. Gate/up: slot 0 = the 32 gate rows' scales, slot 1 =
+// the 32 up rows' (symmetric only, at most 16 groups per row); down: the 64
+// rows' scales over both slots (at most 16 groups per row), or, asymmetric,
+// scales in slot 0 and mins in slot 1 (at most 8 groups per row).
+constexpr int SC_SLOT = 1024;
+constexpr int SC_WAVE = 2 * SC_SLOT;
+
+template <bool GATEUP, bool ASYM, bool SCL>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
@@ -145,6 +155,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Sc[SCL ? NWAVES * SC_WAVE : 16];
   __shared__ int s_scan[257];
   __shared__ int s_wave[NWAVES];
 
@@ -248,6 +259,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
     ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
     ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
+    if (SCL) {
+      const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));
+      const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
+      ts.sc_src[0] = s0;
+      ts.sc_src[1] = GATEUP ? __builtin_amdgcn_readfirstlane((r0 + N / 2) * KG * 2)
+                            : (ASYM ? s0 : s0 + SC_SLOT);
+    }
   };
   auto load_a = [&](const GemmTile& ts, int kt, uint8_t* dst) {
 #pragma unroll
@@ -261,11 +279,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     for (int f = 0; f < NFRAG; ++f)
       cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+    if (!SCL) {
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f) {
+        const int so = frow(f) * KG * 2 + kt * s_step;
+        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, so, 0);
+        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, ts.s_lane, so, 0) : 0u;
+      }
+    }
+  };
+  // this wave's scale tile: two direct 1 KB loads (past a block's end they
+  // read other rows' scales or zeros, never used)
+  uint8_t* const sc_wave = Sc + wave * SC_WAVE;
+  auto load_sc = [&](const GemmTile& ts) {
+    if (SCL) {
+      const uint32_t lo = (uint32_t)lane_o * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void_t*)sc_wave, 16, lo, ts.sc_src[0], 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ASYM && !GATEUP ? rM : rS,
+                                               (lds_void_t*)(sc_wave + SC_SLOT), 16, lo,
+                                               ts.sc_src[1], 0, 0);
+    }
+  };
+  // the scales (and mins) of stage kt from the wave's scale tile
+  auto read_sc = [&](int kt, uint32_t* rs, uint32_t* rm) {
+    const int grp = (lg * 32 + kt * BK) / g.G;
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-      const int so = frow(f) * KG * 2 + kt * s_step;
-      rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, so, 0);
-      rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, ts.s_lane, so, 0) : 0u;
+      const int row = GATEUP ? 16 * (f & 1) + r16 : 16 * f + r16;
+      const int off = (GATEUP && f >= 2 ? SC_SLOT : 0) + (row * KG + grp) * 2;
+      rs[f] = *reinterpret_cast<const uint16_t*>(sc_wave + off);
+      rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(sc_wave + SC_SLOT + off) : 0u;
     }
   };
 
@@ -406,6 +449,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   setup(tile, cur);
   u32x4 cb[NFRAG];
   uint32_t rs[NFRAG], rm[NFRAG];
+  load_sc(cur);
   load_b(cur, 0, cb, rs, rm);
   load_a(cur, 0, As0);
   load_a(cur, min(1, klast), As1);
@@ -413,6 +457,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     refresh_lane();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
     lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
+    if (SCL) read_sc(0, rs, rm);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
@@ -428,6 +473,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       // register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
       compute_stage(curs, cb, rs, rm);
+      if (SCL) read_sc(min(kt + 1, klast), rsn, rmn);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       lds_barrier();
       // the hand-over of the next stage's registers stays here: moved up into
@@ -454,6 +500,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     refresh_lane();
     if (has_next) {
       setup(next, nts);
+      load_sc(nts);
       load_b(nts, 0, cb, rs, rm);
       load_a(nts, 0, As0);
     }
@@ -488,14 +535,21 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   wgs = cdiv(wgs, NXCD) * NXCD;
   const dim3 grid(wgs), block(NTHREADS);
   LaunchScope ls(name, s);
-  auto go = [&](auto asym) {
-    constexpr bool A = decltype(asym)::value;
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A>), grid, block, 0, s, g, n_ntiles);
+  // scales through LDS when a wave's rows fit its two 1 KB slots
+  const int KG = g.K / g.G;
+  const bool asym = g.Wmin != nullptr;
+  const bool scl = GATEUP ? (!asym && KG <= 16) : (asym ? KG <= 8 : KG <= 16);
+  auto go = [&](auto a, auto l) {
+    constexpr bool A = decltype(a)::value, L = decltype(l)::value;
+    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, L>), grid, block, 0, s, g, n_ntiles);
   };
-  if (g.Wmin != nullptr)
-    go(std::true_type{});
-  else
-    go(std::false_type{});
+  if (asym) {
+    if (scl) go(std::true_type{}, std::true_type{});
+    else go(std::true_type{}, std::false_type{});
+  } else {
+    if (scl) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 
