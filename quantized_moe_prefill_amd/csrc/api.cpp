@@ -248,12 +248,25 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   g.expect_rows = (int)T;
   // the weight-streaming gate/up reads the bf16 activations itself; the tiled
   // one wants them as fp16 in kperm order
-  const bool x_direct = gateup_streams(g);
+  const bool x_direct = gemm_streams(g, true);
   if (x_direct) {
     g.A = x;
     g.a_bf16 = true;
   } else {
     QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+  }
+  // A shared expert of the routed experts' shape runs as one more group of
+  // the tiled launches (its T rows join the routed tiles instead of two
+  // launches of their own that fill a fraction of the GPU).
+  const bool fold_gu = s.Is > 0 && s.Is == s.I && !x_direct;
+  if (fold_gu) {
+    g.rows2 = (int)T;
+    g.A2 = x16;
+    g.W2 = w->s13;
+    g.Wscale2 = w->s13_scale;
+    g.Wmin2 = s.asym ? w->s13_min : nullptr;
+    g.C2 = hs;
+    g.ldc2 = s.Is;
   }
   QMOE_HIP(launch_gateup(g, st), "gateup launch");
 
@@ -269,9 +282,20 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   d.K = s.I;
   d.C = yperm;
   d.ldc = s.H;
+  d.rows2 = 0;
+  const bool fold_dn = fold_gu && !gemm_streams(d, false);
+  if (fold_dn) {
+    d.rows2 = (int)T;
+    d.A2 = hs;
+    d.W2 = w->s2;
+    d.Wscale2 = w->s2_scale;
+    d.Wmin2 = s.asym ? w->s2_min : nullptr;
+    d.C2 = ysh;
+    d.ldc2 = s.H;
+  }
   QMOE_HIP(launch_down(d, st), "down launch");
 
-  if (s.Is > 0) {
+  if (s.Is > 0 && !(fold_gu && fold_dn)) {
     GroupedGemm gs{};
     gs.A = x_direct ? x : x16;
     gs.a_bf16 = x_direct;
@@ -292,12 +316,14 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
     gs.C = hs;
     gs.ldc = s.Is;
     gs.expect_rows = (int)T;
-    if (gs.a_bf16 && !gateup_streams(gs)) {
-      QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
-      gs.A = x16;
-      gs.a_bf16 = false;
+    if (!fold_gu) {
+      if (gs.a_bf16 && !gemm_streams(gs, true)) {
+        QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+        gs.A = x16;
+        gs.a_bf16 = false;
+      }
+      QMOE_HIP(launch_gateup(gs, st, "shared_gateup_gemm"), "shared gateup launch");
     }
-    QMOE_HIP(launch_gateup(gs, st, "shared_gateup_gemm"), "shared gateup launch");
     GroupedGemm ds = gs;
     ds.A = hs;
     ds.a_bf16 = false;

@@ -99,13 +99,13 @@ __device__ __forceinline__ int rowswz(int r) { return ((r & 3) << 2) | ((r >> 2)
 // before any is used, so their latencies overlap.
 template <int NL>
 __device__ __forceinline__ void gather_rows(const GroupedGemm& g, int row0, int rows, int r_first,
-                                            int r_step, int* src) {
+                                            int r_step, int* src, bool direct = false) {
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int r = r_first + i * r_step;
     src[i] = row0 + (r < rows ? r : 0);
   }
-  if (g.gather != nullptr) {
+  if (g.gather != nullptr && !direct) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) src[i] = g.gather[src[i]];
     const int div = g.gather_div;
@@ -124,6 +124,7 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 struct GemmTile {
   int row0, rows, c0;
   bool cvalid;
+  int shared;  // the tile belongs to the extra group (uniform)
   uint32_t a_off[ALD];  // byte offsets of this lane's activation loads
   uint32_t b_lane, s_lane;
   uint32_t sc_src[2];  // scale tiles in LDS: byte offsets of the two 1 KB sources
@@ -138,7 +139,7 @@ struct GemmTile {
 constexpr int SC_SLOT = 1024;
 constexpr int SC_WAVE = 2 * SC_SLOT;
 
-template <bool GATEUP, bool ASYM, bool SCL>
+template <bool GATEUP, bool ASYM, bool SCL, bool FOLD>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Sc[SCL ? NWAVES * SC_WAVE : 16];
-  __shared__ int s_scan[257];
+  __shared__ int s_scan[258];
   __shared__ int s_wave[NWAVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,8 +167,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 
   // ---- tile list: per-expert tile prefix (tiles of BM rows) ----
   int n_mtiles;
+  const bool has2 = FOLD && g.counts != nullptr && g.rows2 > 0;
+  const int ngrp = g.E + (has2 ? 1 : 0);
   if (g.counts != nullptr) {
-    const int c = tid < g.E ? g.counts[tid] : 0;
+    const int c = tid < g.E ? g.counts[tid] : (has2 && tid == g.E ? g.rows2 : 0);
     int incl = (c + BM - 1) / BM;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -177,10 +180,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
     for (int w = 0; w < wave; ++w) incl += s_wave[w];
-    if (tid < 256) s_scan[tid + 1] = incl;
+    if (tid < 257) s_scan[tid + 1] = incl;
     if (tid == 0) s_scan[0] = 0;
     __syncthreads();
-    n_mtiles = s_scan[g.E];
+    n_mtiles = s_scan[ngrp];
   } else {
     n_mtiles = cdiv(g.rows_single, BM);
   }
@@ -205,6 +208,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3);
   const int s_step = (BK / g.G) * 2;  // scale bytes per stage along a row
+  // the extra group's operands (one expert)
+  const __amdgpu_buffer_rsrc_t rA2 =
+      has2 ? __builtin_amdgcn_make_buffer_rsrc((void*)g.A2, 0, g.rows2 * K * 2, kRsrcWord3) : rA;
+  const __amdgpu_buffer_rsrc_t rW2 =
+      has2 ? __builtin_amdgcn_make_buffer_rsrc((void*)g.W2, 0, N * (K / 2), kRsrcWord3) : rW;
+  const __amdgpu_buffer_rsrc_t rS2 =
+      has2 ? __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale2, 0, N * KG * 2, kRsrcWord3) : rS;
+  const __amdgpu_buffer_rsrc_t rM2 =
+      has2 ? __builtin_amdgcn_make_buffer_rsrc((void*)(ASYM ? g.Wmin2 : g.Wscale2), 0, N * KG * 2,
+                                               kRsrcWord3)
+           : rM;
 
   // Per-lane constants are derived from an opaque copy of the lane index, so
   // the compiler cannot compute them once up front and hold them in
@@ -230,25 +244,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     const int ntile = tile - mtile * n_ntiles;
     int e;
     if (g.counts != nullptr) {
-      // largest e with s_scan[e] <= mtile (binary search over the E+1 prefixes)
-      int lo = 0, hi = g.E;  // s_scan[lo] <= mtile < s_scan[hi]
+      // largest e with s_scan[e] <= mtile (binary search over the prefixes)
+      int lo = 0, hi = ngrp;  // s_scan[lo] <= mtile < s_scan[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (s_scan[mid] <= mtile) lo = mid; else hi = mid;
       }
       e = lo;
       const int local = mtile - s_scan[e];
-      ts.row0 = g.offsets[e] + local * BM;
-      ts.rows = min(BM, g.counts[e] - local * BM);
+      ts.shared = FOLD ? __builtin_amdgcn_readfirstlane(e == g.E ? 1 : 0) : 0;
+      if (ts.shared) {
+        e = 0;
+        ts.row0 = local * BM;
+        ts.rows = min(BM, g.rows2 - ts.row0);
+      } else {
+        ts.row0 = g.offsets[e] + local * BM;
+        ts.rows = min(BM, g.counts[e] - local * BM);
+      }
     } else {
       e = 0;
+      ts.shared = 0;
       ts.row0 = mtile * BM;
       ts.rows = min(BM, g.rows_single - ts.row0);
     }
     // load i of wave w fills rows 4 (ALD w + i) .. +3; lane l covers row
     // 4 (ALD w + i) + l/16, LDS slot l%16, i.e. source chunk (l%16) ^ rowswz(row)
     int src[ALD];
-    gather_rows<ALD>(g, ts.row0, ts.rows, 4 * ALD * wave + lg, 4, src);
+    gather_rows<ALD>(g, ts.row0, ts.rows, 4 * ALD * wave + lg, 4, src, ts.shared != 0);
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
       const int r = 4 * (ALD * wave + i) + lg;
@@ -260,7 +282,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
     ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
     if (SCL) {
-      const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));
+      const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));  // e = 0 for the extra group
       const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
       ts.sc_src[0] = s0;
       ts.sc_src[1] = GATEUP ? __builtin_amdgcn_readfirstlane((r0 + N / 2) * KG * 2)
@@ -271,20 +293,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 #pragma unroll
     for (int i = 0; i < ALD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, ts.a_off[i], kt * BK * 2, 0, 0);
+          ts.shared ? rA2 : rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, ts.a_off[i],
+          kt * BK * 2, 0, 0);
   };
   // weights and the group's scale (and min) of stage kt into registers
   auto load_b = [&](const GemmTile& ts, int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f)
       cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+                                            ts.shared ? rW2 : rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
     if (!SCL) {
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
         const int so = frow(f) * KG * 2 + kt * s_step;
-        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, so, 0);
-        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rM, ts.s_lane, so, 0) : 0u;
+        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(ts.shared ? rS2 : rS, ts.s_lane, so, 0);
+        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ts.shared ? rM2 : rM,
+                                                                     ts.s_lane, so, 0)
+                     : 0u;
       }
     }
   };
@@ -294,8 +319,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   auto load_sc = [&](const GemmTile& ts) {
     if (SCL) {
       const uint32_t lo = (uint32_t)lane_o * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void_t*)sc_wave, 16, lo, ts.sc_src[0], 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ASYM && !GATEUP ? rM : rS,
+      const __amdgpu_buffer_rsrc_t s_r = ts.shared ? rS2 : rS;
+      const __amdgpu_buffer_rsrc_t m_r = ts.shared ? rM2 : rM;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, (lds_void_t*)sc_wave, 16, lo, ts.sc_src[0], 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ASYM && !GATEUP ? m_r : s_r,
                                                (lds_void_t*)(sc_wave + SC_SLOT), 16, lo,
                                                ts.sc_src[1], 0, 0);
     }
@@ -368,6 +395,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // 16-byte row pieces. Down: the same, in two halves of 64 rows.
   auto epilogue = [&](const GemmTile& ts) {
     int rq = 4 * lg, rr = r16, row0 = ts.row0, rows = ts.rows;
+    uint16_t* const C = ts.shared ? g.C2 : g.C;
+    const int ldc = ts.shared ? g.ldc2 : g.ldc;
     asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
     if (GATEUP) {
       uint8_t* sub = (wave < 4 ? As2 : Ex) + (wave & 3) * (BM * 64);
@@ -394,7 +423,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         const int rl = q * 16 + (lane_o >> 2);
         const int p = lane_o & 3;
         const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
-        if (ts.cvalid && rl < rows) st16(g.C + (int64_t)(row0 + rl) * g.ldc + ts.c0 + p * 8, d);
+        if (ts.cvalid && rl < rows) st16(C + (int64_t)(row0 + rl) * ldc + ts.c0 + p * 8, d);
       }
     } else {
       // y in two halves of 64 rows: this wave's half sub-tile is 64 rows x
@@ -425,7 +454,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           const int p = lane_o & 7;
           const u32x4 d = ld16(sub + rl * 128 + (p ^ (rl & 7)) * 16);
           const int row = half * 64 + rl;
-          if (ts.cvalid && row < rows) st16(g.C + (int64_t)(row0 + row) * g.ldc + ts.c0 + p * 8, d);
+          if (ts.cvalid && row < rows) st16(C + (int64_t)(row0 + row) * ldc + ts.c0 + p * 8, d);
         }
       }
     }
@@ -518,7 +547,9 @@ template <bool GATEUP>
 hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name) {
   const int n_ntiles = GATEUP ? cdiv(g.N / 2, BN / 2) : cdiv(g.N, BN);
   const int m_bound =
-      g.counts != nullptr ? cdiv(g.max_rows, BM) + g.E : cdiv(g.rows_single, BM);
+      g.counts != nullptr
+          ? cdiv(g.max_rows, BM) + g.E + (g.rows2 > 0 ? cdiv(g.rows2, BM) + 1 : 0)
+          : cdiv(g.rows_single, BM);
   if (m_bound <= 0) return hipSuccess;
   if (g_num_cus == 0) {
     int dev = 0;
@@ -535,20 +566,27 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   wgs = cdiv(wgs, NXCD) * NXCD;
   const dim3 grid(wgs), block(NTHREADS);
   LaunchScope ls(name, s);
-  // scales through LDS when a wave's rows fit its two 1 KB slots
+  // scales through LDS when a wave's rows fit its two 1 KB slots; an extra
+  // (shared-expert) group is a variant of its own, without the LDS scales,
+  // so that the common kernels keep their registers
   const int KG = g.K / g.G;
   const bool asym = g.Wmin != nullptr;
-  const bool scl = GATEUP ? (!asym && KG <= 16) : (asym ? KG <= 8 : KG <= 16);
-  auto go = [&](auto a, auto l) {
-    constexpr bool A = decltype(a)::value, L = decltype(l)::value;
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, L>), grid, block, 0, s, g, n_ntiles);
+  const bool fold = g.counts != nullptr && g.rows2 > 0;
+  const bool scl = !fold && (GATEUP ? (!asym && KG <= 16) : (asym ? KG <= 8 : KG <= 16));
+  auto go = [&](auto a, auto l, auto f) {
+    constexpr bool A = decltype(a)::value, L = decltype(l)::value, F = decltype(f)::value;
+    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, L, F>), grid, block, 0, s, g, n_ntiles);
   };
+  const std::true_type yes{};
+  const std::false_type no{};
   if (asym) {
-    if (scl) go(std::true_type{}, std::true_type{});
-    else go(std::true_type{}, std::false_type{});
+    if (fold) go(yes, no, yes);
+    else if (scl) go(yes, yes, no);
+    else go(yes, no, no);
   } else {
-    if (scl) go(std::false_type{}, std::true_type{});
-    else go(std::false_type{}, std::false_type{});
+    if (fold) go(no, no, yes);
+    else if (scl) go(no, yes, no);
+    else go(no, no, no);
   }
   return hipGetLastError();
 }
@@ -571,7 +609,7 @@ static bool use_stream(const GroupedGemm& g, bool gateup) {
   return g.expect_rows > 0 && g.expect_rows <= kStreamMaxRows && stream_supported(g, gateup);
 }
 
-bool gateup_streams(const GroupedGemm& g) { return use_stream(g, true); }
+bool gemm_streams(const GroupedGemm& g, bool gateup) { return use_stream(g, gateup); }
 
 hipError_t launch_gateup(const GroupedGemm& g, hipStream_t s, const char* name) {
   if (use_stream(g, true)) return launch_stream(g, true, s, name);

@@ -78,6 +78,17 @@ struct GroupedGemm {
   // A holds bf16 rows in natural order (the weight-streaming gate/up kernel
   // converts them itself); otherwise fp16 in kperm chunk order
   bool a_bf16;
+  // Tiled kernel only: one more group after the E routed ones (a shared
+  // expert with the same N and K), rows2 rows of A2 in order (no gather),
+  // one expert's weights W2 / Wscale2 / Wmin2, output C2 with leading
+  // dimension ldc2. rows2 == 0: none.
+  int rows2;
+  const uint16_t* A2;
+  const uint8_t* W2;
+  const uint16_t* Wscale2;
+  const uint16_t* Wmin2;
+  uint16_t* C2;
+  int ldc2;
 };
 constexpr int kStreamMaxRows = 16;
 // gate/up with fused SwiGLU: N = 2I weight rows, writes h = silu(g)*u
@@ -87,9 +98,9 @@ hipError_t launch_gateup(const GroupedGemm& g, hipStream_t s, const char* name =
 hipError_t launch_down(const GroupedGemm& g, hipStream_t s, const char* name = "down_gemm");
 // Weight-streaming form of the two GEMMs above for a few rows per group.
 bool stream_supported(const GroupedGemm& g, bool gateup);
-// launch_gateup(g) would run the weight-streaming kernel (which can read bf16
-// activations directly: a_bf16)
-bool gateup_streams(const GroupedGemm& g);
+// launch_gateup(g) / launch_down(g) would run the weight-streaming kernel
+// (which reads bf16 activations directly, a_bf16, and ignores rows2)
+bool gemm_streams(const GroupedGemm& g, bool gateup);
 hipError_t launch_stream(const GroupedGemm& g, bool gateup, hipStream_t s, const char* name);
 
 // ---- combine / norm ---------------------------------------------------
