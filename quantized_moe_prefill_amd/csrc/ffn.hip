@@ -289,7 +289,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
                             : (ASYM ? s0 : s0 + SC_SLOT);
     }
   };
-  auto load_a = [&](const GemmTile& ts, int kt, uint8_t* dst) {
+  auto load_a = [&](const GemmTile& ts, int kt, uint8_t* __restrict__ dst) {
 #pragma unroll
     for (int i = 0; i < ALD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -328,14 +328,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     }
   };
   // the scales (and mins) of stage kt from the wave's scale tile
-  auto read_sc = [&](int kt, uint32_t* rs, uint32_t* rm) {
+  auto read_sc = [&](const uint8_t* __restrict__ scw, int kt, uint32_t* rs, uint32_t* rm) {
     const int grp = (lg * 32 + kt * BK) / g.G;
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
       const int row = GATEUP ? 16 * (f & 1) + r16 : 16 * f + r16;
       const int off = (GATEUP && f >= 2 ? SC_SLOT : 0) + (row * KG + grp) * 2;
-      rs[f] = *reinterpret_cast<const uint16_t*>(sc_wave + off);
-      rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(sc_wave + SC_SLOT + off) : 0u;
+      rs[f] = *reinterpret_cast<const uint16_t*>(scw + off);
+      rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(scw + SC_SLOT + off) : 0u;
     }
   };
 
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // results are never stored. The down GEMM swaps the operands
   // (C^T = W A^T), so each lane ends up with four consecutive output
   // columns of one row.
-  auto compute_stage = [&](const uint8_t* as_base, const u32x4* cb, const uint32_t* rs,
+  auto compute_stage = [&](const uint8_t* __restrict__ as_base, const u32x4* cb, const uint32_t* rs,
                            const uint32_t* rm) {
     f16x2 cs[NFRAG], cm[NFRAG];
 #pragma unroll
@@ -486,13 +486,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     refresh_lane();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
     lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
-    if (SCL) read_sc(0, rs, rm);
+    if (SCL) read_sc(sc_wave, 0, rs, rm);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // stage kt reads ring slot kt % 3 and loads stage kt + 2 into slot (kt + 2) % 3
-    auto stage = [&](int kt, const uint8_t* curs, uint8_t* nxt2) {
+    auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2) {
       u32x4 cbn[NFRAG];
       uint32_t rsn[NFRAG], rmn[NFRAG];
       load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       // register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
       compute_stage(curs, cb, rs, rm);
-      if (SCL) read_sc(min(kt + 1, klast), rsn, rmn);
+      if (SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       lds_barrier();
       // the hand-over of the next stage's registers stays here: moved up into
