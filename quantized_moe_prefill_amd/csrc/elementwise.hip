@@ -27,25 +27,39 @@ __device__ __forceinline__ void acc8_f16(float* a, u32x4 v, float w) {
 
 // out[t] = sum_j w[t,j] y_perm[inv[t*k+j]] (+ sw[t] y_sh[t]) (+ res[t]);
 // y_perm and y_sh are fp16, res and out bf16.
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t* __restrict__ yperm, const int32_t* __restrict__ inv,
     const float* __restrict__ tw, const uint16_t* __restrict__ ysh,
-    const float* __restrict__ sw, const uint16_t* res, uint16_t* out, int T, int H, int k) {
+    const float* __restrict__ sw, const uint16_t* res, uint16_t* out, int T, int H) {
   const int cpr = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)T * cpr) return;
   const int t = (int)(idx / cpr);
   const int c = (int)(idx - (int64_t)t * cpr) * 8;
+  // every load of the token is issued before the first sum: the row
+  // indices and weights, then the K rows, the shared row and the residual;
+  // the sums then run in the fixed order j = 0 .. K-1, shared, residual
+  int r[K];
+  float w[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    r[j] = inv[(int64_t)t * K + j];
+    w[j] = tw[(int64_t)t * K + j];
+  }
+  u32x4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = ld16(yperm + (int64_t)r[j] * H + c);
+  u32x4 vs = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+  if (ysh != nullptr) vs = ld16(ysh + (int64_t)t * H + c);
+  if (res != nullptr) vr = ld16(res + (int64_t)t * H + c);
   float a[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) a[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t p = (int64_t)t * k + j;
-    const int r = inv[p];
-    acc8_f16(a, ld16(yperm + (int64_t)r * H + c), tw[p]);
-  }
-  if (ysh != nullptr) acc8_f16(a, ld16(ysh + (int64_t)t * H + c), sw[t]);
-  if (res != nullptr) acc8_bf16(a, ld16(res + (int64_t)t * H + c), 1.f);
+#pragma unroll
+  for (int j = 0; j < K; ++j) acc8_f16(a, v[j], w[j]);
+  if (ysh != nullptr) acc8_f16(a, vs, sw[t]);
+  if (res != nullptr) acc8_bf16(a, vr, 1.f);
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(a[2 * i], a[2 * i + 1]);
@@ -94,8 +108,22 @@ hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const floa
   const int64_t n = (int64_t)T * (H / 8);
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   LaunchScope ls("combine", s);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y_perm, inv, topk_w, y_shared, shared_w,
-                     residual, out, T, H, k);
+#define QMOE_COMBINE(KK)                                                                       \
+  case KK:                                                                                     \
+    hipLaunchKernelGGL(combine_kernel<KK>, grid, block, 0, s, y_perm, inv, topk_w, y_shared,  \
+                       shared_w, residual, out, T, H);                                         \
+    break;
+  switch (k) {
+    QMOE_COMBINE(1)
+    QMOE_COMBINE(2)
+    QMOE_COMBINE(3)
+    QMOE_COMBINE(4)
+    QMOE_COMBINE(5)
+    QMOE_COMBINE(6)
+    QMOE_COMBINE(7)
+    default: QMOE_COMBINE(8)
+  }
+#undef QMOE_COMBINE
   return hipGetLastError();
 }
 

@@ -104,15 +104,27 @@ __global__ __launch_bounds__(PT) void permute_scatter_kernel(
   }
   __syncthreads();
 
-  const int end = min(P, (b + 1) * PCH);
-  for (int p = b * PCH + tid; p < end; p += PT) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) {
-      const int pos = s_base[e] + inv[p];
-      sorted_pairs[pos] = p;
-      inv[p] = pos;
-    } else {
-      inv[p] = 0;
+  // the chunk's ids and ranks are loaded before any is used
+  constexpr int PER = PCH / PT;
+  int ev[PER], rk[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int p = b * PCH + tid + q * PT;
+    ev[q] = p < P ? ids[p] : -1;
+    rk[q] = p < P ? inv[p] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int p = b * PCH + tid + q * PT;
+    if (p < P) {
+      const int e = ev[q];
+      if ((unsigned)e < (unsigned)E) {
+        const int pos = s_base[e] + rk[q];
+        sorted_pairs[pos] = p;
+        inv[p] = pos;
+      } else {
+        inv[p] = 0;
+      }
     }
   }
 }
