@@ -60,6 +60,11 @@ __all__ = [
     "moe_stack",
     "silu",
     "sigmoid",
+    "quantize_rows_i8",
+    "dequant_rows_i8",
+    "expert_ffn_i8",
+    "moe_layer_i8",
+    "moe_layer_rows_i8",
 ]
 
 
@@ -393,3 +398,146 @@ def moe_stack(x_bits, layers, k: int, G: int, quant: str, eps: float, chunk: int
             xc = round_to_bf16(res["out"])
         x[r0:r0 + chunk] = xc
     return x
+
+
+# ---------------------------------------------------------------------------
+# integer route: 8-bit activations x symmetric 4-bit experts
+# ---------------------------------------------------------------------------
+#
+# The pages name an integer MoE prefill route for the symmetric expert file
+# (hipfire 0.4.3 benchmarks page, "Read this before comparing columns": the
+# "symmetric IU4 MoE" route, admitted only on the symmetric file) and an INT8
+# prefill route that replaced an F16 one within a stated quality budget
+# (same page, "Qwen3.8-Flash (Flash-Next)" table, first row). They fix no
+# activation format. The reading used here: each activation row (a token's
+# x, and each (token, expert) row of h) is quantized to 8-bit integers with
+# one scale per row; the products with the 4-bit weights are then exact
+# integer dot products, and the layer is the exact layer evaluated on the
+# 8-bit-rounded activations. So the oracle below is the plain layer on
+# dequantized activations: x^ = q_x * s_x, h^ = q_h * s_h. h is rounded to
+# fp16 before its quantization (the GPU route stores h as fp16 between its
+# two products, and a quantized code is decided on the value actually
+# quantized).
+
+_I8_TINY = 2.0 ** -100
+
+
+def quantize_rows_i8(v32):
+    """Per-row symmetric 8-bit quantization of float32 rows [R][C].
+
+    The decisions are taken in binary32 (the precision of the GPU route):
+    a = max |v| of the row; r = 127 / a and s = a / 127, each a correctly
+    rounded binary32 division; q = rint(v * r), the product rounded to
+    binary32 and then to the nearest integer (ties to even), which lies in
+    [-127, 127] because v * r <= 127 (1 + 2^-24). A row with a < 2^-100
+    (in particular an all-zero row) gets q = 0 and s = 0.
+    Returns (q int8 [R][C], s float32 [R]).
+    """
+    v = np.asarray(v32, dtype=np.float32)
+    a = np.max(np.abs(v), axis=1) if v.shape[1] else np.zeros(v.shape[0], np.float32)
+    ok = a >= np.float32(_I8_TINY)
+    a_safe = np.where(ok, a, np.float32(1.0)).astype(np.float32)
+    r = (np.float32(127.0) / a_safe).astype(np.float32)
+    s = np.where(ok, (a_safe / np.float32(127.0)).astype(np.float32), np.float32(0.0))
+    prod = (v * r[:, None]).astype(np.float32)
+    q = np.clip(np.rint(prod), -127, 127)
+    q = np.where(ok[:, None], q, 0.0).astype(np.int8)
+    return q, s.astype(np.float32)
+
+
+def dequant_rows_i8(q, s) -> np.ndarray:
+    """q [R][C] int8, s [R] -> float64 q * s (exact)."""
+    return np.asarray(q, np.float64) * np.asarray(s, np.float64)[:, None]
+
+
+def _f16_round(v) -> np.ndarray:
+    """float64 -> nearest fp16 (ties to even), as float64."""
+    return np.asarray(v, np.float64).astype(np.float16).astype(np.float64)
+
+
+def _i8_expert(Xhat, W13, W2):
+    """One expert on the integer route: Xhat [n][H] are dequantized 8-bit
+    activations. Returns (h16 [n][I], hq, sh, y [n][H])."""
+    I = W13.shape[0] // 2
+    h = silu(Xhat @ W13[:I].T) * (Xhat @ W13[I:].T)
+    h16 = _f16_round(h)
+    hq, sh = quantize_rows_i8(h16.astype(np.float32))
+    return h16, hq, sh, dequant_rows_i8(hq, sh) @ W2.T
+
+
+def expert_ffn_i8(x_bits, sorted_pairs, offsets, k: int, w: dict, G: int):
+    """The routed experts on the integer route (symmetric weights only).
+
+    1. x (bf16) -> q_x, s_x per token (quantize_rows_i8);
+    2. row r of expert e (offsets[e] <= r < offsets[e+1]) is token
+       t = sorted_pairs[r] // k: h = silu(x^_t Wg^T) * (x^_t Wu^T),
+       x^ = q_x s_x, rounded to fp16;
+    3. h -> q_h, s_h per row (quantize_rows_i8 on the fp16 values);
+    4. y_perm[r] = h^_r Wd^T, h^ = q_h s_h.
+    Products in float64 on the dequantized weights. Returns a dict with xq,
+    sx, h16 [P][I], hq, sh [P], y_perm [P][H] (float64, unweighted).
+    """
+    xq, sx = quantize_rows_i8(bf16_to_f64(x_bits).astype(np.float32))
+    xhat = dequant_rows_i8(xq, sx)
+    E = len(offsets) - 1
+    P = int(offsets[-1])
+    I = w["w13"].shape[1] // 2
+    H = xhat.shape[1]
+    h16 = np.zeros((P, I))
+    hq = np.zeros((P, I), np.int8)
+    sh = np.zeros(P, np.float32)
+    y = np.zeros((P, H))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        W13, W2 = _expert_mats(w, e, G, "sym")
+        X = xhat[np.asarray(sorted_pairs[a:b]) // k]
+        h16[a:b], hq[a:b], sh[a:b], y[a:b] = _i8_expert(X, W13, W2)
+    return dict(xq=xq, sx=sx, h16=h16, hq=hq, sh=sh, y_perm=y)
+
+
+def moe_layer_i8(x_bits, li, k: int, G: int, logits32=None, residual_bits=None):
+    """One MoE layer on the integer route: routing exactly as moe_layer (on
+    the bf16 activations, fp32 logits, optional teacher forcing), experts by
+    expert_ffn_i8, combine as moe_layer. No shared expert."""
+    w = _weights_dict(li)
+    if w["s13"] is not None:
+        raise ValueError("the integer route has no shared expert")
+    xf = bf16_to_f64(x_bits)
+    E = w["w_router"].shape[0]
+    L = router_logits(xf, w["w_router"], w["router_bias"])
+    L32 = L.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
+    ids, tw = select_topk(L32, k)
+    counts, offsets, sorted_pairs, inv = permute(ids, E)
+    f = expert_ffn_i8(x_bits, sorted_pairs, offsets, k, w, G)
+    res = bf16_to_f64(residual_bits) if residual_bits is not None else None
+    out = combine(f["y_perm"], inv, tw, None, None, res)
+    f.update(logits=L, logits32=L32, ids=ids, weights=tw, counts=counts, offsets=offsets,
+             sorted_pairs=sorted_pairs, inv=inv, out=out)
+    return f
+
+
+def moe_layer_rows_i8(x_bits, rows, li, k: int, G: int, logits32_rows=None, cache=None):
+    """moe_layer_i8's output for a subset of tokens (each token's output,
+    its activation scale and its k rows of h depend on its own x row only).
+    Returns dict(ids, weights, out) for the listed rows."""
+    w = _weights_dict(li)
+    rows = np.asarray(rows, dtype=np.int64)
+    xb = np.asarray(x_bits)[rows]
+    xf = bf16_to_f64(xb)
+    L = router_logits(xf, w["w_router"], w["router_bias"])
+    L32 = L.astype(np.float32) if logits32_rows is None else np.asarray(logits32_rows, np.float32)
+    ids, tw = select_topk(L32, k)
+    xq, sx = quantize_rows_i8(xf.astype(np.float32))
+    xhat = dequant_rows_i8(xq, sx)
+    cache = {} if cache is None else cache
+    out = np.zeros_like(xf)
+    for i in range(len(rows)):
+        for j in range(k):
+            e = int(ids[i, j])
+            if e not in cache:
+                cache[e] = _expert_mats(w, e, G, "sym")
+            W13, W2 = cache[e]
+            out[i] += tw[i, j] * _i8_expert(xhat[i:i + 1], W13, W2)[3][0]
+    return dict(ids=ids, weights=tw, logits=L, out=out)

@@ -447,3 +447,161 @@ def test_stack_layer_is_residual_plus_moe_of_norm():
     xn_b = oracle.round_to_bf16(xn)
     moe = oracle.moe_layer(xn_b, layers[0], cfg.k, cfg.G, cfg.quant)["out"]
     assert np.array_equal(a, oracle.round_to_bf16(xf + moe))
+
+
+# ---------------------------------------------------------------------------
+# integer route (8-bit activations x symmetric 4-bit weights)
+# ---------------------------------------------------------------------------
+
+def test_quantize_rows_i8_hand_values():
+    v = np.array([[1.0, -2.0, 0.5, 0.0],
+                  [0.0, 0.0, 0.0, 0.0],
+                  [1e-35, -1e-35, 0.0, 0.0]], np.float32)
+    q, s = oracle.quantize_rows_i8(v)
+    # row 0: max 2 -> r = 63.5 exactly; 1 * 63.5 = 63.5 ties to the even 64,
+    # 0.5 * 63.5 = 31.75 -> 32, -2 * 63.5 = -127
+    assert q[0].tolist() == [64, -127, 32, 0]
+    assert s[0] == np.float32(2.0 / 127.0)
+    # all-zero and negligible rows quantize to zero with a zero scale
+    assert q[1].tolist() == [0, 0, 0, 0] and s[1] == 0.0
+    assert q[2].tolist() == [0, 0, 0, 0] and s[2] == 0.0
+
+
+def test_quantize_rows_i8_integer_rows_are_exact():
+    # v = c * j with integer |j| <= 127, max |j| = 127 and c a power of two:
+    # r = 1/c and s = c exactly, so q must reproduce j
+    rng = np.random.default_rng(3)
+    j = rng.integers(-127, 128, size=(5, 64))
+    j[:, 7] = np.array([127, -127, 127, -127, 127])
+    for c in (1.0, 2.0 ** -6, 2.0 ** 9):
+        q, s = oracle.quantize_rows_i8((j * c).astype(np.float32))
+        assert np.array_equal(q.astype(np.int64), j)
+        assert np.all(s == np.float32(c))
+
+
+def test_quantize_rows_i8_error_bound_random():
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal((64, 300)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    q, s = oracle.quantize_rows_i8(v)
+    vv = v.astype(np.float64)
+    a = np.abs(vv).max(axis=1)
+    err = np.abs(q.astype(np.float64) * s.astype(np.float64)[:, None] - vv)
+    # |q s - v| <= s/2 up to the binary32 roundings of r, of v*r and of s
+    assert np.all(err <= (0.5 + 1e-5) * s[:, None] + 1e-6 * a[:, None])
+    assert np.all(np.abs(q.astype(np.int64)).max(axis=1) == 127)
+    assert np.all((q == 0) | (np.sign(q) == np.sign(v)))
+    # the scale is a / 127 to within binary32 rounding
+    assert np.allclose(s, a / 127.0, rtol=2 ** -23, atol=0)
+
+
+def _int_route_expert_bruteforce(xq, sx, nib13, sc13, nib2, sc2, G):
+    """The integer route of one expert on a few rows, written out with
+    Python integers per quantization group: gate/up sums of q_x * (n - 8)
+    per group of G, times the group's scale, times the row scale; down the
+    same on the fp16-rounded, re-quantized h (quantizer and fp16 rounding
+    applied between the two products as the route defines)."""
+    n_rows, H = xq.shape
+    I = nib13.shape[0] // 2
+    y = np.zeros((n_rows, nib2.shape[0]))
+    for r in range(n_rows):
+        acc = []
+        for n in range(2 * I):
+            tot = Fraction(0)
+            for g0 in range(0, H, G):
+                isum = sum(int(xq[r, kk]) * (int(nib13[n, kk]) - 8) for kk in range(g0, g0 + G))
+                tot += Fraction(float(sc13[n, g0 // G])) * isum
+            acc.append(tot * Fraction(float(sx[r])))
+        g = np.array([float(a) for a in acc[:I]])
+        u = np.array([float(a) for a in acc[I:]])
+        h16 = (g / (1.0 + np.exp(-g)) * u).astype(np.float16).astype(np.float32)
+        hq, sh = oracle.quantize_rows_i8(h16[None, :])
+        for c in range(nib2.shape[0]):
+            tot = Fraction(0)
+            for g0 in range(0, I, G):
+                isum = sum(int(hq[0, i]) * (int(nib2[c, i]) - 8) for i in range(g0, g0 + G))
+                tot += Fraction(float(sc2[c, g0 // G])) * isum
+            y[r, c] = float(tot * Fraction(float(sh[0])))
+    return y
+
+
+def test_i8_expert_ffn_matches_integer_bruteforce_tiny():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny"], T=6, H=32, E=2, k=1, I=16, G=8)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    ids = np.array([[0], [1], [1], [0], [1], [0]])
+    counts, offsets, sp, inv = oracle.permute(ids, cfg.E)
+    w = oracle.moe_oracle._weights_dict(li)
+    f = oracle.expert_ffn_i8(xb, sp, offsets, 1, w, cfg.G)
+    # the quantized activations are the quantizer's, row by row
+    xq, sx = oracle.quantize_rows_i8(oracle.bf16_to_f64(xb).astype(np.float32))
+    assert np.array_equal(f["xq"], xq) and np.array_equal(f["sx"], sx)
+    for e in range(cfg.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        toks = np.asarray(sp[a:b])
+        nib13 = oracle.unpack_nibbles(w["w13"][e])
+        nib2 = oracle.unpack_nibbles(w["w2"][e])
+        sc13 = w["w13_scale"][e].view(np.float16)
+        sc2 = w["w2_scale"][e].view(np.float16)
+        ref = _int_route_expert_bruteforce(xq[toks], sx[toks], nib13, sc13, nib2, sc2, cfg.G)
+        assert np.allclose(f["y_perm"][a:b], ref, rtol=1e-9, atol=1e-12)
+
+
+def test_i8_route_is_fp_route_on_representable_activations():
+    # activations that are already 8-bit codes times a power of two: the
+    # integer route's gate/up products equal the floating-point route's, so
+    # its h is the fp route's h rounded to fp16
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny"], T=8, G=128)
+    li = make_layer(cfg)
+    rng = np.random.default_rng(5)
+    j = rng.integers(-127, 128, size=(cfg.T, cfg.H))
+    j[:, 0] = 127
+    xb = _bf16(j * 2.0 ** -5)
+    fp = oracle.moe_layer(xb, li, cfg.k, cfg.G, "sym")
+    i8 = oracle.moe_layer_i8(xb, li, cfg.k, cfg.G)
+    assert np.array_equal(i8["sorted_pairs"], fp["sorted_pairs"])
+    assert np.array_equal(i8["h16"], fp["h_perm"].astype(np.float16).astype(np.float64))
+
+
+def test_i8_route_error_against_fp_route():
+    # the integer route differs from the exact layer by the 8-bit rounding of
+    # x and h only: its relative error is that of the activations (about
+    # max/(127 sqrt(12)) of each row's RMS: ~1 % for Gaussian x, a few % for
+    # the heavier-tailed h), far from zero and far below order one
+    from dataclasses import replace
+    cfg = replace(CONFIGS["a3b_pp512"], T=32, H=256, E=16, I=128)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    fp = oracle.moe_layer(xb, li, cfg.k, cfg.G, "sym")
+    i8 = oracle.moe_layer_i8(xb, li, cfg.k, cfg.G, logits32=fp["logits32"])
+    rel = np.linalg.norm(i8["out"] - fp["out"]) / np.linalg.norm(fp["out"])
+    assert 1e-3 < rel < 5e-2, rel
+    # each x row's rounding error is bounded by half its scale
+    xf = oracle.bf16_to_f64(xb)
+    xhat = oracle.dequant_rows_i8(i8["xq"], i8["sx"])
+    assert np.all(np.abs(xhat - xf) <= 0.5001 * i8["sx"].astype(np.float64)[:, None])
+
+
+def test_i8_zero_token_gives_zero_output():
+    cfg = CONFIGS["tiny"]
+    from dataclasses import replace
+    cfg = replace(cfg, G=128)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg)).copy()
+    xb[3] = 0
+    r = oracle.moe_layer_i8(xb, li, cfg.k, cfg.G)
+    assert np.all(r["out"][3] == 0.0) and np.all(r["sx"][3] == 0.0)
+    assert np.any(r["out"][2] != 0.0)
+
+
+def test_i8_rows_subset_matches_full_layer():
+    from dataclasses import replace
+    cfg = replace(CONFIGS["tiny"], G=128)
+    li = make_layer(cfg)
+    xb = _xbits(make_tokens(cfg))
+    full = oracle.moe_layer_i8(xb, li, cfg.k, cfg.G)
+    rows = [0, 9, 63, 31]
+    sub = oracle.moe_layer_rows_i8(xb, rows, li, cfg.k, cfg.G)
+    assert np.array_equal(sub["ids"], full["ids"][rows])
+    assert np.allclose(sub["out"], full["out"][rows], rtol=1e-12, atol=1e-15)
