@@ -1,6 +1,9 @@
 """MoE-layer prefill benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload a3b_pp8192] [--no-cpu]
+    python bench.py --route i8 ...        the integer route (moe_layer_forward_i8):
+                                          8-bit activations on the int8 matrix cores,
+                                          gate/up roofline against the int8 peak
     python bench.py --calib-copy ...      also run a 1 GiB device copy (counter scale)
     python bench.py --pmc-summary FETCH.csv WRITE.csv
                                           HBM bytes per launch from two rocprofv3
@@ -30,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_I8_TOPS = 5000.0       # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer prefill tokens/sec at T=8192; % of bf16 MFMA peak and HBM GB/s"
 
@@ -37,6 +41,8 @@ METRIC = "MoE-layer prefill tokens/sec at T=8192; % of bf16 MFMA peak and HBM GB
 KERNELS = ("router_split", "router_gemm", "router_select", "permute_rank", "permute_scatter",
            "x_to_f16", "gateup_gemm", "down_gemm", "shared_gateup_gemm", "shared_down_gemm",
            "combine")
+KERNELS_I8 = ("router_split", "router_gemm", "router_select", "permute_rank", "permute_scatter",
+              "quant_x_i8", "gateup_gemm_i8", "quant_h_i8", "down_gemm_i8", "combine")
 
 # HBM bytes per gate/up launch on the a3b_pp8192 workload, from rocprofv3
 # FETCH_SIZE + WRITE_SIZE (each scaled by the copy-kernel calibration factor),
@@ -66,6 +72,8 @@ def parse():
     ap.add_argument("--workload", default="a3b_pp8192")
     ap.add_argument("--T", type=int, default=0, help="rows (default: the workload's T)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--route", choices=("fp16", "i8"), default="fp16",
+                    help="expert route: fp16 matrix cores (default) or the integer route")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one elementwise kernel that reads and writes 1 GiB "
                          "(counter calibration)")
@@ -126,7 +134,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
     print(f"gemm source hash {gemm_source_hash()}")
 
 
-def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8):
+def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False):
     """The oracle as it stands, on the whole batch, repeated until about
     min_seconds of CPU work (at most max_passes passes)."""
     import numpy as np
@@ -145,7 +153,10 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8):
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
+        if i8:
+            oracle.moe_layer_i8(xb, cpu, cfg.k, cfg.G)
+        else:
+            oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
         dt += time.perf_counter() - t0
         passes += 1
     return {
@@ -154,7 +165,8 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8):
         "cores": blas_threads or cores,
         "kind": "oracle",
         "sample": f"the whole {x.shape[0]}-token batch, {passes} passes of the float64 numpy "
-                  f"oracle (dequantize all experts + route + experts + combine), {dt:.1f} s in "
+                  f"oracle{' (integer route)' if i8 else ''} (dequantize all experts + route + "
+                  f"experts + combine), {dt:.1f} s in "
                   f"total; {cores} cores visible, BLAS threads {blas_threads}",
     }
 
@@ -210,6 +222,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stacked = cfg.n_layers > 1
+    i8 = a.route == "i8"
+    if i8 and (stacked or cfg.quant != "sym" or cfg.G != 128 or cfg.shared_I):
+        print(f"the integer route needs one layer of symmetric experts with group 128 and no "
+              f"shared expert ({cfg.name} is not)", file=sys.stderr)
+        sys.exit(2)
     x = make_tokens(cfg, device=dev, rows=T)
     if stacked:
         layers = [make_stack_layer(cfg, l, device=dev) for l in range(cfg.n_layers)]
@@ -222,11 +239,20 @@ def main():
         li = layers[0]
     else:
         li = make_layer(cfg, device=dev)
-        layer = qm.MoELayer(cfg, li, dev, T)
         out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        if i8:
+            shape = qm.shape_of(cfg)
+            experts = qm.Experts(li)
+            ws = qm.workspace(shape, T, dev, qm.MOE_WS_LAYER_I8)
 
-        def step():
-            layer.forward(x, out=out)
+            def step():
+                qm.moe_layer_forward_i8(shape, x, li.w_router, li.router_bias, experts, out=out,
+                                        ws=ws)
+        else:
+            layer = qm.MoELayer(cfg, li, dev, T)
+
+            def step():
+                layer.forward(x, out=out)
     torch.cuda.synchronize()
 
     for _ in range(a.warmup):
@@ -298,7 +324,7 @@ def main():
         step()
     torch.cuda.synchronize()
     kernels = {}
-    for name in KERNELS + ("rmsnorm",):
+    for name in (KERNELS_I8 if i8 else KERNELS) + ("rmsnorm",):
         n, tot = qm.profile_read(name)
         if n:
             kernels[name] = round(tot / n * 1000.0, 2)  # microseconds per launch
@@ -313,7 +339,8 @@ def main():
     chunk_rows = min(cfg.chunk or T, T)
     gu_launch_rows = chunk_rows if stacked else T
     gu_flops = 4.0 * cfg.H * cfg.I * gu_launch_rows * cfg.k
-    gu_us = kernels.get("gateup_gemm")
+    gu_name = "gateup_gemm_i8" if i8 else "gateup_gemm"
+    gu_us = kernels.get(gu_name)
     achieved = gu_flops / (gu_us * 1e-6) / 1e12 if gu_us else None
     total_flops = layer_flops(T) * n_apps
     layer_tflops = total_flops / (ms * 1e-3) / 1e12
@@ -330,23 +357,24 @@ def main():
     # the token rows once, h written
     per = 2 if cfg.quant == "sym" else 4
     gu_bytes = (active * (cfg.I * cfg.H + 2 * cfg.I * (cfg.H // cfg.G) * per)
-                + T * cfg.H * 2 + P * cfg.I * 2)
+                + T * cfg.H * (1 if i8 else 2) + P * cfg.I * 2)
+    peak = PEAK_I8_TOPS if i8 else PEAK_BF16_TFLOPS
     if cold:
         gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9 if gu_us else None
-        roofline = {"kernel": "gateup_gemm", "bound": "hbm",
+        roofline = {"kernel": gu_name, "bound": "hbm",
                     "achieved": round(gu_gbs, 1) if gu_gbs else None, "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gu_gbs / PEAK_HBM_GBS, 4) if gu_gbs else None,
                     "traffic": None, "bytes_per_launch": gu_bytes}
     else:
         roofline = {
-            "kernel": "gateup_gemm",
+            "kernel": gu_name,
             "bound": "mfma",
             "achieved": round(achieved, 1) if achieved else None,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+            "peak": peak,
+            "unit": "TOP/s" if i8 else "TFLOP/s",
+            "frac": round(achieved / peak, 4) if achieved else None,
             "traffic": (GATEUP_TRAFFIC.get(gemm_source_hash())
-                        if (cfg.name, T) == ("a3b_pp8192", 8192) else None),
+                        if (cfg.name, T, i8) == ("a3b_pp8192", 8192, False) else None),
             "flops_per_launch": gu_flops,
         }
 
@@ -367,16 +395,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": "i8" if i8 else "fp16",
         "data": "synthetic",
         "config": {
             "workload": desc,
             "T": T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I,
             "group": cfg.G, "quant": cfg.quant, "shared_inter": cfg.shared_I,
-            "layers": cfg.n_layers,
+            "layers": cfg.n_layers, "route": "int8 activations" if i8 else "fp16",
         },
         "layer_tflops": round(layer_tflops, 1),
-        "layer_mfma_frac": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+        "layer_mfma_frac": round(layer_tflops / peak, 4),
         "active_experts": active,
         "layer_hbm_gbs": round(hbm_gbs, 1),
         "layer_hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
@@ -403,7 +431,7 @@ def main():
         if stacked:
             rec["cpu_baseline"] = stack_cpu_baseline(cfg, [l.to("cpu") for l in layers[:2]], x)
         else:
-            rec["cpu_baseline"] = cpu_baseline(cfg, li, x)
+            rec["cpu_baseline"] = cpu_baseline(cfg, li, x, i8=i8)
     print(json.dumps(rec), flush=True)
 
 

@@ -104,7 +104,9 @@ typedef enum {
   MOE_WS_LAYER = 0,       /* moe_layer_forward */
   MOE_WS_ROUTE = 1,       /* moe_route */
   MOE_WS_PERMUTE = 2,     /* moe_permute */
-  MOE_WS_EXPERT_FFN = 3   /* moe_expert_ffn */
+  MOE_WS_EXPERT_FFN = 3,  /* moe_expert_ffn */
+  MOE_WS_LAYER_I8 = 4,    /* moe_layer_forward_i8 */
+  MOE_WS_EXPERT_FFN_I8 = 5 /* moe_expert_ffn_i8 */
 } moe_ws_kind_t;
 
 int moe_abi_version(void);
@@ -191,6 +193,55 @@ moe_status_t moe_layer_forward(const moe_shape_t *shape, int64_t T, const uint16
                                const float *shared_gate, const moe_experts_t *experts,
                                const uint16_t *residual, uint16_t *out, void *ws,
                                size_t ws_bytes, hipStream_t stream);
+
+/* ---- integer route: 8-bit activations x symmetric 4-bit experts ----------
+ * The pages admit an integer MoE prefill route for the symmetric expert file
+ * only (hipfire 0.4.3 benchmarks page, "Read this before comparing columns":
+ * the "symmetric IU4 MoE" route) and report an INT8 prefill route replacing
+ * an F16 one within a quality budget (same page, "Qwen3.8-Flash
+ * (Flash-Next)" table). This library's definition of that route:
+ *   - every activation row is quantized to int8 with one scale per row
+ *     (moe_quantize_rows_i8): x per token; h per (token, expert) row, after
+ *     rounding h to fp16;
+ *   - the expert products are then exact: y = s_row * sum over groups of
+ *     scale_g * sum_k q[k] * (nibble[k] - 8), int32 per group of 128,
+ *     scales applied in fp32.
+ * So the result is the exact layer evaluated on the 8-bit-rounded
+ * activations; it differs from moe_expert_ffn by that rounding (about 1 % of
+ * x's RMS per element for Gaussian rows, more for heavy-tailed h rows).
+ * Supported: quant == MOE_Q4_SYM, group_size == 128, shared_inter == 0
+ * (MOE_ERR_UNSUPPORTED otherwise), and T * H, T * k * I and the packed
+ * weight bytes E * 2I * H / 2 below 2^31. */
+
+/* Per-row int8 quantization of bf16 rows x [rows][cols] (cols % 8 == 0):
+ *   a = max_c |x[r,c]|;  scale[r] = a / 127;
+ *   q[r,c] = rint(x[r,c] * (127 / a))   (ties to even, in [-127, 127]),
+ * with both divisions correctly rounded and the product rounded to fp32
+ * before rint; a row with a < 2^-100 gives q = 0 and scale = 0.
+ *   q [rows][cols] int8 (natural order), scale [rows] fp32.              */
+moe_status_t moe_quantize_rows_i8(int64_t rows, int64_t cols, const uint16_t *x, int8_t *q,
+                                  float *scale, hipStream_t stream);
+
+/* moe_expert_ffn on the integer route (see above); same arguments, no shared
+ * expert. y_perm [P][H] fp16, unweighted.
+ *   h_perm  [P][I] fp16 or NULL: if given, receives the fp16 h rows (row r
+ *           of expert-sorted order) from which the int8 h is quantized
+ *   ws  >= moe_workspace_size(MOE_WS_EXPERT_FFN_I8, T) bytes (int8 x and its
+ *          scales, fp16 h, int8 h and its scales)                          */
+moe_status_t moe_expert_ffn_i8(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                               const moe_experts_t *experts, const int32_t *counts,
+                               const int32_t *offsets, const int32_t *sorted_pairs,
+                               uint16_t *y_perm, uint16_t *h_perm, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* moe_layer_forward with the experts on the integer route: routing, grouping
+ * and combine exactly as moe_layer_forward (fp32 router on the bf16 x).
+ *   ws  >= moe_workspace_size(MOE_WS_LAYER_I8, T) bytes                   */
+moe_status_t moe_layer_forward_i8(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                                  const float *w_router, const float *router_bias,
+                                  const moe_experts_t *experts, const uint16_t *residual,
+                                  uint16_t *out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* RMSNorm over rows of [T][H] bf16:
  *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )

@@ -455,17 +455,21 @@ def _f16_round(v) -> np.ndarray:
     return np.asarray(v, np.float64).astype(np.float16).astype(np.float64)
 
 
-def _i8_expert(Xhat, W13, W2):
-    """One expert on the integer route: Xhat [n][H] are dequantized 8-bit
-    activations. Returns (h16 [n][I], hq, sh, y [n][H])."""
+def _i8_gateup(Xhat, W13):
+    """Gate/up of one expert on the integer route: Xhat [n][H] are
+    dequantized 8-bit activations. Returns h [n][I] rounded to fp16."""
     I = W13.shape[0] // 2
-    h = silu(Xhat @ W13[:I].T) * (Xhat @ W13[I:].T)
-    h16 = _f16_round(h)
-    hq, sh = quantize_rows_i8(h16.astype(np.float32))
-    return h16, hq, sh, dequant_rows_i8(hq, sh) @ W2.T
+    return _f16_round(silu(Xhat @ W13[:I].T) * (Xhat @ W13[I:].T))
 
 
-def expert_ffn_i8(x_bits, sorted_pairs, offsets, k: int, w: dict, G: int):
+def _i8_down(h16, W2):
+    """Down projection of fp16 h rows on the integer route: returns
+    (hq, sh, y)."""
+    hq, sh = quantize_rows_i8(np.asarray(h16, np.float64).astype(np.float32))
+    return hq, sh, dequant_rows_i8(hq, sh) @ W2.T
+
+
+def expert_ffn_i8(x_bits, sorted_pairs, offsets, k: int, w: dict, G: int, h16_forced=None):
     """The routed experts on the integer route (symmetric weights only).
 
     1. x (bf16) -> q_x, s_x per token (quantize_rows_i8);
@@ -476,6 +480,11 @@ def expert_ffn_i8(x_bits, sorted_pairs, offsets, k: int, w: dict, G: int):
     4. y_perm[r] = h^_r Wd^T, h^ = q_h s_h.
     Products in float64 on the dequantized weights. Returns a dict with xq,
     sx, h16 [P][I], hq, sh [P], y_perm [P][H] (float64, unweighted).
+
+    h16_forced [P][I] (teacher forcing): steps 3-4 take these fp16 values
+    instead of the oracle's own h. A quantized code is decided on the value
+    actually quantized; h computed in another order rounds to fp16
+    differently in rare cases, and then a code can differ by one step.
     """
     xq, sx = quantize_rows_i8(bf16_to_f64(x_bits).astype(np.float32))
     xhat = dequant_rows_i8(xq, sx)
@@ -493,14 +502,18 @@ def expert_ffn_i8(x_bits, sorted_pairs, offsets, k: int, w: dict, G: int):
             continue
         W13, W2 = _expert_mats(w, e, G, "sym")
         X = xhat[np.asarray(sorted_pairs[a:b]) // k]
-        h16[a:b], hq[a:b], sh[a:b], y[a:b] = _i8_expert(X, W13, W2)
+        h16[a:b] = _i8_gateup(X, W13)
+        hin = h16[a:b] if h16_forced is None else np.asarray(h16_forced, np.float64)[a:b]
+        hq[a:b], sh[a:b], y[a:b] = _i8_down(hin, W2)
     return dict(xq=xq, sx=sx, h16=h16, hq=hq, sh=sh, y_perm=y)
 
 
-def moe_layer_i8(x_bits, li, k: int, G: int, logits32=None, residual_bits=None):
+def moe_layer_i8(x_bits, li, k: int, G: int, logits32=None, residual_bits=None,
+                 h16_forced=None):
     """One MoE layer on the integer route: routing exactly as moe_layer (on
     the bf16 activations, fp32 logits, optional teacher forcing), experts by
-    expert_ffn_i8, combine as moe_layer. No shared expert."""
+    expert_ffn_i8 (h16_forced as there), combine as moe_layer. No shared
+    expert."""
     w = _weights_dict(li)
     if w["s13"] is not None:
         raise ValueError("the integer route has no shared expert")
@@ -510,7 +523,7 @@ def moe_layer_i8(x_bits, li, k: int, G: int, logits32=None, residual_bits=None):
     L32 = L.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
     ids, tw = select_topk(L32, k)
     counts, offsets, sorted_pairs, inv = permute(ids, E)
-    f = expert_ffn_i8(x_bits, sorted_pairs, offsets, k, w, G)
+    f = expert_ffn_i8(x_bits, sorted_pairs, offsets, k, w, G, h16_forced=h16_forced)
     res = bf16_to_f64(residual_bits) if residual_bits is not None else None
     out = combine(f["y_perm"], inv, tw, None, None, res)
     f.update(logits=L, logits32=L32, ids=ids, weights=tw, counts=counts, offsets=offsets,
@@ -518,10 +531,13 @@ def moe_layer_i8(x_bits, li, k: int, G: int, logits32=None, residual_bits=None):
     return f
 
 
-def moe_layer_rows_i8(x_bits, rows, li, k: int, G: int, logits32_rows=None, cache=None):
+def moe_layer_rows_i8(x_bits, rows, li, k: int, G: int, logits32_rows=None, cache=None,
+                      h16_rows=None):
     """moe_layer_i8's output for a subset of tokens (each token's output,
     its activation scale and its k rows of h depend on its own x row only).
-    Returns dict(ids, weights, out) for the listed rows."""
+    h16_rows [len(rows)][k][I]: teacher forcing of the fp16 h of each
+    (token, slot), as in expert_ffn_i8. Returns dict(ids, weights, out, h16)
+    for the listed rows."""
     w = _weights_dict(li)
     rows = np.asarray(rows, dtype=np.int64)
     xb = np.asarray(x_bits)[rows]
@@ -533,11 +549,15 @@ def moe_layer_rows_i8(x_bits, rows, li, k: int, G: int, logits32_rows=None, cach
     xhat = dequant_rows_i8(xq, sx)
     cache = {} if cache is None else cache
     out = np.zeros_like(xf)
+    I = w["w13"].shape[1] // 2
+    h16 = np.zeros((len(rows), k, I))
     for i in range(len(rows)):
         for j in range(k):
             e = int(ids[i, j])
             if e not in cache:
                 cache[e] = _expert_mats(w, e, G, "sym")
             W13, W2 = cache[e]
-            out[i] += tw[i, j] * _i8_expert(xhat[i:i + 1], W13, W2)[3][0]
-    return dict(ids=ids, weights=tw, logits=L, out=out)
+            h16[i, j] = _i8_gateup(xhat[i:i + 1], W13)[0]
+            hin = h16[i, j] if h16_rows is None else np.asarray(h16_rows, np.float64)[i, j]
+            out[i] += tw[i, j] * _i8_down(hin[None, :], W2)[2][0]
+    return dict(ids=ids, weights=tw, logits=L, out=out, h16=h16)

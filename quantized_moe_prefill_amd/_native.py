@@ -24,6 +24,8 @@ MOE_WS_LAYER = 0
 MOE_WS_ROUTE = 1
 MOE_WS_PERMUTE = 2
 MOE_WS_EXPERT_FFN = 3
+MOE_WS_LAYER_I8 = 4
+MOE_WS_EXPERT_FFN_I8 = 5
 
 # Every symbol include/moe.h declares.
 EXPORTED = [
@@ -35,6 +37,9 @@ EXPORTED = [
     "moe_expert_ffn",
     "moe_combine",
     "moe_layer_forward",
+    "moe_quantize_rows_i8",
+    "moe_expert_ffn_i8",
+    "moe_layer_forward_i8",
     "moe_rmsnorm",
     "moe_profile_enable",
     "moe_profile_reset",
@@ -102,6 +107,12 @@ def lib():
     L.moe_combine.argtypes = [sp, i64, P, P, P, P, P, P, P, P]
     L.moe_layer_forward.restype = st
     L.moe_layer_forward.argtypes = [sp, i64, P, P, P, P, ep, P, P, P, ctypes.c_size_t, P]
+    L.moe_quantize_rows_i8.restype = st
+    L.moe_quantize_rows_i8.argtypes = [i64, i64, P, P, P, P]
+    L.moe_expert_ffn_i8.restype = st
+    L.moe_expert_ffn_i8.argtypes = [sp, i64, P, ep, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_layer_forward_i8.restype = st
+    L.moe_layer_forward_i8.argtypes = [sp, i64, P, P, P, ep, P, P, P, ctypes.c_size_t, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 BUILDDIR = os.path.join(ROOT, "_build")
 LIBNAME = "libqmoe.so"
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "ffn.hip", "ffn_stream.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "ffn.hip", "ffn_stream.hip", "ffn_i8.hip", "elementwise.hip"]
 ARCH = "gfx950"
 
 

@@ -153,6 +153,50 @@ static size_t ffn_ws(const Shape& s, int64_t T) {
   return al((size_t)T * s.H * 2) + al(P * s.I * 2) + al((size_t)T * s.Is * 2);
 }
 
+// ---- integer route ----
+static moe_status_t check_i8(const Shape& s, int64_t T) {
+  if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "the integer route needs MOE_Q4_SYM experts");
+  if (s.G != 128) return fail(MOE_ERR_UNSUPPORTED, "the integer route needs group_size 128");
+  if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "the integer route has no shared expert");
+  const int64_t lim = int64_t(1) << 31;
+  if (T * s.H >= lim || T * s.k * s.I >= lim || (int64_t)s.E * s.I * s.H >= lim)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the integer route needs T*H, T*k*I and E*2I*H/2 below 2^31");
+  return MOE_OK;
+}
+
+struct LayoutI8 {
+  size_t xq, sx, h16, hq, sh, total;
+};
+// moe_expert_ffn_i8 scratch: int8 x and scales, fp16 h, int8 h and scales
+static LayoutI8 ffn_i8_layout(const Shape& s, int64_t T, size_t base) {
+  LayoutI8 L{};
+  const size_t P = (size_t)T * s.k;
+  size_t o = base;
+  L.xq = o;  o = al(o + (size_t)T * s.H);
+  L.sx = o;  o = al(o + (size_t)T * 4);
+  L.h16 = o; o = al(o + P * s.I * 2);
+  L.hq = o;  o = al(o + P * s.I);
+  L.sh = o;  o = al(o + P * 4);
+  L.total = o;
+  return L;
+}
+// moe_layer_forward_i8: routing and grouping regions of the layer layout,
+// then the integer FFN scratch, then y_perm
+struct LayerI8 {
+  Layout r;
+  LayoutI8 f;
+  size_t yperm, total;
+};
+static LayerI8 layer_i8_layout(const Shape& s, int64_t T) {
+  LayerI8 L{};
+  L.r = layer_layout(s, T);
+  L.f = ffn_i8_layout(s, T, L.r.x16);  // replaces x16 .. ysh of the fp16 layer
+  L.yperm = L.f.total;
+  L.total = al(L.yperm + (size_t)T * s.k * s.H * 2);
+  return L;
+}
+
 static moe_status_t check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return MOE_OK;
   if (ws == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL (need %zu bytes)", need);
@@ -339,6 +383,52 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   return MOE_OK;
 }
 
+static moe_status_t ffn_i8_impl(const Shape& s, int64_t T, const uint16_t* x,
+                                const moe_experts_t* w, const int32_t* counts,
+                                const int32_t* offsets, const int32_t* sorted, uint16_t* yperm,
+                                uint16_t* h_out, uint8_t* base, const LayoutI8& L,
+                                hipStream_t st) {
+  const int P = (int)(T * s.k);
+  auto* xq = reinterpret_cast<int8_t*>(base + L.xq);
+  auto* sx = reinterpret_cast<float*>(base + L.sx);
+  auto* h16 = h_out != nullptr ? h_out : reinterpret_cast<uint16_t*>(base + L.h16);
+  auto* hq = reinterpret_cast<int8_t*>(base + L.hq);
+  auto* sh = reinterpret_cast<float*>(base + L.sh);
+  QMOE_HIP(launch_quant_rows_i8(x, false, (int)T, s.H, true, xq, sx, st), "quantize x launch");
+  GemmI8 g{};
+  g.A = xq;
+  g.a_scale = sx;
+  g.gather = sorted;
+  g.gather_div = s.k;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.E = s.E;
+  g.max_rows = P;
+  g.a_rows = (int)T;
+  g.W = w->w13;
+  g.Wscale = w->w13_scale;
+  g.N = 2 * s.I;
+  g.K = s.H;
+  g.C = h16;
+  g.ldc = s.I;
+  QMOE_HIP(launch_gateup_i8(g, st), "gateup (int8) launch");
+  QMOE_HIP(launch_quant_rows_i8(h16, true, P, s.I, true, hq, sh, st), "quantize h launch");
+  GemmI8 d = g;
+  d.A = hq;
+  d.a_scale = sh;
+  d.gather = nullptr;
+  d.gather_div = 1;
+  d.a_rows = P;
+  d.W = w->w2;
+  d.Wscale = w->w2_scale;
+  d.N = s.H;
+  d.K = s.I;
+  d.C = yperm;
+  d.ldc = s.H;
+  QMOE_HIP(launch_down_i8(d, st), "down (int8) launch");
+  return MOE_OK;
+}
+
 }  // namespace qmoe
 
 using namespace qmoe;
@@ -364,6 +454,12 @@ moe_status_t moe_workspace_size(const moe_shape_t* shape, int64_t T, int32_t kin
     case MOE_WS_ROUTE: *bytes = route_ws(s, T); break;
     case MOE_WS_PERMUTE: *bytes = al(permute_ws_bytes((int)(T * s.k), s.E)); break;
     case MOE_WS_EXPERT_FFN: *bytes = ffn_ws(s, T); break;
+    case MOE_WS_LAYER_I8:
+    case MOE_WS_EXPERT_FFN_I8:
+      st = check_i8(s, T);
+      if (st != MOE_OK) return st;
+      *bytes = kind == MOE_WS_LAYER_I8 ? layer_i8_layout(s, T).total : ffn_i8_layout(s, T, 0).total;
+      break;
     default: return fail(MOE_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", kind);
   }
   return MOE_OK;
@@ -535,6 +631,97 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
   st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs, stream);
   if (st != MOE_OK) return st;
   QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_quantize_rows_i8(int64_t rows, int64_t cols, const uint16_t* x, int8_t* q,
+                                  float* scale, hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "rows must be >= 0 and cols > 0");
+  if (cols % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 8");
+  if (rows >= (int64_t(1) << 31) || cols >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "rows and cols must be below 2^31");
+  if (rows == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(q, "q");
+  QMOE_REQUIRE(scale, "scale");
+  QMOE_HIP(launch_quant_rows_i8(x, false, (int)rows, (int)cols, false, q, scale, stream),
+           "quantize launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_i8(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                               const moe_experts_t* experts, const int32_t* counts,
+                               const int32_t* offsets, const int32_t* sorted_pairs,
+                               uint16_t* y_perm, uint16_t* h_perm, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  st = check_i8(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  st = check_experts(s, experts);
+  if (st != MOE_OK) return st;
+  QMOE_REQUIRE(counts, "counts");
+  QMOE_REQUIRE(offsets, "offsets");
+  QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
+  QMOE_REQUIRE(y_perm, "y_perm");
+  QMOE_OPTIONAL(h_perm, "h_perm");
+  const LayoutI8 L = ffn_i8_layout(s, T, 0);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  return ffn_i8_impl(s, T, x, experts, counts, offsets, sorted_pairs, y_perm, h_perm,
+                     static_cast<uint8_t*>(ws), L, stream);
+}
+
+moe_status_t moe_layer_forward_i8(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                  const float* w_router, const float* router_bias,
+                                  const moe_experts_t* experts, const uint16_t* residual,
+                                  uint16_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  st = check_i8(s, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(out, "out");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(residual, "residual");
+  st = check_experts(s, experts);
+  if (st != MOE_OK) return st;
+  const LayerI8 L = layer_i8_layout(s, T);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  auto* split = reinterpret_cast<uint16_t*>(b + L.r.split);
+  auto* partial = reinterpret_cast<float*>(b + L.r.partial);
+  auto* hist = reinterpret_cast<int32_t*>(b + L.r.hist);
+  auto* ids = reinterpret_cast<int32_t*>(b + L.r.ids);
+  auto* tw = reinterpret_cast<float*>(b + L.r.tw);
+  auto* counts = reinterpret_cast<int32_t*>(b + L.r.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(b + L.r.offsets);
+  auto* sorted = reinterpret_cast<int32_t*>(b + L.r.sorted);
+  auto* inv = reinterpret_cast<int32_t*>(b + L.r.inv);
+  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
+  if (router_uses_gemv((int)T)) {
+    QMOE_HIP(launch_route_permute_small(x, w_router, nullptr, partial, router_bias, (int)T, s.H,
+                                        s.E, s.k, ids, tw, nullptr, counts, offsets, sorted, inv,
+                                        stream),
+             "router launch");
+  } else {
+    st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
+                    partial, stream);
+    if (st != MOE_OK) return st;
+    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
+             "permute launch");
+  }
+  st = ffn_i8_impl(s, T, x, experts, counts, offsets, sorted, yperm, nullptr, b, L.f, stream);
+  if (st != MOE_OK) return st;
+  QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");
   return MOE_OK;
 }

@@ -87,6 +87,27 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, offset
+// mode).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
+// operations are outstanding, leaving the LDS and export counters alone.
+// The builtin form keeps the compiler's own wait bookkeeping exact.
+__host__ __device__ constexpr inline int waitcnt_vm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00;
+}
+
+// Address-space pointer types of the direct global->LDS loads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Workgroup barrier for LDS hand-offs only. __syncthreads() also orders

@@ -58,15 +58,6 @@ constexpr int SUB_BYTES = BM * 128;  // one wave's epilogue sub-tile (128 rows x
 constexpr int EX_BYTES = (NWAVES - 2 * ASTAGES) * SUB_BYTES;
 static_assert(A_STAGE_BYTES == 2 * SUB_BYTES && NWAVES > 2 * ASTAGES, "epilogue LDS layout");
 
-// Word 3 of a raw buffer resource on gfx950 (32-bit data format, offset
-// mode).
-constexpr int kRsrcWord3 = 0x00020000;
-
-// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
-// operations are outstanding, leaving the LDS and export counters alone.
-// The builtin form keeps the compiler's own wait bookkeeping exact.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-
 // bf16 activations -> fp16 in kperm chunk order (exact for |x| < 65504).
 __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x,
                                                        uint16_t* __restrict__ out,
@@ -113,9 +104,6 @@ __device__ __forceinline__ void gather_rows(const GroupedGemm& g, int row0, int 
     for (int i = 0; i < NL; ++i) src[i] /= div;
   }
 }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 // What one tile of the expert GEMM needs besides the shared setup: its
 // rows, this lane's activation sources and weight offsets. (At namespace

@@ -37,7 +37,6 @@ constexpr int STHREADS = 64 * SWAVES;
 constexpr int SBK = 128;               // K per stage
 constexpr int SWG_PER_CU = 2;          // resident workgroups per CU (at least)
 constexpr int SMAXG = 256;             // groups per launch
-constexpr int kRsrcWord3S = 0x00020000;
 
 int g_stream_cus = 0;
 
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(STHREADS, SWG_PER_CU) void expert_stream_kernel(Gro
   constexpr int NSC = 32 * NS > G ? 32 * NS / G : 1;
 
   const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, g.a_rows * K * 2, kRsrcWord3S);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, g.a_rows * K * 2, kRsrcWord3);
   // activation operand: lane (r16, lg) supplies row r16, its K block
   u32x4 av[NS][4];
   auto load_a_row = [&](int src) {
@@ -141,11 +140,11 @@ __global__ __launch_bounds__(STHREADS, SWG_PER_CU) void expert_stream_kernel(Gro
 
   const int n_groups = g.counts != nullptr ? g.E : 1;
   const __amdgpu_buffer_rsrc_t rW =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, 0, n_groups * N * (K / 2), kRsrcWord3S);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, 0, n_groups * N * (K / 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rS =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale, 0, n_groups * N * KG * 2, kRsrcWord3S);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale, 0, n_groups * N * KG * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3S);
+      (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3);
 
   // Fragment f of an item covers weight rows c0 + frow(f) + 0..15 of its
   // group. Gate/up: fragments 0 .. NF/2 - 1 are gate rows (h columns c0 ..

@@ -103,6 +103,35 @@ bool stream_supported(const GroupedGemm& g, bool gateup);
 bool gemm_streams(const GroupedGemm& g, bool gateup);
 hipError_t launch_stream(const GroupedGemm& g, bool gateup, hipStream_t s, const char* name);
 
+// ---- integer route: 8-bit activations x symmetric 4-bit weights --------
+// Per-row 8-bit quantization of bf16 (or fp16) rows [rows][cols], cols % 8
+// == 0: q = rint(v * (127 / a)), s = a / 127, a = max |v| of the row (rows
+// with a < 2^-100 give zeros). gemm_order stores each 8-element chunk as
+// elements 0,2,4,6,1,3,5,7 (the int8 GEMMs' operand order), else natural.
+hipError_t launch_quant_rows_i8(const uint16_t* src, bool src_f16, int rows, int cols,
+                                bool gemm_order, int8_t* q, float* scale, hipStream_t s);
+
+struct GemmI8 {
+  const int8_t* A;         // int8 activation rows [a_rows][K], int8 GEMM chunk order
+  const float* a_scale;    // [a_rows] row scales
+  const int32_t* gather;   // row r -> A row gather[r] / gather_div ; NULL: A row r
+  int gather_div;
+  const int32_t* counts;   // [E] rows per group
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int max_rows;            // upper bound of all rows (sizes the grid)
+  int a_rows;
+  const uint8_t* W;        // [E][N][K/2] symmetric 4-bit codes
+  const uint16_t* Wscale;  // fp16 [E][N][K/128]
+  int N, K;                // K % 128 == 0; the group size is 128
+  uint16_t* C;             // fp16 output rows, leading dimension ldc
+  int ldc;
+};
+// gate/up (N = 2I) with SwiGLU: C = h [rows][I] fp16, natural order
+hipError_t launch_gateup_i8(const GemmI8& g, hipStream_t s);
+// down (N = H): C = y [rows][H] fp16
+hipError_t launch_down_i8(const GemmI8& g, hipStream_t s);
+
 // ---- combine / norm ---------------------------------------------------
 hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const float* topk_w,
                           const uint16_t* y_shared, const float* shared_w,

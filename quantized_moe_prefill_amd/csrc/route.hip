@@ -29,9 +29,6 @@ namespace qmoe {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 constexpr int RBM = 128;   // tokens per GEMM tile
 constexpr int RBN = 256;   // output columns (split rows) per tile
 constexpr int RBK = 64;    // K per stage
@@ -371,7 +368,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
   const int n = blockIdx.x;
   const int rows = E + (sg != nullptr ? 1 : 0);
   const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, kRsrcWord3);
   float acc[kRouterGemvT];
 #pragma unroll
   for (int t = 0; t < kRouterGemvT; ++t) acc[t] = 0.f;

@@ -165,6 +165,52 @@ def moe_layer_forward(shape, x, w_router, router_bias, shared_gate, experts: Exp
     return out
 
 
+def moe_quantize_rows_i8(x):
+    """bf16 rows [R][C] -> (int8 codes [R][C], fp32 scales [R])."""
+    R, C = x.shape
+    dev = x.device
+    q = torch.empty((R, C), dtype=torch.int8, device=dev)
+    sc = torch.empty((max(R, 1),), dtype=torch.float32, device=dev)
+    N.check(N.lib().moe_quantize_rows_i8(R, C, _ptr(x, "x", _U16, dev), _ptr(q, "q"),
+                                         _ptr(sc, "scale"), _stream(dev)))
+    return q, sc[:R]
+
+
+def moe_expert_ffn_i8(shape, x, experts: Experts, counts, offsets, sorted_pairs, ws=None,
+                      want_h=False):
+    """Returns y_perm, or (y_perm, h_perm) with want_h (the fp16 h rows the
+    int8 h was quantized from)."""
+    T = x.shape[0]
+    dev = x.device
+    P = T * shape.top_k
+    y_perm = torch.empty((max(P, 1), shape.hidden), dtype=torch.float16, device=dev)
+    h = torch.empty((max(P, 1), shape.inter), dtype=torch.float16, device=dev) if want_h else None
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_EXPERT_FFN_I8)
+    N.check(N.lib().moe_expert_ffn_i8(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), experts.ref(),
+        _ptr(counts, "counts", (torch.int32,), dev), _ptr(offsets, "offsets", (torch.int32,), dev),
+        _ptr(sorted_pairs, "sorted_pairs", (torch.int32,), dev), _ptr(y_perm, "y_perm"),
+        _ptr(h, "h_perm"), _ptr(ws, "ws"), ws.numel(), _stream(dev)))
+    return (y_perm[:P], h[:P]) if want_h else y_perm[:P]
+
+
+def moe_layer_forward_i8(shape, x, w_router, router_bias, experts: Experts, residual=None,
+                         out=None, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_LAYER_I8)
+    N.check(N.lib().moe_layer_forward_i8(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev), experts.ref(),
+        _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _ptr(ws, "ws"),
+        ws.numel(), _stream(dev)))
+    return out
+
+
 def moe_rmsnorm(x, weight, eps: float, out=None):
     T, H = x.shape
     dev = x.device

@@ -23,7 +23,7 @@ def _lib():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_list():
@@ -161,3 +161,38 @@ def test_other_entry_points_validation():
     ms = ctypes.c_double(0)
     assert L.moe_profile_read(None, ctypes.byref(n), ctypes.byref(ms)) == N.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_profile_read(b"combine", ctypes.byref(n), ctypes.byref(ms)) == N.MOE_OK and n.value == 0
+
+
+def test_integer_route_validation_before_launch():
+    L = _lib()
+    s = _shape()
+    st, n8 = _ws(s, 8192, N.MOE_WS_LAYER_I8)
+    assert st == N.MOE_OK
+    P = 8192 * 8
+    # int8 x, fp16 h and int8 h, fp16 y_perm and the routing arrays
+    assert n8 >= 8192 * 2048 + P * 768 * 3 + P * 2048 * 2 + 4 * P * 4
+    st, f8 = _ws(s, 8192, N.MOE_WS_EXPERT_FFN_I8)
+    assert st == N.MOE_OK and f8 >= 8192 * 2048 + P * 768 * 3 and n8 >= f8
+    # the route is defined for symmetric experts, G = 128, no shared expert
+    for kw in (dict(quant=1), dict(group_size=64), dict(shared_inter=512)):
+        st, _ = _ws(_shape(**kw), 16, N.MOE_WS_LAYER_I8)
+        assert st == N.MOE_ERR_UNSUPPORTED, kw
+        assert b"integer route" in L.moe_last_error()
+    e = _experts()
+    assert L.moe_layer_forward_i8(ctypes.byref(s), 4, FAKE, FAKE, None, ctypes.byref(e), None, FAKE,
+                                  FAKE, 16, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_layer_forward_i8(ctypes.byref(s), 4, None, FAKE, None, ctypes.byref(e), None, FAKE,
+                                  FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    sa = _shape(quant=1)
+    ea = _experts(w13_min=FAKE, w2_min=FAKE)
+    assert L.moe_layer_forward_i8(ctypes.byref(sa), 4, FAKE, FAKE, None, ctypes.byref(ea), None, FAKE,
+                                  FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_expert_ffn_i8(ctypes.byref(s), 4, FAKE, ctypes.byref(e), FAKE, FAKE, FAKE, None, None,
+                               FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT  # no y_perm
+    assert L.moe_expert_ffn_i8(ctypes.byref(s), 4, FAKE, ctypes.byref(e), FAKE, FAKE, FAKE, FAKE,
+                               FAKE + 8, FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED  # misaligned h_perm
+    assert L.moe_expert_ffn_i8(ctypes.byref(s), 0, None, None, None, None, None, None, None, None, 0,
+                               None) == N.MOE_OK
+    assert L.moe_quantize_rows_i8(4, 12, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_rows_i8(4, 16, FAKE, None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_quantize_rows_i8(0, 16, None, None, None, None) == N.MOE_OK
