@@ -14,13 +14,25 @@
 // v_mfma_i32_16x16x64_i8; its fp16 scale / 16 is applied in fp32, and the
 // row scale of the activations once at the end.
 //
+// The group sums reach fp32 without a conversion instruction: the first
+// product of a group accumulates onto the integer bit pattern of
+// M = 1.5 * 2^23, and since |sum| < 128 * 127 * 128 < 2^22 the result's bits
+// read as the float M + sum exactly. The fp32 accumulator takes
+// scale * (M + sum) in one fma and drops the offsets scale * M every three
+// groups (one fma per result), which keeps its magnitude within a few group
+// offsets: the rounding error stays near 2^-24 * 3M * scale per group, about
+// 1e-4 of a typical group sum's contribution.
+//
 // Tile and schedule as in the fp16 grouped GEMM (ffn.hip): BM = 128 rows x
 // BN = 512 weight rows per persistent 512-thread workgroup, eight waves of
 // 64 weight rows each, the gathered int8 activation rows in a three-stage
 // LDS ring filled by direct global->LDS loads two stages ahead, each wave's
 // packed weights straight from global memory into registers one stage
 // ahead, the tile list walked XCD by XCD. A stage is one group (K = 128):
-// 16 KB of activations per stage instead of 32 KB for fp16.
+// 16 KB of activations per stage instead of 32 KB for fp16. The group
+// scales of a wave's 64 weight rows (up to 16 groups per row) come in once
+// per tile, by two direct 1 KB loads into a per-wave LDS tile, instead of
+// one 2-byte load per fragment and stage.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,6 +53,13 @@ constexpr int NFRAG = 4;
 constexpr int ALD = 2;            // direct activation loads per wave and stage (8 rows each)
 constexpr int A_STAGE_BYTES = BM * BK;
 constexpr int SUB_BYTES = BM * 64;  // one wave's epilogue sub-tile
+// Per-wave scale tile: two 1 KB slots. Gate/up: slot 0 = the 32 gate rows'
+// scales, slot 1 = the 32 up rows'; down: the 64 rows' scales over both.
+constexpr int SC_SLOT = 1024;
+constexpr int SC_WAVE = 2 * SC_SLOT;
+constexpr int SC_MAX_GROUPS = 16;  // groups per row that fit
+constexpr int kMagicBits = 0x4B400000;  // 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;
 static_assert(ALD * NWAVES * 8 == BM, "the direct loads of a stage cover its rows");
 
 // ---------------------------------------------------------------------------
@@ -106,6 +125,7 @@ struct TileI8 {
   bool cvalid;
   uint32_t a_off[ALD];
   uint32_t b_lane, s_lane;
+  uint32_t sc_src[2];  // byte offsets of the two scale slots' sources
 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
@@ -118,7 +138,7 @@ __device__ __forceinline__ void unpack8_i8(uint32_t w, uint32_t& even, uint32_t&
   odd = t & 0xF0F0F0F0u;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool SCL>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, int n_ntiles) {
   // LDS: the activation ring (128 rows x 128 bytes per stage; the 16-byte
   // chunk c of row r sits in slot c ^ (r & 7), so that the eight lanes of a
@@ -128,6 +148,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
   __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Ep[NWAVES * SUB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Sc[SCL ? NWAVES * SC_WAVE : 16];
   __shared__ float s_rs[2][BM];
   __shared__ int s_scan[258];
   __shared__ int s_wave[NWAVES];
@@ -220,6 +241,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
     const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
     ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
     ts.s_lane = (uint32_t)wrow0 * KG * 2;
+    if (SCL) {
+      const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));
+      const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
+      ts.sc_src[0] = s0;
+      ts.sc_src[1] = GATEUP ? __builtin_amdgcn_readfirstlane((r0 + N / 2) * KG * 2) : s0 + SC_SLOT;
+    }
     // the rows' activation scales (read by the epilogue, after at least one
     // workgroup barrier)
     if (tid < BM) {
@@ -243,23 +270,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
     for (int f = 0; f < NFRAG; ++f)
       cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+    if (!SCL) {
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f)
-      rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, frow(f) * KG * 2 + kt * 2, 0);
+      for (int f = 0; f < NFRAG; ++f)
+        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(rS, ts.s_lane, frow(f) * KG * 2 + kt * 2, 0);
+    }
+  };
+  // this wave's scale tile (past a block's end the loads read other rows'
+  // scales or zeros, never used)
+  uint8_t* const sc_wave = Sc + wave * (SCL ? SC_WAVE : 0);
+  auto load_sc = [&](const TileI8& ts) {
+    if (SCL) {
+      const uint32_t lo = (uint32_t)lane_o * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void_t*)sc_wave, 16, lo, ts.sc_src[0], 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void_t*)(sc_wave + SC_SLOT), 16, lo,
+                                               ts.sc_src[1], 0, 0);
+    }
+  };
+  // the scales of stage kt from the wave's scale tile
+  auto read_sc = [&](const uint8_t* __restrict__ scw, int kt, uint32_t* rs) {
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+      const int row = GATEUP ? 16 * (f & 1) + r16 : 16 * f + r16;
+      const int off = (GATEUP && f >= 2 ? SC_SLOT : 0) + (row * KG + kt) * 2;
+      rs[f] = *reinterpret_cast<const uint16_t*>(scw + off);
+    }
   };
 
   f32x4 acc[MSUB][NFRAG];
 
   // One stage: the weights unpacked once, then per 16-row sub-tile two
-  // int8 products per fragment (an exact group sum) and one fp32 fma per
-  // result with the group's scale.
+  // int8 products per fragment (an exact group sum, offset by M) and one
+  // fp32 fma per result with the group's scale; off[f] collects the scales
+  // whose offsets are still in the accumulators.
   auto compute_stage = [&](const uint8_t* __restrict__ as_base, const u32x4* cb,
-                           const uint32_t* rs) {
+                           const uint32_t* rs, float* off) {
     i32x4 b0[NFRAG], b1[NFRAG];
     float sc[NFRAG];
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
       sc[f] = f16_to_f32((uint16_t)rs[f]) * 0.0625f;
+      off[f] += sc[f];
       uint32_t e0, o0, e1, o1, e2, o2, e3, o3;
       unpack8_i8(cb[f][0], e0, o0);
       unpack8_i8(cb[f][1], e1, o1);
@@ -271,20 +322,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
     const int sw = r16 & 7;
     const uint8_t* ap0 = as_base + r16 * BK + (((2 * lg) ^ sw) * 16);
     const uint8_t* ap1 = as_base + r16 * BK + (((2 * lg + 1) ^ sw) * 16);
-    const i32x4 zero = {0, 0, 0, 0};
+    const i32x4 magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 #pragma unroll
     for (int mi = 0; mi < MSUB; ++mi) {
       const i32x4 a0 = __builtin_bit_cast(i32x4, ld16(ap0 + mi * 16 * BK));
       const i32x4 a1 = __builtin_bit_cast(i32x4, ld16(ap1 + mi * 16 * BK));
       i32x4 t[NFRAG];
 #pragma unroll
-      for (int f = 0; f < NFRAG; ++f) t[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[f], zero, 0, 0, 0);
+      for (int f = 0; f < NFRAG; ++f) t[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[f], magic, 0, 0, 0);
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) t[f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[f], t[f], 0, 0, 0);
 #pragma unroll
-      for (int f = 0; f < NFRAG; ++f)
+      for (int f = 0; f < NFRAG; ++f) {
+        // (the whole vector is reinterpreted: a bit cast of one element of
+        // an ext_vector_type value is compiled as a cast of element 0)
+        const f32x4 tf = __builtin_bit_cast(f32x4, t[f]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[mi][f][v] = fmaf(sc[f], (float)t[f][v], acc[mi][f][v]);
+        for (int v = 0; v < 4; ++v) acc[mi][f][v] = fmaf(sc[f], tf[v], acc[mi][f][v]);
+      }
     }
   };
 
@@ -358,8 +413,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
   };
 
   // ---- persistent loop; waits as in the fp16 kernel: within a stage the
-  // weight and scale loads are issued before the activation loads, so "at
-  // most ALD outstanding" at the end of stage s means stage s+1 has landed.
+  // weight (and scale) loads are issued before the activation loads, so "at
+  // most ALD outstanding" at the end of stage s means stage s+1 has landed;
+  // a tile's scale tile is loaded before its first weights.
   int tile = t_begin + wg_in_xcd;
   if (tile >= t_end) return;
   const int klast = nk - 1;
@@ -368,6 +424,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
   setup(tile, cur, par);
   u32x4 cb[NFRAG];
   uint32_t rs[NFRAG];
+  load_sc(cur);
   load_b(cur, 0, cb, rs);
   load_a(cur, 0, As0);
   load_a(cur, min(1, klast), As1);
@@ -375,17 +432,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
     refresh_lane();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
     lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
+    if (SCL) read_sc(sc_wave, 0, rs);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float off[NFRAG] = {0.f, 0.f, 0.f, 0.f};
+    auto recenter = [&]() {
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f) {
+#pragma unroll
+        for (int i = 0; i < MSUB; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][f][v] = fmaf(-kMagic, off[f], acc[i][f][v]);
+        off[f] = 0.f;
+      }
+    };
     auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2) {
       u32x4 cbn[NFRAG];
       uint32_t rsn[NFRAG];
       load_b(cur, min(kt + 1, klast), cbn, rsn);
       load_a(cur, min(kt + 2, klast), nxt2);
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(curs, cb, rs);
+      compute_stage(curs, cb, rs, off);
+      if (SCL) read_sc(sc_wave, min(kt + 1, klast), rsn);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -399,6 +469,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
       stage(kt, As0, As2);
       if (kt + 1 < nk) stage(kt + 1, As1, As0);
       if (kt + 2 < nk) stage(kt + 2, As2, As1);
+      recenter();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
@@ -408,6 +479,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
     refresh_lane();
     if (has_next) {
       setup(next, nts, par ^ 1);
+      load_sc(nts);
       load_b(nts, 0, cb, rs);
       load_a(nts, 0, As0);
     }
@@ -424,6 +496,7 @@ int g_i8_cus = 0;
 
 template <bool GATEUP>
 hipError_t launch_i8(const GemmI8& g, hipStream_t s, const char* name) {
+  const bool scl = g.K / BK <= SC_MAX_GROUPS;
   const int n_ntiles = GATEUP ? cdiv(g.N / 2, BN / 2) : cdiv(g.N, BN);
   const int m_bound = cdiv(g.max_rows, BM) + g.E;
   if (g.max_rows <= 0) return hipSuccess;
@@ -439,8 +512,12 @@ hipError_t launch_i8(const GemmI8& g, hipStream_t s, const char* name) {
   if (wgs > bound) wgs = bound;
   wgs = cdiv(wgs, NXCD) * NXCD;
   LaunchScope ls(name, s);
-  hipLaunchKernelGGL((expert_gemm_i8_kernel<GATEUP>), dim3(wgs), dim3(NTHREADS), 0, s, g,
-                     n_ntiles);
+  if (scl)
+    hipLaunchKernelGGL((expert_gemm_i8_kernel<GATEUP, true>), dim3(wgs), dim3(NTHREADS), 0, s, g,
+                       n_ntiles);
+  else
+    hipLaunchKernelGGL((expert_gemm_i8_kernel<GATEUP, false>), dim3(wgs), dim3(NTHREADS), 0, s, g,
+                       n_ntiles);
   return hipGetLastError();
 }
 
