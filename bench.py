@@ -48,9 +48,12 @@ KERNELS_I8 = ("router_split", "router_gemm", "router_select", "permute_rank", "p
 # FETCH_SIZE + WRITE_SIZE (each scaled by the copy-kernel calibration factor),
 # keyed by the hash of the expert-GEMM sources they were measured on: a
 # changed kernel reports null until it is measured again.
-GATEUP_TRAFFIC = {"bcad9b561b323f77": 662103896}   # {source sha256[:16]: bytes per launch}
+GATEUP_TRAFFIC = {"2218f8583a8366fc": 662240275}   # {source sha256[:16]: bytes per launch}
 GEMM_SOURCES = ("quantized_moe_prefill_amd/csrc/ffn.hip", "quantized_moe_prefill_amd/csrc/common.h",
                 "quantized_moe_prefill_amd/csrc/dequant.h")
+# the same for the integer route's gate/up launch
+GATEUP_I8_TRAFFIC = {"02f583f676117712": 525602122}
+I8_SOURCES = ("quantized_moe_prefill_amd/csrc/ffn_i8.hip", "quantized_moe_prefill_amd/csrc/common.h")
 CALIB_BYTES = 1 << 30
 # Weight-streaming regime: with this few rows the layer reads each active
 # expert's weights once, and those (tens of MB) would stay in the 256 MB
@@ -82,10 +85,10 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_source_hash() -> str:
+def gemm_source_hash(sources=GEMM_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -131,7 +134,8 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
             tot = (f * sf + w * sw) * 1024.0
         print(f"{k[:55]:55s} {nf.get(k, 0):4d} {f if f is not None else float('nan'):12.1f} "
               f"{w if w is not None else float('nan'):12.1f} {tot if tot else float('nan'):14.4g}")
-    print(f"gemm source hash {gemm_source_hash()}")
+    print(f"gemm source hash {gemm_source_hash()}, integer-route gemm source hash "
+          f"{gemm_source_hash(I8_SOURCES)}")
 
 
 def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False):
@@ -373,8 +377,9 @@ def main():
             "peak": peak,
             "unit": "TOP/s" if i8 else "TFLOP/s",
             "frac": round(achieved / peak, 4) if achieved else None,
-            "traffic": (GATEUP_TRAFFIC.get(gemm_source_hash())
-                        if (cfg.name, T, i8) == ("a3b_pp8192", 8192, False) else None),
+            "traffic": ((GATEUP_I8_TRAFFIC.get(gemm_source_hash(I8_SOURCES)) if i8
+                         else GATEUP_TRAFFIC.get(gemm_source_hash()))
+                        if (cfg.name, T) == ("a3b_pp8192", 8192) else None),
             "flops_per_launch": gu_flops,
         }
 
