@@ -116,6 +116,7 @@ struct GemmTile {
   uint32_t a_off[ALD];  // byte offsets of this lane's activation loads
   uint32_t b_lane, s_lane;
   uint32_t sc_src[2];  // scale tiles in LDS: byte offsets of the two 1 KB sources
+  uint32_t win_lane;   // scale windows: byte offset of this lane's row's groups
 };
 
 // Scales (and mins) of a tile in LDS: each wave's rows take two 1 KB slots,
@@ -127,7 +128,17 @@ struct GemmTile {
 constexpr int SC_SLOT = 1024;
 constexpr int SC_WAVE = 2 * SC_SLOT;
 
-template <bool GATEUP, bool ASYM, bool SCL, bool FOLD>
+// How a kernel variant reads the group scales (and mins):
+//  - SC_STAGE: one 2-byte load per fragment and K stage;
+//  - SC_TILE: the tile's scales through the per-wave LDS tile above;
+//  - SC_WINDOW (G = 32): a row's 8 groups of two consecutive K stages are 16
+//    contiguous bytes, so one direct 16-byte-per-lane load per wave (lane l
+//    = the wave's weight row l) fills a window of two stages for its 64
+//    rows: 1 KB of scales in slot 0, 1 KB of mins in slot 1, refilled every
+//    other stage, in place of eight 2-byte loads per stage.
+constexpr int SC_STAGE = 0, SC_TILE = 1, SC_WINDOW = 2;
+
+template <bool GATEUP, bool ASYM, int SCM, bool FOLD>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
@@ -144,7 +155,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Sc[SCL ? NWAVES * SC_WAVE : 16];
+  constexpr bool SCL = SCM == SC_TILE;
+  constexpr bool WIN = SCM == SC_WINDOW;
+  __shared__ __attribute__((aligned(16))) uint8_t Sc[SCM != SC_STAGE ? NWAVES * SC_WAVE : 16];
   __shared__ int s_scan[258];
   __shared__ int s_wave[NWAVES];
 
@@ -269,6 +282,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
     ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
     ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
+    if (WIN) {
+      // lane l loads the window of the wave's weight row l: gate/up lanes
+      // 0-31 the gate rows c0 + l, 32-63 the up rows of the same columns
+      const int l = lane_o;
+      const int wr = GATEUP ? (l < 32 ? l : N / 2 + l - 32) : l;
+      ts.win_lane = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0) + wr) * KG * 2;
+    }
     if (SCL) {
       const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));  // e = 0 for the extra group
       const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
@@ -290,7 +310,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     for (int f = 0; f < NFRAG; ++f)
       cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             ts.shared ? rW2 : rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
-    if (!SCL) {
+    if (SCM == SC_STAGE) {
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
         const int so = frow(f) * KG * 2 + kt * s_step;
@@ -304,7 +324,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // this wave's scale tile: two direct 1 KB loads (past a block's end they
   // read other rows' scales or zeros, never used)
   uint8_t* const sc_wave = Sc + wave * SC_WAVE;
+  // the scale (and min) window w (K stages 2w, 2w+1) of the wave's rows
+  auto load_win = [&](const GemmTile& ts, int w) {
+    if (WIN) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.shared ? rS2 : rS, (lds_void_t*)sc_wave, 16,
+                                               ts.win_lane, w * 16, 0, 0);
+      if (ASYM)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.shared ? rM2 : rM,
+                                                 (lds_void_t*)(sc_wave + SC_SLOT), 16,
+                                                 ts.win_lane, w * 16, 0, 0);
+    }
+  };
+  // the scales (and mins) of stage kt from the current window: fragment f's
+  // rows are the wave's rows 16 f + r16, and lane group lg's K block is group
+  // 4 (kt % 2) + lg of the window
+  auto read_win = [&](int kt, uint32_t* rs, uint32_t* rm) {
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f) {
+      const int off = (16 * f + r16) * 16 + (4 * (kt & 1) + lg) * 2;
+      rs[f] = *reinterpret_cast<const uint16_t*>(sc_wave + off);
+      rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(sc_wave + SC_SLOT + off) : 0u;
+    }
+  };
   auto load_sc = [&](const GemmTile& ts) {
+    if (WIN) load_win(ts, 0);
     if (SCL) {
       const uint32_t lo = (uint32_t)lane_o * 16u;
       const __amdgpu_buffer_rsrc_t s_r = ts.shared ? rS2 : rS;
@@ -475,15 +518,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
     lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
     if (SCL) read_sc(sc_wave, 0, rs, rm);
+    if (WIN) read_win(0, rs, rm);
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // stage kt reads ring slot kt % 3 and loads stage kt + 2 into slot (kt + 2) % 3
-    auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2) {
+    // `odd`: kt is odd (a constant at every call), the stage that refills the
+    // scale window with that of stages kt + 1, kt + 2
+    auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2,
+                     bool odd) {
       u32x4 cbn[NFRAG];
       uint32_t rsn[NFRAG], rmn[NFRAG];
       load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
+      if (WIN && odd) load_win(cur, (kt + 1) >> 1);
       load_a(cur, min(kt + 2, klast), nxt2);
       // issue the loads here, a whole stage before they are needed: left to
       // itself the scheduler sinks them to the end of the stage (to shorten
@@ -492,6 +540,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       compute_stage(curs, cb, rs, rm);
       if (SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
+      // (after the wait: a window refilled in this stage has landed)
+      if (WIN) read_win(kt + 1, rsn, rmn);
       lds_barrier();
       // the hand-over of the next stage's registers stays here: moved up into
       // the stage it would wait for loads that were just issued
@@ -503,10 +553,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         rm[f] = rmn[f];
       }
     };
-    for (int kt = 0; kt < nk; kt += 3) {
-      stage(kt, As0, As2);
-      if (kt + 1 < nk) stage(kt + 1, As1, As0);
-      if (kt + 2 < nk) stage(kt + 2, As2, As1);
+    if (WIN) {
+      // unrolled by six, so that the window refills sit at fixed stages
+      for (int kt = 0; kt < nk; kt += 6) {
+        stage(kt, As0, As2, false);
+        if (kt + 1 < nk) stage(kt + 1, As1, As0, true);
+        if (kt + 2 < nk) stage(kt + 2, As2, As1, false);
+        if (kt + 3 < nk) stage(kt + 3, As0, As2, true);
+        if (kt + 4 < nk) stage(kt + 4, As1, As0, false);
+        if (kt + 5 < nk) stage(kt + 5, As2, As1, true);
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += 3) {
+        stage(kt, As0, As2, false);
+        if (kt + 1 < nk) stage(kt + 1, As1, As0, false);
+        if (kt + 2 < nk) stage(kt + 2, As2, As1, false);
+      }
     }
     // the repeated loads of the last stages land before the ring is reused
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -561,20 +623,34 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   const bool asym = g.Wmin != nullptr;
   const bool fold = g.counts != nullptr && g.rows2 > 0;
   const bool scl = !fold && (GATEUP ? (!asym && KG <= 16) : (asym ? KG <= 8 : KG <= 16));
-  auto go = [&](auto a, auto l, auto f) {
-    constexpr bool A = decltype(a)::value, L = decltype(l)::value, F = decltype(f)::value;
-    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, L, F>), grid, block, 0, s, g, n_ntiles);
+  // scale windows: asymmetric experts with G = 32 whose scales do not fit
+  // the tile (the shared-expert variant included)
+  const bool win = asym && !scl && g.G == 32;
+  auto go = [&](auto a, auto m, auto f) {
+    constexpr bool A = decltype(a)::value, F = decltype(f)::value;
+    constexpr int M = decltype(m)::value;
+    hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, M, F>), grid, block, 0, s, g, n_ntiles);
   };
   const std::true_type yes{};
   const std::false_type no{};
+  const std::integral_constant<int, SC_STAGE> stage_sc{};
+  const std::integral_constant<int, SC_TILE> tile_sc{};
+  const std::integral_constant<int, SC_WINDOW> win_sc{};
   if (asym) {
-    if (fold) go(yes, no, yes);
-    else if (scl) go(yes, yes, no);
-    else go(yes, no, no);
+    if (fold) {
+      if (win) go(yes, win_sc, yes);
+      else go(yes, stage_sc, yes);
+    } else if (scl) {
+      go(yes, tile_sc, no);
+    } else if (win) {
+      go(yes, win_sc, no);
+    } else {
+      go(yes, stage_sc, no);
+    }
   } else {
-    if (fold) go(no, no, yes);
-    else if (scl) go(no, yes, no);
-    else go(no, no, no);
+    if (fold) go(no, stage_sc, yes);
+    else if (scl) go(no, tile_sc, no);
+    else go(no, stage_sc, no);
   }
   return hipGetLastError();
 }
