@@ -65,6 +65,9 @@ __all__ = [
     "expert_ffn_i8",
     "moe_layer_i8",
     "moe_layer_rows_i8",
+    "unpack_codes",
+    "dequant_bits",
+    "moe_layer_mixed",
 ]
 
 
@@ -561,3 +564,98 @@ def moe_layer_rows_i8(x_bits, rows, li, k: int, G: int, logits32_rows=None, cach
             hin = h16[i, j] if h16_rows is None else np.asarray(h16_rows, np.float64)[i, j]
             out[i] += tw[i, j] * _i8_down(hin[None, :], W2)[2][0]
     return dict(ids=ids, weights=tw, logits=L, out=out, h16=h16)
+
+
+# ---------------------------------------------------------------------------
+# lower-bit expert tiers (3 and 2 bits) beside 4-bit experts
+# ---------------------------------------------------------------------------
+#
+# The pages ship expert files where most routed experts are stored below
+# 4 bits and the rest stay at 4 bits (hipfire 0.4.3 benchmarks page, "New
+# Flash-Next tiers": 3-bit experts on part of the routed experts; 2-bit
+# experts, there with an E8P codebook, on others). They define neither
+# format. The reading used here: plain symmetric scalar codes of b bits per
+# weight, w = (q - 2^(b-1)) * scale with one fp16 scale per group of G along
+# K, in this library's row layouts (stated in unpack_codes). E8P's lattice
+# codebook is not defined on the pages and is not reproduced.
+
+def unpack_codes(packed, bits: int) -> np.ndarray:
+    """Packed rows [R][K*bits/8] -> codes [R][K] (0 .. 2^bits - 1).
+
+    4 bits: byte j holds element 2j in bits 0-3 and 2j+1 in bits 4-7.
+    2 bits: little-endian 32-bit word m holds elements 16m .. 16m+15; its
+            bytes 0, 1, 2, 3 hold the word's elements 0-3, 8-11, 4-7, 12-15,
+            element i of a byte's four in bits 2i and 2i+1.
+    3 bits: 12 bytes per 32-element block: 8 bytes of the elements' low two
+            bits in the 2-bit layout, then a 32-bit word whose bit 4c+i is the
+            high bit of element 8c+i and bit 16+4c+i that of element 8c+i+4
+            (c, i in 0..3).
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    if bits == 4:
+        return unpack_nibbles(p)
+    R = p.shape[0]
+    if bits == 2:
+        words = p.reshape(R, -1, 4).astype(np.int64)
+        out = np.empty((R, words.shape[1], 16), dtype=np.int64)
+        for b, first in enumerate((0, 8, 4, 12)):     # byte b of a word -> its four elements
+            for i in range(4):
+                out[:, :, first + i] = (words[:, :, b] >> (2 * i)) & 3
+        return out.reshape(R, -1)
+    if bits == 3:
+        blocks = p.reshape(R, -1, 12)
+        low = unpack_codes(blocks[:, :, :8].reshape(R, -1), 2).reshape(R, -1, 32)
+        hw = blocks[:, :, 8:12].astype(np.int64)
+        h = hw[:, :, 0] | (hw[:, :, 1] << 8) | (hw[:, :, 2] << 16) | (hw[:, :, 3] << 24)
+        high = np.zeros_like(low)
+        for c in range(4):
+            for i in range(4):
+                high[:, :, 8 * c + i] = (h >> (4 * c + i)) & 1
+                high[:, :, 8 * c + i + 4] = (h >> (16 + 4 * c + i)) & 1
+        return (low + 4 * high).reshape(R, -1)
+    raise ValueError(f"unsupported width {bits}")
+
+
+def dequant_bits(packed, scale, G: int, bits: int) -> np.ndarray:
+    """Symmetric b-bit weights [R][K]: w = (q - 2^(b-1)) * scale[r, k // G]."""
+    q = unpack_codes(packed, bits).astype(np.float64) - float(1 << (bits - 1))
+    s = f16_to_f64(scale)
+    return q * np.repeat(s, G, axis=1)
+
+
+def _mixed_mats(ml, e, G):
+    b = int(ml.bits[e])
+    j = int(ml.slot[e])
+    w13, s13, w2, s2 = (np.asarray(t.detach().cpu().numpy() if hasattr(t, "detach") else t)
+                        for t in ml.tiers[b])
+    if s13.dtype == np.float16:
+        s13, s2 = s13.view(np.uint16), s2.view(np.uint16)
+    return dequant_bits(w13[j], s13[j], G, b), dequant_bits(w2[j], s2[j], G, b)
+
+
+def moe_layer_mixed(x_bits, ml, k: int, G: int, logits32=None):
+    """One layer whose expert e is stored with ml.bits[e] bits per weight:
+    routing as moe_layer (fp32 logits, optional teacher forcing), each
+    expert's SwiGLU FFN on its dequantized weights, combine. Returns the
+    routing arrays, y_perm and out (float64)."""
+    w_router = ml.w_router.detach().cpu().numpy() if hasattr(ml.w_router, "detach") else ml.w_router
+    bias = ml.router_bias
+    if bias is not None and hasattr(bias, "detach"):
+        bias = bias.detach().cpu().numpy()
+    xf = bf16_to_f64(x_bits)
+    E = w_router.shape[0]
+    L = router_logits(xf, w_router, bias)
+    L32 = L.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
+    ids, tw = select_topk(L32, k)
+    counts, offsets, sorted_pairs, inv = permute(ids, E)
+    P = int(offsets[-1])
+    y = np.zeros((P, xf.shape[1]))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        W13, W2 = _mixed_mats(ml, e, G)
+        _, y[a:b] = swiglu_expert(xf[np.asarray(sorted_pairs[a:b]) // k], W13, W2)
+    out = combine(y, inv, tw)
+    return dict(logits=L, logits32=L32, ids=ids, weights=tw, counts=counts, offsets=offsets,
+                sorted_pairs=sorted_pairs, inv=inv, y_perm=y, out=out)

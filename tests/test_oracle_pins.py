@@ -605,3 +605,118 @@ def test_i8_rows_subset_matches_full_layer():
     sub = oracle.moe_layer_rows_i8(xb, rows, li, cfg.k, cfg.G)
     assert np.array_equal(sub["ids"], full["ids"][rows])
     assert np.allclose(sub["out"], full["out"][rows], rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# lower-bit expert tiers
+# ---------------------------------------------------------------------------
+
+def test_unpack_2bit_hand_word():
+    # byte 0 = 0xE4 -> elements 0..3 = 0,1,2,3; byte 1 = 0x1B -> elements
+    # 8..11 = 3,2,1,0; byte 2 = 0xFF -> elements 4..7 = 3; byte 3 = 0 -> 12..15 = 0
+    p = np.array([[0xE4, 0x1B, 0xFF, 0x00]], dtype=np.uint8)
+    assert oracle.unpack_codes(p, 2).tolist() == [[0, 1, 2, 3, 3, 3, 3, 3, 3, 2, 1, 0, 0, 0, 0, 0]]
+
+
+def test_unpack_3bit_hand_block():
+    low = [0xE4, 0x00, 0x00, 0x00, 0x00, 0x00, 0x00, 0x03]  # elements 0..3 = 0,1,2,3; element 28 = 3
+    # high-bit word 0x80010001: bit 0 -> element 0, bit 16 -> element 4,
+    # bit 31 = 16 + 4*3 + 3 -> element 8*3 + 3 + 4 = 31
+    hw = [0x01, 0x00, 0x01, 0x80]
+    q = oracle.unpack_codes(np.array([low + hw], dtype=np.uint8), 3)[0].tolist()
+    expect = [0] * 32
+    expect[0:4] = [4, 1, 2, 3]
+    expect[4] = 4
+    expect[28] = 3
+    expect[31] = 4
+    assert q == expect
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_unpack_round_trip(bits):
+    from synth.mixed import pack_codes
+    g = torch.Generator().manual_seed(bits)
+    q = torch.randint(0, 1 << bits, (7, 128), generator=g)
+    assert np.array_equal(oracle.unpack_codes(pack_codes(q, bits).numpy(), bits), q.numpy())
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_dequant_bits_closed_form_and_quantizer_error(bits):
+    from synth.mixed import pack_codes, quantize_sym_bits
+    half = 1 << (bits - 1)
+    q = torch.arange(1 << bits).repeat(32 // (1 << bits) * 4).reshape(1, -1)[:, :32]
+    p = pack_codes(q, bits).numpy()
+    w = oracle.dequant_bits(p, _const_f16((1, 1), 0.5), 32, bits)
+    assert w[0].tolist() == [(v - half) * 0.5 for v in q[0].tolist()]
+    g = torch.Generator().manual_seed(9)
+    wt = torch.randn(16, 256, generator=g) * 0.02
+    p, s = quantize_sym_bits(wt, 64, bits)
+    back = oracle.dequant_bits(p.numpy(), s.numpy().view(np.uint16), 64, bits)
+    s64 = np.repeat(s.numpy().astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(back - wt.numpy()) <= s64 / 2 + 2.0 ** -11 * np.abs(wt.numpy()).max())
+
+
+def test_mixed_all_4bit_equals_4bit_layer():
+    from dataclasses import replace
+    from synth.mixed import make_mixed_layer
+    cfg = replace(CONFIGS["tiny"], T=24, G=64)
+    ml = make_mixed_layer(cfg, [4] * cfg.E)
+    li = make_layer(cfg)
+    assert torch.equal(ml.tiers[4][0], li.w13) and torch.equal(ml.tiers[4][2], li.w2)
+    xb = _xbits(make_tokens(cfg))
+    a = oracle.moe_layer_mixed(xb, ml, cfg.k, cfg.G)
+    b = oracle.moe_layer(xb, li, cfg.k, cfg.G, "sym")
+    assert np.allclose(a["out"], b["out"], rtol=1e-12, atol=1e-15)
+
+
+def test_mixed_layer_matches_dense_bruteforce():
+    from dataclasses import replace
+    from synth.mixed import make_mixed_layer
+    cfg = replace(CONFIGS["tiny"], T=20, H=128, E=6, k=2, I=64, G=32)
+    bits = [4, 3, 2, 3, 2, 4]
+    ml = make_mixed_layer(cfg, bits)
+    xb = _xbits(make_tokens(cfg))
+    r = oracle.moe_layer_mixed(xb, ml, cfg.k, cfg.G)
+    xf = oracle.bf16_to_f64(xb)
+    # every expert on every token from its own bytes, unpacked by hand
+    # (shifts and masks written out here, not the oracle's unpacker), then
+    # masked by the routing weights
+    def codes(packed, b):
+        p = packed.numpy().astype(np.int64)
+        R = p.shape[0]
+        if b == 4:
+            out = np.stack([p & 15, p >> 4], axis=-1).reshape(R, -1)
+        elif b == 2:
+            w = p.reshape(R, -1, 4)
+            order = np.concatenate([(w[..., 0:1] >> (2 * i)) & 3 for i in range(4)] +
+                                   [(w[..., 2:3] >> (2 * i)) & 3 for i in range(4)] +
+                                   [(w[..., 1:2] >> (2 * i)) & 3 for i in range(4)] +
+                                   [(w[..., 3:4] >> (2 * i)) & 3 for i in range(4)], axis=-1)
+            out = order.reshape(R, -1)
+        else:
+            blk = p.reshape(R, -1, 12)
+            lo = codes(torch.from_numpy(blk[..., :8].reshape(R, -1).astype(np.uint8)), 2).reshape(R, -1, 32)
+            h = sum(blk[..., 8 + j] << (8 * j) for j in range(4))
+            hi = np.zeros_like(lo)
+            for e32 in range(32):
+                c, i = divmod(e32, 8)
+                bit = 4 * c + i if i < 4 else 16 + 4 * c + (i - 4)
+                hi[..., e32] = (h >> bit) & 1
+            out = (lo | (hi << 2)).reshape(R, -1)
+        return out
+    dense = np.zeros((cfg.T, cfg.E, cfg.H))
+    for e in range(cfg.E):
+        b, j = bits[e], ml.slot[e]
+        w13, s13, w2, s2 = ml.tiers[b]
+        def deq(pk, sc):
+            q = codes(pk[j], b).astype(np.float64) - (1 << (b - 1))
+            return q * np.repeat(sc[j].numpy().astype(np.float64), cfg.G, axis=1)
+        W13, W2 = deq(w13, s13), deq(w2, s2)
+        g = xf @ W13[:cfg.I].T
+        u = xf @ W13[cfg.I:].T
+        dense[:, e] = (g / (1 + np.exp(-g)) * u) @ W2.T
+    wfull = np.zeros((cfg.T, cfg.E))
+    for t in range(cfg.T):
+        wfull[t, r["ids"][t]] = r["weights"][t]
+    ref = np.einsum("te,teh->th", wfull, dense)
+    assert np.allclose(r["out"], ref, rtol=1e-9, atol=1e-12)
