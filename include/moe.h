@@ -243,6 +243,57 @@ moe_status_t moe_layer_forward_i8(const moe_shape_t *shape, int64_t T, const uin
                                   uint16_t *out, void *ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* ---- mixed-width experts: lower-bit tiers beside 4-bit experts ------------
+ * The pages ship expert files where most routed experts are stored below
+ * 4 bits and the rest stay at 4 bits (hipfire 0.4.3 benchmarks page, "New
+ * Flash-Next tiers": 3-bit experts, and 2-bit experts, there with an E8P
+ * codebook). They define neither format; this library's lower-bit codes are
+ * plain symmetric scalar codes, w = (q - 2^(bits-1)) * scale, one fp16 scale
+ * per group of G along K, with these row layouts (K * bits / 8 bytes a row):
+ *   bits 4: byte j = element 2j (bits 0-3) | element 2j+1 (bits 4-7);
+ *   bits 2: little-endian 32-bit word m holds elements 16m .. 16m+15, its
+ *           bytes 0, 1, 2, 3 the word's elements 0-3, 8-11, 4-7, 12-15,
+ *           element i of a byte's four in bits 2i, 2i+1;
+ *   bits 3: 12 bytes per 32-element block: the low two bits of its elements
+ *           in the 2-bit layout (8 bytes), then a 32-bit word whose bit 4c+i
+ *           is the third bit of element 8c+i and bit 16+4c+i that of element
+ *           8c+i+4 (c, i in 0..3).
+ * (E8P's lattice codebook is not implemented.) Each width's experts are
+ * stored in their own tensors; expert e of the layer is expert
+ * expert_slot[e] of the tier whose bits equal expert_bits[e]. */
+typedef struct {
+  int32_t bits;                /* 4, 3 or 2 */
+  int32_t num_experts;         /* E_b: experts stored at this width */
+  const uint8_t  *w13;         /* [E_b][2I][H * bits / 8] */
+  const uint16_t *w13_scale;   /* fp16 [E_b][2I][H/G] */
+  const uint8_t  *w2;          /* [E_b][H][I * bits / 8] */
+  const uint16_t *w2_scale;    /* fp16 [E_b][H][I/G] */
+} moe_tier_t;
+
+/* moe_expert_ffn over mixed-width experts (same numerics: fp16 weights
+ * dequantized in registers, fp16 matrix cores, fp32 accumulation).
+ *   tiers        host array of n_tiers (1..3) descriptors of distinct widths
+ *   expert_bits  [E] int32 device array: each expert's width (one of the tiers')
+ *   expert_slot  [E] int32 device array: its index within that tier's tensors
+ *                (a slot outside [0, E_b) reads zeros, no fault)
+ * Needs quant == MOE_Q4_SYM and shared_inter == 0; ws as moe_expert_ffn
+ * (MOE_WS_EXPERT_FFN). One launch per tier and GEMM. */
+moe_status_t moe_expert_ffn_mixed(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                                  const moe_tier_t *tiers, int32_t n_tiers,
+                                  const int32_t *expert_bits, const int32_t *expert_slot,
+                                  const int32_t *counts, const int32_t *offsets,
+                                  const int32_t *sorted_pairs, uint16_t *y_perm, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward over mixed-width experts: routing, grouping and combine
+ * as moe_layer_forward; ws as moe_layer_forward (MOE_WS_LAYER). */
+moe_status_t moe_layer_forward_mixed(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                                     const float *w_router, const float *router_bias,
+                                     const moe_tier_t *tiers, int32_t n_tiers,
+                                     const int32_t *expert_bits, const int32_t *expert_slot,
+                                     const uint16_t *residual, uint16_t *out, void *ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* RMSNorm over rows of [T][H] bf16:
  *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )
  * computed in fp32; weight [H] fp32. out must not alias x. */

@@ -40,6 +40,8 @@ EXPORTED = [
     "moe_quantize_rows_i8",
     "moe_expert_ffn_i8",
     "moe_layer_forward_i8",
+    "moe_expert_ffn_mixed",
+    "moe_layer_forward_mixed",
     "moe_rmsnorm",
     "moe_profile_enable",
     "moe_profile_reset",
@@ -64,6 +66,12 @@ class MoeExperts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w13", "w13_scale", "w13_min", "w2", "w2_scale", "w2_min",
         "s13", "s13_scale", "s13_min", "s2", "s2_scale", "s2_min")]
+
+
+class MoeTier(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -113,6 +121,12 @@ def lib():
     L.moe_expert_ffn_i8.argtypes = [sp, i64, P, ep, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.moe_layer_forward_i8.restype = st
     L.moe_layer_forward_i8.argtypes = [sp, i64, P, P, P, ep, P, P, P, ctypes.c_size_t, P]
+    tp = ctypes.POINTER(MoeTier)
+    L.moe_expert_ffn_mixed.restype = st
+    L.moe_expert_ffn_mixed.argtypes = [sp, i64, P, tp, i32, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_layer_forward_mixed.restype = st
+    L.moe_layer_forward_mixed.argtypes = [sp, i64, P, P, P, tp, i32, P, P, P, P, P,
+                                          ctypes.c_size_t, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

@@ -429,6 +429,79 @@ static moe_status_t ffn_i8_impl(const Shape& s, int64_t T, const uint16_t* x,
   return MOE_OK;
 }
 
+// ---- mixed-width experts ----
+static moe_status_t check_tiers(const Shape& s, const moe_tier_t* tiers, int32_t n) {
+  if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "mixed-width experts need MOE_Q4_SYM");
+  if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "mixed-width layers have no shared expert");
+  if (tiers == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "tiers is NULL");
+  if (n < 1 || n > 3) return fail(MOE_ERR_INVALID_ARGUMENT, "n_tiers must be 1..3 (got %d)", n);
+  unsigned seen = 0;
+  for (int i = 0; i < n; ++i) {
+    const moe_tier_t& t = tiers[i];
+    if (t.bits != 4 && t.bits != 3 && t.bits != 2)
+      return fail(MOE_ERR_UNSUPPORTED, "tier bits must be 4, 3 or 2 (got %d)", t.bits);
+    if (seen & (1u << t.bits)) return fail(MOE_ERR_INVALID_ARGUMENT, "two tiers of %d bits", t.bits);
+    seen |= 1u << t.bits;
+    if (t.num_experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "tier num_experts must be >= 1");
+    QMOE_REQUIRE(t.w13, "tier w13");
+    QMOE_REQUIRE(t.w13_scale, "tier w13_scale");
+    QMOE_REQUIRE(t.w2, "tier w2");
+    QMOE_REQUIRE(t.w2_scale, "tier w2_scale");
+    if ((int64_t)t.num_experts * 2 * s.I * s.H / 8 * t.bits >= (int64_t(1) << 31))
+      return fail(MOE_ERR_UNSUPPORTED, "a tier's packed weights must be below 2^31 bytes");
+  }
+  return MOE_OK;
+}
+
+static moe_status_t ffn_mixed_impl(const Shape& s, int64_t T, const uint16_t* x,
+                                   const moe_tier_t* tiers, int32_t n_tiers,
+                                   const int32_t* ebits, const int32_t* eslot,
+                                   const int32_t* counts, const int32_t* offsets,
+                                   const int32_t* sorted, uint16_t* yperm, uint16_t* x16,
+                                   uint16_t* h, hipStream_t st) {
+  const int P = (int)(T * s.k);
+  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+  GroupedGemm g{};
+  g.A = x16;
+  g.gather = sorted;
+  g.gather_div = s.k;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.E = s.E;
+  g.max_rows = P;
+  g.a_rows = (int)T;
+  g.N = 2 * s.I;
+  g.K = s.H;
+  g.G = s.G;
+  g.C = h;
+  g.ldc = s.I;
+  g.tier = ebits;
+  g.slot = eslot;
+  for (int i = 0; i < n_tiers; ++i) {
+    g.W = tiers[i].w13;
+    g.Wscale = tiers[i].w13_scale;
+    g.w_experts = tiers[i].num_experts;
+    g.bits = tiers[i].bits;
+    QMOE_HIP(launch_gateup(g, st), "gateup launch");
+  }
+  GroupedGemm d = g;
+  d.A = h;
+  d.a_rows = P;
+  d.gather = nullptr;
+  d.N = s.H;
+  d.K = s.I;
+  d.C = yperm;
+  d.ldc = s.H;
+  for (int i = 0; i < n_tiers; ++i) {
+    d.W = tiers[i].w2;
+    d.Wscale = tiers[i].w2_scale;
+    d.w_experts = tiers[i].num_experts;
+    d.bits = tiers[i].bits;
+    QMOE_HIP(launch_down(d, st), "down launch");
+  }
+  return MOE_OK;
+}
+
 }  // namespace qmoe
 
 using namespace qmoe;
@@ -720,6 +793,89 @@ moe_status_t moe_layer_forward_i8(const moe_shape_t* shape, int64_t T, const uin
              "permute launch");
   }
   st = ffn_i8_impl(s, T, x, experts, counts, offsets, sorted, yperm, nullptr, b, L.f, stream);
+  if (st != MOE_OK) return st;
+  QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_mixed(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                  const moe_tier_t* tiers, int32_t n_tiers,
+                                  const int32_t* expert_bits, const int32_t* expert_slot,
+                                  const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* sorted_pairs, uint16_t* y_perm, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  st = check_tiers(s, tiers, n_tiers);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(expert_bits, "expert_bits");
+  QMOE_REQUIRE(expert_slot, "expert_slot");
+  QMOE_REQUIRE(counts, "counts");
+  QMOE_REQUIRE(offsets, "offsets");
+  QMOE_REQUIRE(sorted_pairs, "sorted_pairs");
+  QMOE_REQUIRE(y_perm, "y_perm");
+  st = check_ws(ws, ws_bytes, ffn_ws(s, T));
+  if (st != MOE_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2));
+  return ffn_mixed_impl(s, T, x, tiers, n_tiers, expert_bits, expert_slot, counts, offsets,
+                        sorted_pairs, y_perm, x16, h, stream);
+}
+
+moe_status_t moe_layer_forward_mixed(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                     const float* w_router, const float* router_bias,
+                                     const moe_tier_t* tiers, int32_t n_tiers,
+                                     const int32_t* expert_bits, const int32_t* expert_slot,
+                                     const uint16_t* residual, uint16_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  st = check_tiers(s, tiers, n_tiers);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(out, "out");
+  QMOE_REQUIRE(expert_bits, "expert_bits");
+  QMOE_REQUIRE(expert_slot, "expert_slot");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(residual, "residual");
+  const Layout L = layer_layout(s, T);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  auto* split = reinterpret_cast<uint16_t*>(b + L.split);
+  auto* partial = reinterpret_cast<float*>(b + L.partial);
+  auto* hist = reinterpret_cast<int32_t*>(b + L.hist);
+  auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
+  auto* tw = reinterpret_cast<float*>(b + L.tw);
+  auto* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  auto* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  auto* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  auto* x16 = reinterpret_cast<uint16_t*>(b + L.x16);
+  auto* h = reinterpret_cast<uint16_t*>(b + L.h);
+  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
+  if (router_uses_gemv((int)T)) {
+    QMOE_HIP(launch_route_permute_small(x, w_router, nullptr, partial, router_bias, (int)T, s.H,
+                                        s.E, s.k, ids, tw, nullptr, counts, offsets, sorted, inv,
+                                        stream),
+             "router launch");
+  } else {
+    st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
+                    partial, stream);
+    if (st != MOE_OK) return st;
+    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
+             "permute launch");
+  }
+  st = ffn_mixed_impl(s, T, x, tiers, n_tiers, expert_bits, expert_slot, counts, offsets, sorted,
+                      yperm, x16, h, stream);
   if (st != MOE_OK) return st;
   QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");

@@ -138,7 +138,11 @@ constexpr int SC_WAVE = 2 * SC_SLOT;
 //    other stage, in place of eight 2-byte loads per stage.
 constexpr int SC_STAGE = 0, SC_TILE = 1, SC_WINDOW = 2;
 
-template <bool GATEUP, bool ASYM, int SCM, bool FOLD>
+// BITS: the weights' width (4; or 3 or 2, symmetric, see dequant.h). A
+// lane's 32-element K block of a row is 4 * BITS bytes: one 16-, 12- or
+// 8-byte load per fragment and stage. MIX: one width of a mixed-width
+// layer (the expert filter and slot map of GroupedGemm are read).
+template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = false>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
@@ -171,7 +175,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const bool has2 = FOLD && g.counts != nullptr && g.rows2 > 0;
   const int ngrp = g.E + (has2 ? 1 : 0);
   if (g.counts != nullptr) {
-    const int c = tid < g.E ? g.counts[tid] : (has2 && tid == g.E ? g.rows2 : 0);
+    // (a launch for one width of a mixed layer takes only that width's experts)
+    const int c = tid < g.E ? ((!MIX || g.tier[tid] == BITS) ? g.counts[tid] : 0)
+                            : (has2 && tid == g.E ? g.rows2 : 0);
     int incl = (c + BM - 1) / BM;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -199,11 +205,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // buffer resources: 32-bit offsets instead of 64-bit addresses (the host
   // guarantees every byte size below fits in 31 bits); a read past the end
   // of a buffer returns zero
-  const int n_groups = g.counts != nullptr ? g.E : 1;
+  const int n_groups = g.counts != nullptr ? (MIX ? g.w_experts : g.E) : 1;
+  const int wrow_bytes = K / 8 * BITS;  // bytes of one packed weight row
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.A, 0, g.a_rows * K * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rW =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, 0, n_groups * N * (K / 2), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.W, 0, n_groups * N * wrow_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rS =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale, 0, n_groups * N * KG * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
@@ -279,8 +286,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     }
     ts.c0 = GATEUP ? ntile * (BN / 2) + wave * 32 : ntile * BN + wave * 64;
     ts.cvalid = ts.c0 < (GATEUP ? N / 2 : N);
+    // the expert's index in the weight tensors (a mixed layer's width
+    // tensors hold only that width's experts)
+    if (MIX) e = g.slot[e];
     const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
-    ts.b_lane = (uint32_t)wrow0 * (K / 2) + lg * 16;
+    ts.b_lane = (uint32_t)wrow0 * wrow_bytes + lg * 4 * BITS;
     ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
     if (WIN) {
       // lane l loads the window of the wave's weight row l: gate/up lanes
@@ -307,9 +317,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // weights and the group's scale (and min) of stage kt into registers
   auto load_b = [&](const GemmTile& ts, int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f)
-      cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            ts.shared ? rW2 : rW, ts.b_lane, frow(f) * (K / 2) + kt * (BK / 2), 0));
+    for (int f = 0; f < NFRAG; ++f) {
+      const int so = frow(f) * wrow_bytes + kt * (BK / 8 * BITS);
+      if (BITS == 4) {
+        cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ts.shared ? rW2 : rW, ts.b_lane, so, 0));
+      } else if (BITS == 3) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rW, ts.b_lane, so, 0);
+        cb[f] = u32x4{v[0], v[1], v[2], 0u};
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rW, ts.b_lane, so, 0);
+        cb[f] = u32x4{v[0], v[1], 0u, 0u};
+      }
+    }
     if (SCM == SC_STAGE) {
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
@@ -372,6 +392,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 
   f32x4 acc[MSUB][NFRAG];
 
+  // chunk c (elements 8c .. 8c+7 of the lane's 32-element K block) of one
+  // fragment's packed weights -> eight fp16 weights
+  auto dequant_chunk = [&](const u32x4& w, int c, f16x2 s2, f16x2 m2) {
+    if (BITS == 4) return dequant8_f16<ASYM>(w[c], s2, m2);
+    if (BITS == 2) return dequant8_f16_b2(w[c >> 1], c & 1, s2);
+    return dequant8_f16_b3(w[c >> 1], w[2], c, s2);
+  };
+
   // One K stage from ring slot `as_base`: four 32-wide K steps x eight
   // 16-row sub-tiles. Two waves share each SIMD, so the hardware interleaves
   // one wave's dequant and LDS reads with the other's MFMAs. Every sub-tile
@@ -397,7 +425,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // j's MFMAs run (one fragment behind each of the first sub-tiles)
     f16x8 b[NFRAG];
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f) b[f] = dequant8_f16<ASYM>(cb[f][0], cs[f], cm[f]);
+    for (int f = 0; f < NFRAG; ++f) b[f] = dequant_chunk(cb[f], 0, cs[f], cm[f]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x8 bn[NFRAG];
@@ -410,7 +438,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         for (int f = 0; f < NFRAG; ++f)
           acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
                               : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
-        if (j < 3 && mi < NFRAG) bn[mi] = dequant8_f16<ASYM>(cb[mi][j + 1], cs[mi], cm[mi]);
+        if (j < 3 && mi < NFRAG) bn[mi] = dequant_chunk(cb[mi], j + 1, cs[mi], cm[mi]);
         if (mi + 1 < MSUB) a = an;
       }
       if (j < 3) {
@@ -636,7 +664,27 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   const std::integral_constant<int, SC_STAGE> stage_sc{};
   const std::integral_constant<int, SC_TILE> tile_sc{};
   const std::integral_constant<int, SC_WINDOW> win_sc{};
-  if (asym) {
+  if (g.tier != nullptr) {
+    // one width of a mixed-width layer (symmetric, no extra group)
+    auto go_b = [&](auto m, auto b) {
+      constexpr int M = decltype(m)::value, B = decltype(b)::value;
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, false, M, false, B, true>), grid, block, 0,
+                         s, g, n_ntiles);
+    };
+    const std::integral_constant<int, 4> b4{};
+    const std::integral_constant<int, 3> b3{};
+    const std::integral_constant<int, 2> b2{};
+    if (g.bits == 3) {
+      if (scl) go_b(tile_sc, b3);
+      else go_b(stage_sc, b3);
+    } else if (g.bits == 2) {
+      if (scl) go_b(tile_sc, b2);
+      else go_b(stage_sc, b2);
+    } else {
+      if (scl) go_b(tile_sc, b4);
+      else go_b(stage_sc, b4);
+    }
+  } else if (asym) {
     if (fold) {
       if (win) go(yes, win_sc, yes);
       else go(yes, stage_sc, yes);

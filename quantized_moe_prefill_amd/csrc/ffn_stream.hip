@@ -430,6 +430,7 @@ bool stream_supported(const GroupedGemm& g, bool gateup) {
   // K in whole stages, at most 16 of them (four per wave); whole items of
   // columns; at most 256 groups; gate/up: at most 16 tokens and 256 rows
   if (g.K % SBK != 0 || g.K / SBK > 16 || g.E > SMAXG) return false;
+  if (g.tier != nullptr || g.slot != nullptr || (g.bits != 0 && g.bits != 4)) return false;
   int ns, nf;
   stream_tiling(g.K, &ns, &nf);
   if (gateup) {

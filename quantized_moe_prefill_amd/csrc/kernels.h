@@ -89,6 +89,15 @@ struct GroupedGemm {
   const uint16_t* Wmin2;
   uint16_t* C2;
   int ldc2;
+  // One width of a mixed-width layer (tier != NULL; symmetric, no extra
+  // group): the launch computes only the experts e with tier[e] == bits
+  // (tier and slot are device arrays), whose weights and scales are expert
+  // slot[e] of W / Wscale, which hold w_experts experts. bits is 4, or 3 / 2
+  // for the lower-bit codes of dequant.h (rows of K * bits / 8 bytes).
+  const int32_t* tier;
+  const int32_t* slot;
+  int w_experts;
+  int bits;
 };
 constexpr int kStreamMaxRows = 16;
 // gate/up with fused SwiGLU: N = 2I weight rows, writes h = silu(g)*u

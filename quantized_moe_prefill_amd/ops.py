@@ -211,6 +211,59 @@ def moe_layer_forward_i8(shape, x, w_router, router_bias, experts: Experts, resi
     return out
 
 
+class MixedExperts:
+    """Mixed-width expert weights of one layer as the C tier array plus the
+    per-expert width and slot arrays on the device (keeps the tensors
+    alive). Accepts a synth.MixedLayer (or any object with `bits`, `slot`
+    and `tiers` = {bits: (w13, w13_scale, w2, w2_scale)})."""
+
+    def __init__(self, ml, device):
+        self.keep = []
+        tiers = []
+        for b, (w13, s13, w2, s2) in sorted(ml.tiers.items(), reverse=True):
+            self.keep += [w13, s13, w2, s2]
+            tiers.append(N.MoeTier(int(b), int(w13.shape[0]), _ptr(w13, "w13", (torch.uint8,)),
+                                   _ptr(s13, "w13_scale", _U16), _ptr(w2, "w2", (torch.uint8,)),
+                                   _ptr(s2, "w2_scale", _U16)))
+        self.n = len(tiers)
+        self.array = (N.MoeTier * self.n)(*tiers)
+        self.bits = torch.tensor(list(ml.bits), dtype=torch.int32, device=device)
+        self.slot = torch.tensor(list(ml.slot), dtype=torch.int32, device=device)
+
+
+def moe_expert_ffn_mixed(shape, x, experts: MixedExperts, counts, offsets, sorted_pairs, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    P = T * shape.top_k
+    y_perm = torch.empty((max(P, 1), shape.hidden), dtype=torch.float16, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_EXPERT_FFN)
+    N.check(N.lib().moe_expert_ffn_mixed(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), experts.array, experts.n,
+        _ptr(experts.bits, "expert_bits"), _ptr(experts.slot, "expert_slot"),
+        _ptr(counts, "counts", (torch.int32,), dev), _ptr(offsets, "offsets", (torch.int32,), dev),
+        _ptr(sorted_pairs, "sorted_pairs", (torch.int32,), dev), _ptr(y_perm, "y_perm"),
+        _ptr(ws, "ws"), ws.numel(), _stream(dev)))
+    return y_perm[:P]
+
+
+def moe_layer_forward_mixed(shape, x, w_router, router_bias, experts: MixedExperts, residual=None,
+                            out=None, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(shape, T, dev, N.MOE_WS_LAYER)
+    N.check(N.lib().moe_layer_forward_mixed(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev), experts.array, experts.n,
+        _ptr(experts.bits, "expert_bits"), _ptr(experts.slot, "expert_slot"),
+        _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _ptr(ws, "ws"),
+        ws.numel(), _stream(dev)))
+    return out
+
+
 def moe_rmsnorm(x, weight, eps: float, out=None):
     T, H = x.shape
     dev = x.device

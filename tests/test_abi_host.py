@@ -196,3 +196,33 @@ def test_integer_route_validation_before_launch():
     assert L.moe_quantize_rows_i8(4, 12, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
     assert L.moe_quantize_rows_i8(4, 16, FAKE, None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_quantize_rows_i8(0, 16, None, None, None, None) == N.MOE_OK
+
+
+def test_mixed_width_validation_before_launch():
+    L = _lib()
+    s = _shape()
+    st, need = _ws(s, 4)
+    T3 = N.MoeTier * 3
+
+    def tiers(*bits):
+        return T3(*[N.MoeTier(b, 4, FAKE, FAKE, FAKE, FAKE) for b in bits] +
+                  [N.MoeTier(0, 0, None, None, None, None)] * (3 - len(bits)))
+
+    def call(tarr, n, shape=s, ws_bytes=need):
+        return L.moe_layer_forward_mixed(ctypes.byref(shape), 4, FAKE, FAKE, None, tarr, n, FAKE, FAKE,
+                                         None, FAKE, FAKE, ws_bytes, None)
+    assert call(tiers(4, 2), 0) == N.MOE_ERR_INVALID_ARGUMENT
+    assert call(tiers(4, 2), 4) == N.MOE_ERR_INVALID_ARGUMENT
+    assert call(tiers(4, 4), 2) == N.MOE_ERR_INVALID_ARGUMENT        # two tiers of one width
+    assert call(tiers(4, 5), 2) == N.MOE_ERR_UNSUPPORTED             # no 5-bit codes
+    assert call(None, 1) == N.MOE_ERR_INVALID_ARGUMENT
+    assert call(tiers(4, 3, 2), 3, shape=_shape(quant=1)) == N.MOE_ERR_UNSUPPORTED
+    assert call(tiers(4, 3, 2), 3, shape=_shape(shared_inter=512)) == N.MOE_ERR_UNSUPPORTED
+    assert call(tiers(4, 3, 2), 3, ws_bytes=need - 1) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    bad = T3(N.MoeTier(3, 4, None, FAKE, FAKE, FAKE), N.MoeTier(0, 0, None, None, None, None),
+             N.MoeTier(0, 0, None, None, None, None))
+    assert call(bad, 1) == N.MOE_ERR_INVALID_ARGUMENT                 # missing weights
+    assert L.moe_expert_ffn_mixed(ctypes.byref(s), 4, FAKE, tiers(2), 1, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, 0, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_expert_ffn_mixed(ctypes.byref(s), 0, None, tiers(2), 1, None, None, None, None,
+                                  None, None, None, 0, None) == N.MOE_OK
