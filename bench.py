@@ -4,6 +4,9 @@
     python bench.py --route i8 ...        the integer route (moe_layer_forward_i8):
                                           8-bit activations on the int8 matrix cores,
                                           gate/up roofline against the int8 peak
+    python bench.py --tiers 4:32,3:48,2:48 mixed-width experts (moe_layer_forward_mixed):
+                                          the experts that receive the most rows of
+                                          the batch get the first width, and so on
     python bench.py --calib-copy ...      also run a 1 GiB device copy (counter scale)
     python bench.py --pmc-summary FETCH.csv WRITE.csv
                                           HBM bytes per launch from two rocprofv3
@@ -77,6 +80,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--route", choices=("fp16", "i8"), default="fp16",
                     help="expert route: fp16 matrix cores (default) or the integer route")
+    ap.add_argument("--tiers", default="",
+                    help="mixed widths, e.g. 4:32,3:48,2:48 (bits:experts, hottest first)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one elementwise kernel that reads and writes 1 GiB "
                          "(counter calibration)")
@@ -138,7 +143,7 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
           f"{gemm_source_hash(I8_SOURCES)}")
 
 
-def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False):
+def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False, mixed=None):
     """The oracle as it stands, on the whole batch, repeated until about
     min_seconds of CPU work (at most max_passes passes)."""
     import numpy as np
@@ -157,7 +162,9 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False):
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        if i8:
+        if mixed is not None:
+            oracle.moe_layer_mixed(xb, mixed, cfg.k, cfg.G)
+        elif i8:
             oracle.moe_layer_i8(xb, cpu, cfg.k, cfg.G)
         else:
             oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
@@ -169,7 +176,8 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False):
         "cores": blas_threads or cores,
         "kind": "oracle",
         "sample": f"the whole {x.shape[0]}-token batch, {passes} passes of the float64 numpy "
-                  f"oracle{' (integer route)' if i8 else ''} (dequantize all experts + route + "
+                  f"oracle{' (integer route)' if i8 else (' (mixed widths)' if mixed else '')} "
+                  f"(dequantize all experts + route + "
                   f"experts + combine), {dt:.1f} s in "
                   f"total; {cores} cores visible, BLAS threads {blas_threads}",
     }
@@ -227,6 +235,12 @@ def main():
     torch.cuda.set_device(dev)
     stacked = cfg.n_layers > 1
     i8 = a.route == "i8"
+    tiers = [(int(b), int(n)) for b, n in (t.split(":") for t in a.tiers.split(","))] if a.tiers else []
+    if tiers and (i8 or stacked or cfg.quant != "sym" or cfg.shared_I or
+                  sum(n for _, n in tiers) != cfg.E):
+        print(f"mixed widths need one layer of symmetric experts without a shared expert and "
+              f"expert counts that add up to E = {cfg.E}", file=sys.stderr)
+        sys.exit(2)
     if i8 and (stacked or cfg.quant != "sym" or cfg.G != 128 or cfg.shared_I):
         print(f"the integer route needs one layer of symmetric experts with group 128 and no "
               f"shared expert ({cfg.name} is not)", file=sys.stderr)
@@ -244,7 +258,28 @@ def main():
     else:
         li = make_layer(cfg, device=dev)
         out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
-        if i8:
+        mixed = None
+        if tiers:
+            from synth.mixed import make_mixed_layer
+            # widths by how many rows each expert receives in this batch
+            shape = qm.shape_of(cfg)
+            _, ids0, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None)
+            load = torch.bincount(ids0.flatten().long(), minlength=cfg.E).cpu()
+            order = torch.argsort(-load, stable=True).tolist()
+            widths = [4] * cfg.E
+            pos = 0
+            for b, n in tiers:
+                for e in order[pos:pos + n]:
+                    widths[e] = b
+                pos += n
+            mixed = make_mixed_layer(cfg, widths, device=dev)
+            experts = qm.MixedExperts(mixed, dev)
+            ws = qm.workspace(shape, T, dev, qm.MOE_WS_LAYER)
+
+            def step():
+                qm.moe_layer_forward_mixed(shape, x, mixed.w_router, mixed.router_bias, experts,
+                                           out=out, ws=ws)
+        elif i8:
             shape = qm.shape_of(cfg)
             experts = qm.Experts(li)
             ws = qm.workspace(shape, T, dev, qm.MOE_WS_LAYER_I8)
@@ -331,7 +366,9 @@ def main():
     for name in (KERNELS_I8 if i8 else KERNELS) + ("rmsnorm",):
         n, tot = qm.profile_read(name)
         if n:
-            kernels[name] = round(tot / n * 1000.0, 2)  # microseconds per launch
+            # microseconds per launch (per step: a mixed-width layer launches
+            # each expert GEMM once per width)
+            kernels[name] = round(tot / (a.steps if tiers else n) * 1000.0, 2)
     qm.profile_enable(0)
 
     # the work of one layer application over n rows
@@ -355,6 +392,8 @@ def main():
                                          li.shared_gate)
         active = int(torch.unique(ids).numel())
     weight_bytes = (active * cfg.expert_bytes() + cfg.shared_bytes()) * n_apps
+    if tiers:
+        weight_bytes = mixed.nbytes()
     io_bytes = (cfg.E * cfg.H * 4) * n_apps + 2 * T * cfg.H * 2
     hbm_gbs = (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9
     # gate/up launch: the active experts' gate/up weights and scales (+ mins),
@@ -362,6 +401,9 @@ def main():
     per = 2 if cfg.quant == "sym" else 4
     gu_bytes = (active * (cfg.I * cfg.H + 2 * cfg.I * (cfg.H // cfg.G) * per)
                 + T * cfg.H * (1 if i8 else 2) + P * cfg.I * 2)
+    if tiers:
+        gu_bytes = (sum(v[0].numel() + 2 * v[1].numel() for v in mixed.tiers.values())
+                    + T * cfg.H * 2 + P * cfg.I * 2)
     peak = PEAK_I8_TOPS if i8 else PEAK_BF16_TFLOPS
     if cold:
         gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9 if gu_us else None
@@ -379,7 +421,7 @@ def main():
             "frac": round(achieved / peak, 4) if achieved else None,
             "traffic": ((GATEUP_I8_TRAFFIC.get(gemm_source_hash(I8_SOURCES)) if i8
                          else GATEUP_TRAFFIC.get(gemm_source_hash()))
-                        if (cfg.name, T) == ("a3b_pp8192", 8192) else None),
+                        if (cfg.name, T) == ("a3b_pp8192", 8192) and not tiers else None),
             "flops_per_launch": gu_flops,
         }
 
@@ -406,7 +448,9 @@ def main():
             "workload": desc,
             "T": T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k, "inter": cfg.I,
             "group": cfg.G, "quant": cfg.quant, "shared_inter": cfg.shared_I,
-            "layers": cfg.n_layers, "route": "int8 activations" if i8 else "fp16",
+            "layers": cfg.n_layers,
+            "route": ("int8 activations" if i8 else
+                      ("fp16, mixed widths " + a.tiers if tiers else "fp16")),
         },
         "layer_tflops": round(layer_tflops, 1),
         "layer_mfma_frac": round(layer_tflops / peak, 4),
@@ -436,7 +480,8 @@ def main():
         if stacked:
             rec["cpu_baseline"] = stack_cpu_baseline(cfg, [l.to("cpu") for l in layers[:2]], x)
         else:
-            rec["cpu_baseline"] = cpu_baseline(cfg, li, x, i8=i8)
+            rec["cpu_baseline"] = cpu_baseline(cfg, li, x, i8=i8,
+                                               mixed=mixed.to("cpu") if tiers else None)
     print(json.dumps(rec), flush=True)
 
 

@@ -62,6 +62,9 @@ __device__ __forceinline__ f16x8 dequant8_f16_b2(uint32_t w, int h, f16x2 s2) {
 // for element 8c + i + 4. Chunk c (0..3) of the block -> eight fp16 weights
 // (its low bits are chunk c % 2 of 2-bit word c / 2, passed as w).
 __device__ __forceinline__ f16x8 dequant8_f16_b3(uint32_t w, uint32_t hb, int c, f16x2 s2) {
+  // (an opaque copy per call: otherwise the compiler computes the shifted
+  // high-bit words of every chunk up front and holds them in registers)
+  asm("" : "+v"(hb));
   const f16x2 off = {(_Float16)1028.0f, (_Float16)1028.0f};
   const uint32_t mask = __builtin_amdgcn_readfirstlane(0x00030003u);
   uint32_t magic = 0x64006400u;

@@ -161,6 +161,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
   constexpr bool SCL = SCM == SC_TILE;
   constexpr bool WIN = SCM == SC_WINDOW;
+  // a lane's packed weights of one fragment and stage: 4 * BITS bytes
+  typedef uint32_t WV __attribute__((ext_vector_type(BITS)));
   __shared__ __attribute__((aligned(16))) uint8_t Sc[SCM != SC_STAGE ? NWAVES * SC_WAVE : 16];
   __shared__ int s_scan[258];
   __shared__ int s_wave[NWAVES];
@@ -315,19 +317,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           kt * BK * 2, 0, 0);
   };
   // weights and the group's scale (and min) of stage kt into registers
-  auto load_b = [&](const GemmTile& ts, int kt, u32x4* cb, uint32_t* rs, uint32_t* rm) {
+  auto load_b = [&](const GemmTile& ts, int kt, WV* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
       const int so = frow(f) * wrow_bytes + kt * (BK / 8 * BITS);
-      if (BITS == 4) {
+      if constexpr (BITS == 4) {
         cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               ts.shared ? rW2 : rW, ts.b_lane, so, 0));
-      } else if (BITS == 3) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b96(rW, ts.b_lane, so, 0);
-        cb[f] = u32x4{v[0], v[1], v[2], 0u};
+      } else if constexpr (BITS == 3) {
+        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b96(rW, ts.b_lane, so, 0));
       } else {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rW, ts.b_lane, so, 0);
-        cb[f] = u32x4{v[0], v[1], 0u, 0u};
+        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(rW, ts.b_lane, so, 0));
       }
     }
     if (SCM == SC_STAGE) {
@@ -394,10 +394,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 
   // chunk c (elements 8c .. 8c+7 of the lane's 32-element K block) of one
   // fragment's packed weights -> eight fp16 weights
-  auto dequant_chunk = [&](const u32x4& w, int c, f16x2 s2, f16x2 m2) {
-    if (BITS == 4) return dequant8_f16<ASYM>(w[c], s2, m2);
-    if (BITS == 2) return dequant8_f16_b2(w[c >> 1], c & 1, s2);
-    return dequant8_f16_b3(w[c >> 1], w[2], c, s2);
+  auto dequant_chunk = [&](const WV& w, int c, f16x2 s2, f16x2 m2) {
+    if constexpr (BITS == 4) return dequant8_f16<ASYM>(w[c], s2, m2);
+    else if constexpr (BITS == 2) return dequant8_f16_b2(w[c >> 1], c & 1, s2);
+    else return dequant8_f16_b3(w[c >> 1], w[2], c, s2);
   };
 
   // One K stage from ring slot `as_base`: four 32-wide K steps x eight
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // results are never stored. The down GEMM swaps the operands
   // (C^T = W A^T), so each lane ends up with four consecutive output
   // columns of one row.
-  auto compute_stage = [&](const uint8_t* __restrict__ as_base, const u32x4* cb, const uint32_t* rs,
+  auto compute_stage = [&](const uint8_t* __restrict__ as_base, const WV* cb, const uint32_t* rs,
                            const uint32_t* rm) {
     f16x2 cs[NFRAG], cm[NFRAG];
 #pragma unroll
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const int klast = nk - 1;
   GemmTile cur;
   setup(tile, cur);
-  u32x4 cb[NFRAG];
+  WV cb[NFRAG];
   uint32_t rs[NFRAG], rm[NFRAG];
   load_sc(cur);
   load_b(cur, 0, cb, rs, rm);
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // scale window with that of stages kt + 1, kt + 2
     auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2,
                      bool odd) {
-      u32x4 cbn[NFRAG];
+      WV cbn[NFRAG];
       uint32_t rsn[NFRAG], rmn[NFRAG];
       load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
       if (WIN && odd) load_win(cur, (kt + 1) >> 1);
