@@ -294,6 +294,37 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t *shape, int64_t T, const 
                                      const uint16_t *residual, uint16_t *out, void *ws,
                                      size_t ws_bytes, hipStream_t stream);
 
+/* ---- host-resident experts streamed over PCIe, hot set in HBM --------------
+ * The pages run models whose experts do not all fit the GPU: experts stay in
+ * host memory and are streamed over PCIe during prefill, with a set of hot
+ * experts kept resident, and long prompts become limited by that stream
+ * (hipfire 0.4.3 benchmarks page, the Flash-Next rows: "mq2 host experts"
+ * on a narrow PCIe link; the 4096-row chunk limited by the PCIe expert
+ * stream). Here: the hot experts are device tensors, the others (cold) sit in
+ * host memory (pinned, hipHostMalloc, for asynchronous copies); every call
+ * copies the cold experts, as many at a time as half of `stage` holds, into
+ * the device staging buffer and runs them through the same grouped GEMMs
+ * (symmetric 4-bit experts, no shared expert). Copies and kernels are
+ * ordered on `stream`, so the time is the copy time plus the compute time;
+ * the result is bit-identical to moe_layer_forward with every expert on the
+ * device.
+ *   hot        device experts, hot_count of them (hot may be NULL iff hot_count == 0)
+ *   cold       host experts: the cold ones in ascending expert index, same
+ *              layouts as moe_experts_t ([E_cold][...]); min and shared-expert
+ *              pointers NULL
+ *   hot_slot   HOST array [E]: expert e's index in `hot`, or -1 if it is cold
+ *   stage      device buffer of stage_bytes; must hold at least two experts'
+ *              packed weights and scales (moe_stream_stage_bytes(shape, 2))
+ *   ws         >= moe_workspace_size(MOE_WS_LAYER, T) + 2 * 4 * E + 512 bytes */
+moe_status_t moe_stream_stage_bytes(const moe_shape_t *shape, int32_t experts, size_t *bytes);
+moe_status_t moe_layer_forward_streamed(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                                        const float *w_router, const float *router_bias,
+                                        const moe_experts_t *hot, int32_t hot_count,
+                                        const moe_experts_t *cold, const int32_t *hot_slot,
+                                        void *stage, size_t stage_bytes,
+                                        const uint16_t *residual, uint16_t *out, void *ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
 /* RMSNorm over rows of [T][H] bf16:
  *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )
  * computed in fp32; weight [H] fp32. out must not alias x. */

@@ -7,7 +7,8 @@ library; the first call does, and fails loudly if it has not been built.
 from ._native import (MOE_OK, MOE_ERR_HIP, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED,
                       MOE_ERR_WORKSPACE_TOO_SMALL, MOE_WS_EXPERT_FFN, MOE_WS_EXPERT_FFN_I8,
                       MOE_WS_LAYER, MOE_WS_LAYER_I8, MOE_WS_PERMUTE, MOE_WS_ROUTE, MoeError, lib)
-from .ops import (Experts, MixedExperts, MoELayer, MoEStack, make_shape, moe_combine,
+from .ops import (Experts, MixedExperts, MoELayer, MoEStack, StreamedExperts, make_shape,
+                  moe_combine, moe_layer_forward_streamed, moe_stream_stage_bytes,
                   moe_expert_ffn, moe_expert_ffn_i8, moe_expert_ffn_mixed, moe_layer_forward,
                   moe_layer_forward_i8, moe_layer_forward_mixed, moe_permute,
                   moe_quantize_rows_i8, moe_rmsnorm, moe_route, moe_workspace_size,
@@ -16,7 +17,8 @@ from .ops import (Experts, MixedExperts, MoELayer, MoEStack, make_shape, moe_com
 __all__ = [
     "MOE_OK", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARGUMENT", "MOE_ERR_UNSUPPORTED",
     "MOE_ERR_WORKSPACE_TOO_SMALL", "MOE_WS_EXPERT_FFN", "MOE_WS_EXPERT_FFN_I8", "MOE_WS_LAYER",
-    "MOE_WS_LAYER_I8", "MOE_WS_PERMUTE", "MOE_WS_ROUTE", "MoeError", "lib", "Experts", "MixedExperts", "MoELayer",
+    "MOE_WS_LAYER_I8", "MOE_WS_PERMUTE", "MOE_WS_ROUTE", "MoeError", "lib", "Experts", "MixedExperts", "MoELayer", "StreamedExperts",
+    "moe_layer_forward_streamed", "moe_stream_stage_bytes",
     "MoEStack", "make_shape", "moe_combine", "moe_expert_ffn", "moe_expert_ffn_i8", "moe_expert_ffn_mixed",
     "moe_layer_forward", "moe_layer_forward_mixed", "moe_layer_forward_i8", "moe_permute", "moe_quantize_rows_i8",
     "moe_rmsnorm", "moe_route", "moe_workspace_size", "profile_enable", "profile_read",

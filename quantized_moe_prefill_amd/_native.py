@@ -42,6 +42,8 @@ EXPORTED = [
     "moe_layer_forward_i8",
     "moe_expert_ffn_mixed",
     "moe_layer_forward_mixed",
+    "moe_stream_stage_bytes",
+    "moe_layer_forward_streamed",
     "moe_rmsnorm",
     "moe_profile_enable",
     "moe_profile_reset",
@@ -127,6 +129,11 @@ def lib():
     L.moe_layer_forward_mixed.restype = st
     L.moe_layer_forward_mixed.argtypes = [sp, i64, P, P, P, tp, i32, P, P, P, P, P,
                                           ctypes.c_size_t, P]
+    L.moe_stream_stage_bytes.restype = st
+    L.moe_stream_stage_bytes.argtypes = [sp, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_layer_forward_streamed.restype = st
+    L.moe_layer_forward_streamed.argtypes = [sp, i64, P, P, P, ep, i32, ep, P, P, ctypes.c_size_t,
+                                             P, P, P, ctypes.c_size_t, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

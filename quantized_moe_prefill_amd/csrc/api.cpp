@@ -3,6 +3,7 @@
 // per-kernel event timing. See include/moe.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -482,6 +483,7 @@ static moe_status_t ffn_mixed_impl(const Shape& s, int64_t T, const uint16_t* x,
     g.Wscale = tiers[i].w13_scale;
     g.w_experts = tiers[i].num_experts;
     g.bits = tiers[i].bits;
+    g.tier_id = tiers[i].bits;  // expert_bits holds the widths
     QMOE_HIP(launch_gateup(g, st), "gateup launch");
   }
   GroupedGemm d = g;
@@ -497,9 +499,28 @@ static moe_status_t ffn_mixed_impl(const Shape& s, int64_t T, const uint16_t* x,
     d.Wscale = tiers[i].w2_scale;
     d.w_experts = tiers[i].num_experts;
     d.bits = tiers[i].bits;
+    d.tier_id = tiers[i].bits;
     QMOE_HIP(launch_down(d, st), "down launch");
   }
   return MOE_OK;
+}
+
+// ---- host-streamed experts ----
+// One expert's packed bytes (symmetric 4-bit, no mins), each array padded
+// to 256 bytes inside a staging slot.
+struct StageLayout {
+  size_t w13, s13, w2, s2;  // bytes per expert of each array
+};
+static StageLayout stage_layout(const Shape& s) {
+  StageLayout L;
+  L.w13 = (size_t)2 * s.I * s.H / 2;
+  L.s13 = (size_t)2 * s.I * (s.H / s.G) * 2;
+  L.w2 = (size_t)s.H * s.I / 2;
+  L.s2 = (size_t)s.H * (s.I / s.G) * 2;
+  return L;
+}
+static size_t stage_slot_bytes(const StageLayout& L, int n) {
+  return al(L.w13 * n) + al(L.s13 * n) + al(L.w2 * n) + al(L.s2 * n);
 }
 
 }  // namespace qmoe
@@ -877,6 +898,177 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t* shape, int64_t T, const 
   st = ffn_mixed_impl(s, T, x, tiers, n_tiers, expert_bits, expert_slot, counts, offsets, sorted,
                       yperm, x16, h, stream);
   if (st != MOE_OK) return st;
+  QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_stream_stage_bytes(const moe_shape_t* shape, int32_t experts, size_t* bytes) {
+  Shape s;
+  moe_status_t st = check_shape(shape, 0, &s);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr || experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "bad argument");
+  // two slots of experts / 2 (at least one) experts each
+  const int per = experts > 1 ? (experts + 1) / 2 : 1;
+  *bytes = 2 * stage_slot_bytes(stage_layout(s), per);
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                        const float* w_router, const float* router_bias,
+                                        const moe_experts_t* hot, int32_t hot_count,
+                                        const moe_experts_t* cold, const int32_t* hot_slot,
+                                        void* stage, size_t stage_bytes,
+                                        const uint16_t* residual, uint16_t* out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "streamed experts need MOE_Q4_SYM");
+  if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "streamed layers have no shared expert");
+  if (hot_slot == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "hot_slot is NULL");
+  if (hot_count < 0 || hot_count > s.E) return fail(MOE_ERR_INVALID_ARGUMENT, "bad hot_count");
+  // the host-side maps: hot experts keep their slot in `hot` (group 0), the
+  // cold ones are numbered in expert order and dealt to chunks of `cap`
+  ExpertMaps maps;
+  std::vector<int> cold_ids;
+  for (int e = 0; e < s.E; ++e) {
+    const int h = hot_slot[e];
+    if (h >= 0) {
+      if (h >= hot_count) return fail(MOE_ERR_INVALID_ARGUMENT, "hot_slot[%d] = %d >= hot_count", e, h);
+      maps.group[e] = 0;
+      maps.slot[e] = h;
+    } else {
+      cold_ids.push_back(e);
+    }
+  }
+  const int n_cold = (int)cold_ids.size();
+  if (hot_count > 0) {
+    if (hot == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "hot is NULL");
+    QMOE_REQUIRE(hot->w13, "hot->w13");
+    QMOE_REQUIRE(hot->w13_scale, "hot->w13_scale");
+    QMOE_REQUIRE(hot->w2, "hot->w2");
+    QMOE_REQUIRE(hot->w2_scale, "hot->w2_scale");
+  }
+  const StageLayout SL = stage_layout(s);
+  int cap = 0;
+  if (n_cold > 0) {
+    if (cold == nullptr || cold->w13 == nullptr || cold->w13_scale == nullptr ||
+        cold->w2 == nullptr || cold->w2_scale == nullptr)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "cold experts missing");
+    QMOE_REQUIRE(stage, "stage");
+    while (cap < n_cold && 2 * stage_slot_bytes(SL, cap + 1) <= stage_bytes) ++cap;
+    if (cap == 0)
+      return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "stage holds no two experts (%zu bytes)", stage_bytes);
+    for (int c = 0; c < n_cold; ++c) {
+      maps.group[cold_ids[c]] = 1 + c / cap;
+      maps.slot[cold_ids[c]] = c % cap;
+    }
+  }
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(out, "out");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(residual, "residual");
+  const Layout L = layer_layout(s, T);
+  const size_t maps_off = L.total;
+  st = check_ws(ws, ws_bytes, maps_off + al((size_t)2 * 4 * s.E));
+  if (st != MOE_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  auto* split = reinterpret_cast<uint16_t*>(b + L.split);
+  auto* partial = reinterpret_cast<float*>(b + L.partial);
+  auto* hist = reinterpret_cast<int32_t*>(b + L.hist);
+  auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
+  auto* tw = reinterpret_cast<float*>(b + L.tw);
+  auto* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  auto* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  auto* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  auto* x16 = reinterpret_cast<uint16_t*>(b + L.x16);
+  auto* h = reinterpret_cast<uint16_t*>(b + L.h);
+  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
+  auto* dgroup = reinterpret_cast<int32_t*>(b + maps_off);
+  auto* dslot = dgroup + s.E;
+  QMOE_HIP(launch_write_maps(maps, s.E, dgroup, dslot, stream), "maps launch");
+  if (router_uses_gemv((int)T)) {
+    QMOE_HIP(launch_route_permute_small(x, w_router, nullptr, partial, router_bias, (int)T, s.H,
+                                        s.E, s.k, ids, tw, nullptr, counts, offsets, sorted, inv,
+                                        stream),
+             "router launch");
+  } else {
+    st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
+                    partial, stream);
+    if (st != MOE_OK) return st;
+    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
+             "permute launch");
+  }
+  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, stream), "x_to_f16 launch");
+  const int P = (int)(T * s.k);
+  GroupedGemm g{};
+  g.A = x16;
+  g.gather = sorted;
+  g.gather_div = s.k;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.E = s.E;
+  g.max_rows = P;
+  g.a_rows = (int)T;
+  g.N = 2 * s.I;
+  g.K = s.H;
+  g.G = s.G;
+  g.C = h;
+  g.ldc = s.I;
+  g.tier = dgroup;
+  g.slot = dslot;
+  g.bits = 4;
+  GroupedGemm d = g;
+  d.A = h;
+  d.a_rows = P;
+  d.gather = nullptr;
+  d.N = s.H;
+  d.K = s.I;
+  d.C = yperm;
+  d.ldc = s.H;
+  auto run_group = [&](int id, int nexp, const uint8_t* w13, const uint16_t* s13,
+                       const uint8_t* w2, const uint16_t* s2) -> moe_status_t {
+    g.tier_id = d.tier_id = id;
+    g.w_experts = d.w_experts = nexp;
+    g.W = w13;
+    g.Wscale = s13;
+    d.W = w2;
+    d.Wscale = s2;
+    QMOE_HIP(launch_gateup(g, stream), "gateup launch");
+    QMOE_HIP(launch_down(d, stream), "down launch");
+    return MOE_OK;
+  };
+  if (hot_count > 0) {
+    st = run_group(0, hot_count, hot->w13, hot->w13_scale, hot->w2, hot->w2_scale);
+    if (st != MOE_OK) return st;
+  }
+  const size_t slot_bytes = stage_slot_bytes(SL, cap);
+  for (int c0 = 0, j = 0; c0 < n_cold; c0 += cap, ++j) {
+    const int n = std::min(cap, n_cold - c0);
+    uint8_t* base = static_cast<uint8_t*>(stage) + (size_t)(j & 1) * slot_bytes;
+    uint8_t* w13 = base;
+    uint8_t* s13 = w13 + al(SL.w13 * cap);
+    uint8_t* w2 = s13 + al(SL.s13 * cap);
+    uint8_t* s2 = w2 + al(SL.w2 * cap);
+    // the chunk's experts are consecutive in the cold tensors
+    QMOE_HIP(hipMemcpyAsync(w13, cold->w13 + SL.w13 * c0, SL.w13 * n, hipMemcpyHostToDevice, stream),
+             "expert copy");
+    QMOE_HIP(hipMemcpyAsync(s13, reinterpret_cast<const uint8_t*>(cold->w13_scale) + SL.s13 * c0,
+                            SL.s13 * n, hipMemcpyHostToDevice, stream),
+             "expert copy");
+    QMOE_HIP(hipMemcpyAsync(w2, cold->w2 + SL.w2 * c0, SL.w2 * n, hipMemcpyHostToDevice, stream),
+             "expert copy");
+    QMOE_HIP(hipMemcpyAsync(s2, reinterpret_cast<const uint8_t*>(cold->w2_scale) + SL.s2 * c0,
+                            SL.s2 * n, hipMemcpyHostToDevice, stream),
+             "expert copy");
+    st = run_group(1 + j, cap, w13, reinterpret_cast<const uint16_t*>(s13), w2,
+                   reinterpret_cast<const uint16_t*>(s2));
+    if (st != MOE_OK) return st;
+  }
   QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");
   return MOE_OK;

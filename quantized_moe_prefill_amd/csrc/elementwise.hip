@@ -127,6 +127,23 @@ hipError_t launch_combine(const uint16_t* y_perm, const int32_t* inv, const floa
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void write_maps_kernel(ExpertMaps m, int E, int32_t* group,
+                                                         int32_t* slot) {
+  const int e = threadIdx.x;
+  if (e < E) {
+    group[e] = m.group[e];
+    slot[e] = m.slot[e];
+  }
+}
+
+hipError_t launch_write_maps(const ExpertMaps& m, int E, int32_t* group, int32_t* slot,
+                             hipStream_t s) {
+  if (E <= 0 || E > 256) return hipErrorInvalidValue;
+  LaunchScope ls("write_maps", s);
+  hipLaunchKernelGGL(write_maps_kernel, dim3(1), dim3(256), 0, s, m, E, group, slot);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* out, int T,
                           int H, hipStream_t s) {
   const dim3 grid(cdiv(T, 4)), block(256);

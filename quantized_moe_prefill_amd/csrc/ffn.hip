@@ -140,8 +140,8 @@ constexpr int SC_STAGE = 0, SC_TILE = 1, SC_WINDOW = 2;
 
 // BITS: the weights' width (4; or 3 or 2, symmetric, see dequant.h). A
 // lane's 32-element K block of a row is 4 * BITS bytes: one 16-, 12- or
-// 8-byte load per fragment and stage. MIX: one width of a mixed-width
-// layer (the expert filter and slot map of GroupedGemm are read).
+// 8-byte load per fragment and stage. MIX: one group of experts of a
+// mixed layer (the expert filter and slot map of GroupedGemm are read).
 template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = false>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   // LDS, two uses:
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const int ngrp = g.E + (has2 ? 1 : 0);
   if (g.counts != nullptr) {
     // (a launch for one width of a mixed layer takes only that width's experts)
-    const int c = tid < g.E ? ((!MIX || g.tier[tid] == BITS) ? g.counts[tid] : 0)
+    const int c = tid < g.E ? ((!MIX || g.tier[tid] == g.tier_id) ? g.counts[tid] : 0)
                             : (has2 && tid == g.E ? g.rows2 : 0);
     int incl = (c + BM - 1) / BM;
 #pragma unroll

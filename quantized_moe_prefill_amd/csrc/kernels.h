@@ -89,16 +89,27 @@ struct GroupedGemm {
   const uint16_t* Wmin2;
   uint16_t* C2;
   int ldc2;
-  // One width of a mixed-width layer (tier != NULL; symmetric, no extra
-  // group): the launch computes only the experts e with tier[e] == bits
-  // (tier and slot are device arrays), whose weights and scales are expert
-  // slot[e] of W / Wscale, which hold w_experts experts. bits is 4, or 3 / 2
-  // for the lower-bit codes of dequant.h (rows of K * bits / 8 bytes).
+  // One group of experts of a mixed layer (tier != NULL; symmetric, no
+  // extra group): the launch computes only the experts e with
+  // tier[e] == tier_id (tier and slot are device arrays), whose weights and
+  // scales are expert slot[e] of W / Wscale, which hold w_experts experts.
+  // bits is the group's width: 4, or 3 / 2 for the lower-bit codes of
+  // dequant.h (rows of K * bits / 8 bytes).
   const int32_t* tier;
   const int32_t* slot;
+  int tier_id;
   int w_experts;
   int bits;
 };
+
+// Per-expert group and slot maps of a mixed layer (at most 256 experts),
+// passed by value and written to device arrays by one small kernel.
+struct ExpertMaps {
+  int32_t group[256];
+  int32_t slot[256];
+};
+hipError_t launch_write_maps(const ExpertMaps& m, int E, int32_t* group, int32_t* slot,
+                             hipStream_t s);
 constexpr int kStreamMaxRows = 16;
 // gate/up with fused SwiGLU: N = 2I weight rows, writes h = silu(g)*u
 // (fp16, kperm chunk order), ldc = I.

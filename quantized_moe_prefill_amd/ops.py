@@ -264,6 +264,76 @@ def moe_layer_forward_mixed(shape, x, w_router, router_bias, experts: MixedExper
     return out
 
 
+def _host_ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu":
+        raise ValueError(f"{name} must be a host (CPU) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+class StreamedExperts:
+    """A layer's experts split into a device-resident hot set and host-
+    resident (pinned) cold experts, for moe_layer_forward_streamed. `li` has
+    the attribute names of synth.LayerInputs (symmetric, no shared expert);
+    `hot` lists the expert indices kept on `device`."""
+
+    def __init__(self, li, hot, device, pin=True):
+        E = li.w13.shape[0]
+        hot = sorted(set(int(e) for e in hot))
+        cold = [e for e in range(E) if e not in set(hot)]
+        self.hot_slot = (ctypes.c_int32 * E)(*[-1] * E)
+        for j, e in enumerate(hot):
+            self.hot_slot[e] = j
+        names = ("w13", "w13_scale", "w2", "w2_scale")
+        self.hot_t = {n: getattr(li, n)[hot].to(device).contiguous() for n in names} if hot else {}
+        self.cold_t = {}
+        for n in names:
+            t = getattr(li, n)[cold].to("cpu").contiguous() if cold else None
+            self.cold_t[n] = t.pin_memory() if (t is not None and pin) else t
+        self.n_hot = len(hot)
+        self.n_cold = len(cold)
+        h = self.hot_t
+        self.hot = N.MoeExperts(*(_ptr(h.get("w13"), "w13"), _ptr(h.get("w13_scale"), "w13_scale"), None,
+                                  _ptr(h.get("w2"), "w2"), _ptr(h.get("w2_scale"), "w2_scale"), None,
+                                  None, None, None, None, None, None)) if hot else None
+        c = self.cold_t
+        self.cold = N.MoeExperts(_host_ptr(c["w13"], "w13"), _host_ptr(c["w13_scale"], "w13_scale"),
+                                 None, _host_ptr(c["w2"], "w2"), _host_ptr(c["w2_scale"], "w2_scale"),
+                                 None, None, None, None, None, None, None) if cold else None
+
+    def cold_bytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.cold_t.values() if t is not None)
+
+
+def moe_stream_stage_bytes(shape, experts: int) -> int:
+    n = ctypes.c_size_t(0)
+    N.check(N.lib().moe_stream_stage_bytes(ctypes.byref(shape), int(experts), ctypes.byref(n)))
+    return n.value
+
+
+def moe_layer_forward_streamed(shape, x, w_router, router_bias, experts: StreamedExperts, stage,
+                               residual=None, out=None, ws=None):
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        n = moe_workspace_size(shape, T, N.MOE_WS_LAYER) + 8 * shape.num_experts + 512
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    N.check(N.lib().moe_layer_forward_streamed(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev),
+        ctypes.byref(experts.hot) if experts.hot is not None else None, experts.n_hot,
+        ctypes.byref(experts.cold) if experts.cold is not None else None, experts.hot_slot,
+        _ptr(stage, "stage"), stage.numel() if stage is not None else 0,
+        _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _ptr(ws, "ws"),
+        ws.numel(), _stream(dev)))
+    return out
+
+
 def moe_rmsnorm(x, weight, eps: float, out=None):
     T, H = x.shape
     dev = x.device

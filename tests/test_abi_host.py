@@ -226,3 +226,27 @@ def test_mixed_width_validation_before_launch():
                                   FAKE, FAKE, FAKE, 0, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_expert_ffn_mixed(ctypes.byref(s), 0, None, tiers(2), 1, None, None, None, None,
                                   None, None, None, 0, None) == N.MOE_OK
+
+
+def test_streamed_validation_before_launch():
+    L = _lib()
+    s = _shape()
+    n = ctypes.c_size_t(0)
+    assert L.moe_stream_stage_bytes(ctypes.byref(s), 2, ctypes.byref(n)) == N.MOE_OK
+    per = 2 * 768 * 2048 // 2 + 2 * 768 * 16 * 2 + 2048 * 768 // 2 + 2048 * 6 * 2
+    assert n.value >= 2 * per
+    E = 128
+    slots = (ctypes.c_int32 * E)(*[-1] * E)
+    cold = N.MoeExperts(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, None, None, None)
+    st, need = _ws(s, 4)
+
+    def call(shape=s, hot_count=0, hot_slot=slots, stage_bytes=1 << 30, ws_bytes=need + 4096):
+        return L.moe_layer_forward_streamed(ctypes.byref(shape), 4, FAKE, FAKE, None, None, hot_count,
+                                            ctypes.byref(cold), hot_slot, FAKE, stage_bytes, None, FAKE,
+                                            FAKE, ws_bytes, None)
+    assert call(shape=_shape(quant=1)) == N.MOE_ERR_UNSUPPORTED
+    assert call(hot_slot=None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert call(stage_bytes=per) == N.MOE_ERR_WORKSPACE_TOO_SMALL     # not two experts
+    assert call(ws_bytes=need - 1) == N.MOE_ERR_WORKSPACE_TOO_SMALL
+    bad = (ctypes.c_int32 * E)(*([0] + [-1] * (E - 1)))
+    assert call(hot_slot=bad, hot_count=0) == N.MOE_ERR_INVALID_ARGUMENT  # slot 0 of an empty hot set

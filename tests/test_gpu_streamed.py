@@ -1,0 +1,61 @@
+"""GPU checks of moe_layer_forward_streamed: cold experts in pinned host
+memory copied over PCIe into a staging buffer chunk by chunk, hot experts on
+the device. The expert GEMMs are the same kernels on the same tiles, so above
+16 tokens the output must equal moe_layer_forward's with every expert on the
+device bit for bit; at 16 tokens or fewer (where moe_layer_forward takes the
+weight-streaming kernels) it is gated against the oracle."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_moe_prefill_amd as qm
+from synth import CONFIGS, make_layer, make_tokens
+from tests.gpu_util import bits, f64_of_bf16, gate
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run(cfg, hot, stage_experts, T=None):
+    li = make_layer(cfg, device=DEV)
+    x = make_tokens(cfg, device=DEV, rows=T)
+    shape = qm.shape_of(cfg)
+    ex = qm.StreamedExperts(li, hot, DEV)
+    stage = torch.empty(qm.moe_stream_stage_bytes(shape, stage_experts), dtype=torch.uint8, device=DEV)
+    out = qm.moe_layer_forward_streamed(shape, x, li.w_router, li.router_bias, ex, stage)
+    ref = qm.MoELayer(cfg, li, DEV, x.shape[0]).forward(x)
+    torch.cuda.synchronize()
+    return li, x, out, ref
+
+
+@pytest.mark.parametrize("name,hot,stage_experts", [
+    ("tiny", [], 2),                 # every expert cold, one expert per chunk
+    ("tiny", [0, 3, 5], 4),          # hot set + two cold chunks
+    ("tiny", list(range(8)), 2),     # every expert hot
+    ("a3b_pp512", list(range(0, 128, 4)), 16),
+])
+def test_streamed_equals_resident_bitwise(name, hot, stage_experts):
+    cfg = CONFIGS[name]
+    _, _, out, ref = run(cfg, hot, stage_experts)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_streamed_full_size_a3b_pp8192():
+    cfg = CONFIGS["a3b_pp8192"]
+    _, _, out, ref = run(cfg, list(range(32)), 24)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_streamed_small_T_against_oracle(T):
+    cfg = CONFIGS["a3b_pp512"]
+    li, x, out, _ = run(cfg, [1, 2, 3], 8, T=T)
+    shape = qm.shape_of(cfg)
+    logits, _, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None, want_logits=True)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(bits(x), li.to("cpu"), cfg.k, cfg.G, cfg.quant,
+                           logits32=logits.cpu().numpy())
+    gate(f64_of_bf16(out), ref["out"], f"out (streamed, T={T})")
