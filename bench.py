@@ -7,6 +7,11 @@
     python bench.py --tiers 4:32,3:48,2:48 mixed-width experts (moe_layer_forward_mixed):
                                           the experts that receive the most rows of
                                           the batch get the first width, and so on
+    python bench.py --stream-hot 32       host-resident experts streamed over PCIe
+                                          (moe_layer_forward_streamed): the 32 experts
+                                          that receive the most rows stay on the GPU;
+                                          --stage-experts sets the staging size,
+                                          --copy-stream overlaps copies and kernels
     python bench.py --calib-copy ...      also run a 1 GiB device copy (counter scale)
     python bench.py --pmc-summary FETCH.csv WRITE.csv
                                           HBM bytes per launch from two rocprofv3
@@ -80,6 +85,12 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--route", choices=("fp16", "i8"), default="fp16",
                     help="expert route: fp16 matrix cores (default) or the integer route")
+    ap.add_argument("--stream-hot", type=int, default=-1,
+                    help="stream the experts from host memory, keeping this many on the GPU")
+    ap.add_argument("--copy-stream", action="store_true",
+                    help="with --stream-hot: copy on a second stream, overlapping the kernels")
+    ap.add_argument("--stage-experts", type=int, default=32,
+                    help="experts the staging buffer holds (two chunks of half of it)")
     ap.add_argument("--tiers", default="",
                     help="mixed widths, e.g. 4:32,3:48,2:48 (bits:experts, hottest first)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -236,6 +247,11 @@ def main():
     stacked = cfg.n_layers > 1
     i8 = a.route == "i8"
     tiers = [(int(b), int(n)) for b, n in (t.split(":") for t in a.tiers.split(","))] if a.tiers else []
+    streamed = a.stream_hot >= 0
+    if streamed and (i8 or tiers or stacked or cfg.quant != "sym" or cfg.shared_I):
+        print("streamed experts need one layer of symmetric experts without a shared expert",
+              file=sys.stderr)
+        sys.exit(2)
     if tiers and (i8 or stacked or cfg.quant != "sym" or cfg.shared_I or
                   sum(n for _, n in tiers) != cfg.E):
         print(f"mixed widths need one layer of symmetric experts without a shared expert and "
@@ -259,7 +275,24 @@ def main():
         li = make_layer(cfg, device=dev)
         out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
         mixed = None
-        if tiers:
+        sx = None
+        if streamed:
+            shape = qm.shape_of(cfg)
+            _, ids0, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None)
+            load = torch.bincount(ids0.flatten().long(), minlength=cfg.E).cpu()
+            hot = torch.argsort(-load, stable=True).tolist()[:a.stream_hot]
+            sx = qm.StreamedExperts(li, hot, dev)
+            stage = torch.empty(qm.moe_stream_stage_bytes(shape, a.stage_experts), dtype=torch.uint8,
+                                device=dev)
+            ws = torch.empty(qm.moe_workspace_size(shape, T) + 8 * cfg.E + 512, dtype=torch.uint8,
+                             device=dev)
+
+            cstream = torch.cuda.Stream(device=dev) if a.copy_stream else None
+
+            def step():
+                qm.moe_layer_forward_streamed(shape, x, li.w_router, li.router_bias, sx, stage,
+                                              out=out, ws=ws, copy_stream=cstream)
+        elif tiers:
             from synth.mixed import make_mixed_layer
             # widths by how many rows each expert receives in this batch
             shape = qm.shape_of(cfg)
@@ -368,7 +401,7 @@ def main():
         if n:
             # microseconds per launch (per step: a mixed-width layer launches
             # each expert GEMM once per width)
-            kernels[name] = round(tot / (a.steps if tiers else n) * 1000.0, 2)
+            kernels[name] = round(tot / (a.steps if (tiers or streamed) else n) * 1000.0, 2)
     qm.profile_enable(0)
 
     # the work of one layer application over n rows
@@ -421,7 +454,8 @@ def main():
             "frac": round(achieved / peak, 4) if achieved else None,
             "traffic": ((GATEUP_I8_TRAFFIC.get(gemm_source_hash(I8_SOURCES)) if i8
                          else GATEUP_TRAFFIC.get(gemm_source_hash()))
-                        if (cfg.name, T) == ("a3b_pp8192", 8192) and not tiers else None),
+                        if (cfg.name, T) == ("a3b_pp8192", 8192) and not (tiers or streamed)
+                        else None),
             "flops_per_launch": gu_flops,
         }
 
@@ -450,7 +484,9 @@ def main():
             "group": cfg.G, "quant": cfg.quant, "shared_inter": cfg.shared_I,
             "layers": cfg.n_layers,
             "route": ("int8 activations" if i8 else
-                      ("fp16, mixed widths " + a.tiers if tiers else "fp16")),
+                      ("fp16, mixed widths " + a.tiers if tiers else
+                       (f"fp16, {cfg.E - a.stream_hot} experts streamed from host memory, "
+                        f"{a.stream_hot} on the GPU" if streamed else "fp16"))),
         },
         "layer_tflops": round(layer_tflops, 1),
         "layer_mfma_frac": round(layer_tflops / peak, 4),
@@ -462,6 +498,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if streamed:
+        cb = sx.cold_bytes()
+        rec["streamed"] = {"cold_experts": sx.n_cold, "cold_bytes": cb,
+                           "pcie_gbs": round(cb / (ms * 1e-3) / 1e9, 2),
+                           "note": ("host->device copies on a second stream, overlapping the "
+                                    "kernels" if a.copy_stream else
+                                    "host->device copies and kernels ordered on one stream")}
     if cold:
         rec["timing"] = ("median of K steps timed one by one, the Infinity Cache evicted "
                          "(1 GiB of other data read) before each; kernel_us likewise")

@@ -304,10 +304,16 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t *shape, int64_t T, const 
  * host memory (pinned, hipHostMalloc, for asynchronous copies); every call
  * copies the cold experts, as many at a time as half of `stage` holds, into
  * the device staging buffer and runs them through the same grouped GEMMs
- * (symmetric 4-bit experts, no shared expert). Copies and kernels are
- * ordered on `stream`, so the time is the copy time plus the compute time;
- * the result is bit-identical to moe_layer_forward with every expert on the
- * device.
+ * (symmetric 4-bit experts, no shared expert). With copy_stream NULL the
+ * copies are ordered on `stream` with the kernels (time = copies +
+ * compute); with another stream they run there, ordered by events (the
+ * library creates and releases them in the call): they start once the work
+ * `stream` held at entry is done, run at most two chunks ahead of the
+ * kernels, and every kernel that reads a chunk waits for its copies, so they
+ * overlap the routing, the hot experts and the previous chunk's compute.
+ * When the call returns, work queued later on `stream` is ordered after
+ * every copy. The result is bit-identical to moe_layer_forward with
+ * every expert on the device.
  *   hot        device experts, hot_count of them (hot may be NULL iff hot_count == 0)
  *   cold       host experts: the cold ones in ascending expert index, same
  *              layouts as moe_experts_t ([E_cold][...]); min and shared-expert
@@ -323,7 +329,8 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t *shape, int64_t T, con
                                         const moe_experts_t *cold, const int32_t *hot_slot,
                                         void *stage, size_t stage_bytes,
                                         const uint16_t *residual, uint16_t *out, void *ws,
-                                        size_t ws_bytes, hipStream_t stream);
+                                        size_t ws_bytes, hipStream_t stream,
+                                        hipStream_t copy_stream);
 
 /* RMSNorm over rows of [T][H] bf16:
  *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )

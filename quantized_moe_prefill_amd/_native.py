@@ -133,7 +133,7 @@ def lib():
     L.moe_stream_stage_bytes.argtypes = [sp, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_layer_forward_streamed.restype = st
     L.moe_layer_forward_streamed.argtypes = [sp, i64, P, P, P, ep, i32, ep, P, P, ctypes.c_size_t,
-                                             P, P, P, ctypes.c_size_t, P]
+                                             P, P, P, ctypes.c_size_t, P, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

@@ -920,7 +920,8 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
                                         const moe_experts_t* cold, const int32_t* hot_slot,
                                         void* stage, size_t stage_bytes,
                                         const uint16_t* residual, uint16_t* out, void* ws,
-                                        size_t ws_bytes, hipStream_t stream) {
+                                        size_t ws_bytes, hipStream_t stream,
+                                        hipStream_t copy_stream) {
   Shape s;
   moe_status_t st = check_shape(shape, T, &s);
   if (st != MOE_OK) return st;
@@ -990,6 +991,32 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
   auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
   auto* dgroup = reinterpret_cast<int32_t*>(b + maps_off);
   auto* dslot = dgroup + s.E;
+  // Copies on a stream of their own: the first two chunks' copies wait for
+  // what `stream` held at entry (a previous call's kernels may still read the
+  // staging slots), chunk j's copies for the kernels of chunk j-2 (the last
+  // user of the same slot), and chunk j's kernels for chunk j's copies.
+  const bool overlap = copy_stream != nullptr && copy_stream != stream && n_cold > 0;
+  const int n_chunks = cap > 0 ? (n_cold + cap - 1) / cap : 0;
+  std::vector<hipEvent_t> ready, freed;
+  hipEvent_t entry = nullptr;
+  struct EventGuard {
+    std::vector<hipEvent_t>* v[2];
+    hipEvent_t* one;
+    ~EventGuard() {
+      for (auto* vec : v)
+        for (hipEvent_t e : *vec) (void)hipEventDestroy(e);
+      if (*one != nullptr) (void)hipEventDestroy(*one);
+    }
+  } guard{{&ready, &freed}, &entry};
+  if (overlap) {
+    QMOE_HIP(hipEventCreateWithFlags(&entry, hipEventDisableTiming), "event create");
+    for (int j = 0; j < n_chunks + 2; ++j) {
+      hipEvent_t e;
+      QMOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "event create");
+      (j < n_chunks ? ready : freed).push_back(e);
+    }
+    QMOE_HIP(hipEventRecord(entry, stream), "event record");
+  }
   QMOE_HIP(launch_write_maps(maps, s.E, dgroup, dslot, stream), "maps launch");
   if (router_uses_gemv((int)T)) {
     QMOE_HIP(launch_route_permute_small(x, w_router, nullptr, partial, router_bias, (int)T, s.H,
@@ -1047,6 +1074,7 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
     if (st != MOE_OK) return st;
   }
   const size_t slot_bytes = stage_slot_bytes(SL, cap);
+  hipStream_t cs = overlap ? copy_stream : stream;
   for (int c0 = 0, j = 0; c0 < n_cold; c0 += cap, ++j) {
     const int n = std::min(cap, n_cold - c0);
     uint8_t* base = static_cast<uint8_t*>(stage) + (size_t)(j & 1) * slot_bytes;
@@ -1054,20 +1082,26 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
     uint8_t* s13 = w13 + al(SL.w13 * cap);
     uint8_t* w2 = s13 + al(SL.s13 * cap);
     uint8_t* s2 = w2 + al(SL.w2 * cap);
+    if (overlap) QMOE_HIP(hipStreamWaitEvent(cs, j < 2 ? entry : freed[j & 1], 0), "stream wait");
     // the chunk's experts are consecutive in the cold tensors
-    QMOE_HIP(hipMemcpyAsync(w13, cold->w13 + SL.w13 * c0, SL.w13 * n, hipMemcpyHostToDevice, stream),
+    QMOE_HIP(hipMemcpyAsync(w13, cold->w13 + SL.w13 * c0, SL.w13 * n, hipMemcpyHostToDevice, cs),
              "expert copy");
     QMOE_HIP(hipMemcpyAsync(s13, reinterpret_cast<const uint8_t*>(cold->w13_scale) + SL.s13 * c0,
-                            SL.s13 * n, hipMemcpyHostToDevice, stream),
+                            SL.s13 * n, hipMemcpyHostToDevice, cs),
              "expert copy");
-    QMOE_HIP(hipMemcpyAsync(w2, cold->w2 + SL.w2 * c0, SL.w2 * n, hipMemcpyHostToDevice, stream),
+    QMOE_HIP(hipMemcpyAsync(w2, cold->w2 + SL.w2 * c0, SL.w2 * n, hipMemcpyHostToDevice, cs),
              "expert copy");
     QMOE_HIP(hipMemcpyAsync(s2, reinterpret_cast<const uint8_t*>(cold->w2_scale) + SL.s2 * c0,
-                            SL.s2 * n, hipMemcpyHostToDevice, stream),
+                            SL.s2 * n, hipMemcpyHostToDevice, cs),
              "expert copy");
+    if (overlap) {
+      QMOE_HIP(hipEventRecord(ready[j], cs), "event record");
+      QMOE_HIP(hipStreamWaitEvent(stream, ready[j], 0), "stream wait");
+    }
     st = run_group(1 + j, cap, w13, reinterpret_cast<const uint16_t*>(s13), w2,
                    reinterpret_cast<const uint16_t*>(s2));
     if (st != MOE_OK) return st;
+    if (overlap) QMOE_HIP(hipEventRecord(freed[j & 1], stream), "event record");
   }
   QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");

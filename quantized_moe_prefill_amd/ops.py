@@ -315,7 +315,9 @@ def moe_stream_stage_bytes(shape, experts: int) -> int:
 
 
 def moe_layer_forward_streamed(shape, x, w_router, router_bias, experts: StreamedExperts, stage,
-                               residual=None, out=None, ws=None):
+                               residual=None, out=None, ws=None, copy_stream=None):
+    """copy_stream: a torch.cuda.Stream for the host->device copies (they then
+    overlap the kernels), or None to order them on the current stream."""
     T = x.shape[0]
     dev = x.device
     if out is None:
@@ -330,7 +332,7 @@ def moe_layer_forward_streamed(shape, x, w_router, router_bias, experts: Streame
         ctypes.byref(experts.cold) if experts.cold is not None else None, experts.hot_slot,
         _ptr(stage, "stage"), stage.numel() if stage is not None else 0,
         _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _ptr(ws, "ws"),
-        ws.numel(), _stream(dev)))
+        ws.numel(), _stream(dev), copy_stream.cuda_stream if copy_stream is not None else None))
     return out
 
 

@@ -243,7 +243,7 @@ def test_streamed_validation_before_launch():
     def call(shape=s, hot_count=0, hot_slot=slots, stage_bytes=1 << 30, ws_bytes=need + 4096):
         return L.moe_layer_forward_streamed(ctypes.byref(shape), 4, FAKE, FAKE, None, None, hot_count,
                                             ctypes.byref(cold), hot_slot, FAKE, stage_bytes, None, FAKE,
-                                            FAKE, ws_bytes, None)
+                                            FAKE, ws_bytes, None, None)
     assert call(shape=_shape(quant=1)) == N.MOE_ERR_UNSUPPORTED
     assert call(hot_slot=None) == N.MOE_ERR_INVALID_ARGUMENT
     assert call(stage_bytes=per) == N.MOE_ERR_WORKSPACE_TOO_SMALL     # not two experts

@@ -19,13 +19,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run(cfg, hot, stage_experts, T=None):
+def run(cfg, hot, stage_experts, T=None, copy_stream=None):
     li = make_layer(cfg, device=DEV)
     x = make_tokens(cfg, device=DEV, rows=T)
     shape = qm.shape_of(cfg)
     ex = qm.StreamedExperts(li, hot, DEV)
     stage = torch.empty(qm.moe_stream_stage_bytes(shape, stage_experts), dtype=torch.uint8, device=DEV)
-    out = qm.moe_layer_forward_streamed(shape, x, li.w_router, li.router_bias, ex, stage)
+    out = qm.moe_layer_forward_streamed(shape, x, li.w_router, li.router_bias, ex, stage,
+                                        copy_stream=copy_stream)
     ref = qm.MoELayer(cfg, li, DEV, x.shape[0]).forward(x)
     torch.cuda.synchronize()
     return li, x, out, ref
@@ -59,3 +60,31 @@ def test_streamed_small_T_against_oracle(T):
     ref = oracle.moe_layer(bits(x), li.to("cpu"), cfg.k, cfg.G, cfg.quant,
                            logits32=logits.cpu().numpy())
     gate(f64_of_bf16(out), ref["out"], f"out (streamed, T={T})")
+
+
+@pytest.mark.parametrize("name,hot,stage_experts", [
+    ("tiny", [], 2),
+    ("a3b_pp512", list(range(0, 128, 4)), 16),
+])
+def test_streamed_copy_stream_bitwise(name, hot, stage_experts):
+    """Copies on a second stream, three calls back to back into the same
+    staging buffer (a later call's first copies must wait for the earlier
+    call's last kernels), each bit-identical to the resident layer."""
+    cfg = CONFIGS[name]
+    cs = torch.cuda.Stream(device=DEV)
+    li = make_layer(cfg, device=DEV)
+    shape = qm.shape_of(cfg)
+    ex = qm.StreamedExperts(li, hot, DEV)
+    stage = torch.empty(qm.moe_stream_stage_bytes(shape, stage_experts), dtype=torch.uint8, device=DEV)
+    outs, refs = [], []
+    for i in range(3):
+        x = make_tokens(replace(cfg, seed=cfg.seed + i), device=DEV)
+        outs.append(qm.moe_layer_forward_streamed(shape, x, li.w_router, li.router_bias, ex, stage,
+                                                  copy_stream=cs))
+        refs.append(x)
+    torch.cuda.synchronize()
+    layer = qm.MoELayer(cfg, li, DEV, refs[0].shape[0])
+    for i, (out, x) in enumerate(zip(outs, refs)):
+        ref = layer.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"call {i}"
