@@ -161,6 +161,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
   constexpr bool SCL = SCM == SC_TILE;
   constexpr bool WIN = SCM == SC_WINDOW;
+  // each stage dequantizes the next stage's first K step (symmetric experts:
+  // with a min per group the extra live registers spill)
+  constexpr bool XDQ = !ASYM;
   // a lane's packed weights of one fragment and stage: 4 * BITS bytes
   typedef uint32_t WV __attribute__((ext_vector_type(BITS)));
   __shared__ __attribute__((aligned(16))) uint8_t Sc[SCM != SC_STAGE ? NWAVES * SC_WAVE : 16];
@@ -408,7 +411,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // (C^T = W A^T), so each lane ends up with four consecutive output
   // columns of one row.
   auto compute_stage = [&](const uint8_t* __restrict__ as_base, const WV* cb, const uint32_t* rs,
-                           const uint32_t* rm) {
+                           const uint32_t* rm, f16x8* b, const WV* cbn, uint32_t* rsn,
+                           uint32_t* rmn, int kt) {
     f16x2 cs[NFRAG], cm[NFRAG];
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
@@ -421,14 +425,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     auto read_a = [&](int j, int mi) {
       return __builtin_bit_cast(f16x8, ld16(ap[j] + mi * 16 * BK * 2));
     };
-    // weights of step 0 now; those of step j+1 are dequantized while step
-    // j's MFMAs run (one fragment behind each of the first sub-tiles)
-    f16x8 b[NFRAG];
+    // The weights of step j+1 are dequantized while step j's MFMAs run (one
+    // fragment behind each of the first sub-tiles). With XDQ, step 0's come
+    // in dequantized (by the previous stage, or before a tile's first stage)
+    // and step 3 dequantizes the next stage's step 0, so that no stage
+    // starts with a run of dequant work that no MFMA overlaps (the two waves
+    // of a SIMD leave the stage barrier together).
+    if (!XDQ) {
 #pragma unroll
-    for (int f = 0; f < NFRAG; ++f) b[f] = dequant_chunk(cb[f], 0, cs[f], cm[f]);
+      for (int f = 0; f < NFRAG; ++f) b[f] = dequant_chunk(cb[f], 0, cs[f], cm[f]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x8 bn[NFRAG];
+      f16x2 csn[NFRAG], cmn[NFRAG];
+      if (XDQ && j == 3) {
+        if (WIN) {
+          // the window refilled in this stage has landed
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
+          read_win(kt + 1, rsn, rmn);
+        }
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) {
+          csn[f] = __builtin_bit_cast(f16x2, rsn[f] * 0x10001u);
+          cmn[f] = __builtin_bit_cast(f16x2, rmn[f] * 0x10001u);
+        }
+      }
       f16x8 a = read_a(j, 0);
 #pragma unroll
       for (int mi = 0; mi < MSUB; ++mi) {
@@ -438,10 +460,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         for (int f = 0; f < NFRAG; ++f)
           acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
                               : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
-        if (j < 3 && mi < NFRAG) bn[mi] = dequant_chunk(cb[mi], j + 1, cs[mi], cm[mi]);
+        if (mi < NFRAG) {
+          if (j < 3) bn[mi] = dequant_chunk(cb[mi], j + 1, cs[mi], cm[mi]);
+          else if (XDQ) bn[mi] = dequant_chunk(cbn[mi], 0, csn[mi], cmn[mi]);
+        }
         if (mi + 1 < MSUB) a = an;
       }
-      if (j < 3) {
+      if (j < 3 || XDQ) {
 #pragma unroll
         for (int f = 0; f < NFRAG; ++f) b[f] = bn[f];
       }
@@ -537,6 +562,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   setup(tile, cur);
   WV cb[NFRAG];
   uint32_t rs[NFRAG], rm[NFRAG];
+  f16x8 b0[NFRAG];  // dequantized weights of a stage's first K step
   load_sc(cur);
   load_b(cur, 0, cb, rs, rm);
   load_a(cur, 0, As0);
@@ -547,6 +573,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
     if (SCL) read_sc(sc_wave, 0, rs, rm);
     if (WIN) read_win(0, rs, rm);
+    if (XDQ) {
+      // the tile's first step
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f)
+        b0[f] = dequant_chunk(cb[f], 0, __builtin_bit_cast(f16x2, rs[f] * 0x10001u),
+                              __builtin_bit_cast(f16x2, rm[f] * 0x10001u));
+    }
 #pragma unroll
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
@@ -565,11 +598,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       // itself the scheduler sinks them to the end of the stage (to shorten
       // register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
-      compute_stage(curs, cb, rs, rm);
-      if (SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
+      if (XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
+      compute_stage(curs, cb, rs, rm, b0, cbn, rsn, rmn, kt);
+      if (!XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       // (after the wait: a window refilled in this stage has landed)
-      if (WIN) read_win(kt + 1, rsn, rmn);
+      if (!XDQ && WIN) read_win(kt + 1, rsn, rmn);
       lds_barrier();
       // the hand-over of the next stage's registers stays here: moved up into
       // the stage it would wait for loads that were just issued
