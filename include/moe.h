@@ -298,9 +298,10 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t *shape, int64_t T, const 
  * The pages run models whose experts do not all fit the GPU: experts stay in
  * host memory and are streamed over PCIe during prefill, with a set of hot
  * experts kept resident, and long prompts become limited by that stream
- * (hipfire 0.4.3 benchmarks page, the Flash-Next rows: "mq2 host experts"
- * on a narrow PCIe link; the 4096-row chunk limited by the PCIe expert
- * stream). Here: the hot experts are device tensors, the others (cold) sit in
+ * (hipfire 0.4.3 benchmarks page, the Flash-Next rows: 2-bit experts held
+ * in host memory behind a narrow PCIe link, and the note that a 4096-row
+ * prefill chunk is bound by the expert transfers over PCIe). Here: the hot
+ * experts are device tensors, the others (cold) sit in
  * host memory (pinned, hipHostMalloc, for asynchronous copies); every call
  * copies the cold experts, as many at a time as half of `stage` holds, into
  * the device staging buffer and runs them through the same grouped GEMMs
@@ -314,6 +315,9 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t *shape, int64_t T, const 
  * When the call returns, work queued later on `stream` is ordered after
  * every copy. The result is bit-identical to moe_layer_forward with
  * every expert on the device.
+ * Ownership: the caller keeps the cold host memory, `stage`, `ws` and `out`
+ * alive and unchanged until the work the call queued (on both streams) has
+ * completed; two calls in flight at once that share `stage` or `ws` race.
  *   hot        device experts, hot_count of them (hot may be NULL iff hot_count == 0)
  *   cold       host experts: the cold ones in ascending expert index, same
  *              layouts as moe_experts_t ([E_cold][...]); min and shared-expert

@@ -317,7 +317,11 @@ def moe_stream_stage_bytes(shape, experts: int) -> int:
 def moe_layer_forward_streamed(shape, x, w_router, router_bias, experts: StreamedExperts, stage,
                                residual=None, out=None, ws=None, copy_stream=None):
     """copy_stream: a torch.cuda.Stream for the host->device copies (they then
-    overlap the kernels), or None to order them on the current stream."""
+    overlap the kernels), or None to order them on the current stream.
+
+    The copies read `experts`' pinned host tensors asynchronously, outside
+    torch's pinned-memory bookkeeping: keep `experts` and `stage` alive until
+    the current stream has finished this call."""
     T = x.shape[0]
     dev = x.device
     if out is None:
