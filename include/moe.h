@@ -39,7 +39,13 @@
  *    hidden H % 128 == 0, 128 <= H <= 16384;  1 <= E <= 256;  1 <= k <= min(E, 8);
  *    group_size G in {32, 64, 128};  inter I % 128 == 0;
  *    shared_inter == 0 or shared_inter % 128 == 0;
- *    T * k < 2^31;  T * H and T * k * I below 2^34.
+ *    T * k < 2^31;  the kernels address tensors through 32-bit buffer
+ *    descriptors, so each of these must be below 2^31 bytes:
+ *      activations  x, x16: T*H*2;  h: T*k*I*2;  h_shared: T*Is*2
+ *                   (174,762 tokens per call at H = 2048, k = 8, I = 768:
+ *                   longer prompts go through in chunks);
+ *      experts      w13: E*2I*H/2;  w2: E*H*I/2;  their scales (and mins):
+ *                   E*2I*(H/G)*2 and E*H*(I/G)*2.
  */
 #ifndef QMOE_MOE_H
 #define QMOE_MOE_H

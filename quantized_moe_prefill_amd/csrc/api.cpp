@@ -99,10 +99,19 @@ static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
     return fail(MOE_ERR_UNSUPPORTED, "shared_inter must be 0 or a multiple of 128");
   if (s->num_experts > 256) return fail(MOE_ERR_UNSUPPORTED, "num_experts must be <= 256");
   if (s->top_k > 8) return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= 8");
-  if (T * s->top_k >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "T * top_k must be < 2^31");
-  if (T * s->hidden / 8 >= (int64_t(1) << 31) || T * s->top_k * s->inter / 8 >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "activation tensors must hold fewer than 2^34 elements");
+  // The GEMM kernels address each activation, weight, scale and min tensor
+  // through a 32-bit buffer descriptor with offsets computed in int: every
+  // such tensor must stay below 2^31 bytes.
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t E = s->num_experts, H = s->hidden, I = s->inter, Is = s->shared_inter;
+  if (T * s->top_k >= lim) return fail(MOE_ERR_UNSUPPORTED, "T * top_k must be < 2^31");
+  if (T * H * 2 >= lim || T * s->top_k * I * 2 >= lim || T * Is * 2 >= lim)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "activation tensors (x, h, h_shared) must be below 2^31 bytes; "
+                "split the tokens into chunks");
+  if (E * 2 * I * (H / 2) >= lim || E * H * (I / 2) >= lim || E * 2 * I * (H / G) * 2 >= lim ||
+      E * H * (I / G) * 2 >= lim)
+    return fail(MOE_ERR_UNSUPPORTED, "expert weight tensors must be below 2^31 bytes");
   out->H = (int)s->hidden;
   out->E = (int)s->num_experts;
   out->k = (int)s->top_k;

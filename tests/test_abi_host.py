@@ -96,6 +96,23 @@ def test_negative_T_and_null_shape():
     assert L.moe_workspace_size(ctypes.byref(_shape()), (1 << 31) // 8, 0, ctypes.byref(n)) == N.MOE_ERR_UNSUPPORTED
 
 
+def test_32bit_descriptor_limits():
+    """Every tensor a GEMM reaches through a 32-bit buffer descriptor stays
+    below 2^31 bytes: the largest T whose h (T*k*I*2 bytes) fits passes, the
+    next one is refused; so are expert tensors of 2^31 bytes or more."""
+    L = _lib()
+    n = ctypes.c_size_t(0)
+    s = _shape()  # H = 2048, E = 128, k = 8, I = 768
+    t_max = ((1 << 31) - 1) // (8 * 768 * 2)  # h (T*k*I*2) is the largest descriptor-addressed activation
+    assert L.moe_workspace_size(ctypes.byref(s), t_max, 0, ctypes.byref(n)) == N.MOE_OK
+    assert L.moe_workspace_size(ctypes.byref(s), t_max + 1, 0, ctypes.byref(n)) == N.MOE_ERR_UNSUPPORTED
+    # w13 = E * 2I * H / 2 bytes: 256 * 4096 * 2048 = 2^31
+    big = _shape(num_experts=256, inter=2048, hidden=4096)
+    assert L.moe_workspace_size(ctypes.byref(big), 16, 0, ctypes.byref(n)) == N.MOE_ERR_UNSUPPORTED
+    ok = _shape(num_experts=128, inter=2048, hidden=4096)
+    assert L.moe_workspace_size(ctypes.byref(ok), 16, 0, ctypes.byref(n)) == N.MOE_OK
+
+
 FAKE = 0x10000  # an aligned non-null address that is never dereferenced
 
 
