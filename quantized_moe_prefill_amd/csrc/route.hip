@@ -30,7 +30,7 @@ namespace qmoe {
 namespace {
 
 constexpr int RBM = 128;   // tokens per GEMM tile
-constexpr int RBN = 256;   // output columns (split rows) per tile
+constexpr int RBN = 192;   // output columns (split rows) per tile: 3 x 128 experts = 2 tiles
 constexpr int RBK = 64;    // K per stage
 constexpr int RSTAGES = 3;
 constexpr int RTHREADS = 512;
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Bs[RSTAGES][RBN][RBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 x 64 each
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 x 48 each
   const int r16 = lane & 15, lg = lane >> 4;
 
   int b = blockIdx.x;
@@ -85,11 +85,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   const int kbeg = ks * klen;
   const int nst = klen / RBK;
 
-  // direct loads: A 128 rows = 16 loads of 8 rows, B 256 rows = 32 loads;
-  // wave w issues A loads 2w, 2w+1 and B loads 4w .. 4w+3 each stage
+  // direct loads: A 128 rows = 16 loads of 8 rows, B 192 rows = 24 loads;
+  // wave w issues A loads 2w, 2w+1 and B loads 3w .. 3w+2 each stage
   const int lrow = lane >> 3, lslot = lane & 7;
   const uint16_t* a_src[2];
-  const uint16_t* b_src[4];
+  const uint16_t* b_src[3];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (2 * wave + i) * 8 + lrow;
@@ -97,8 +97,8 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
     a_src[i] = x + (int64_t)t * H + kbeg + 8 * (lslot ^ (r & 7));
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (4 * wave + i) * 8 + lrow;
+  for (int i = 0; i < 3; ++i) {
+    const int r = (3 * wave + i) * 8 + lrow;
     const int n = min(col0 + r, N - 1);
     b_src[i] = w + (int64_t)n * H + kbeg + 8 * (lslot ^ (r & 7));
   }
@@ -109,24 +109,24 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
       __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[i] + k0),
                                        (lds_void_t*)&As[buf][(2 * wave + i) * 8][0], 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 3; ++i)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[i] + k0),
-                                       (lds_void_t*)&Bs[buf][(4 * wave + i) * 8][0], 16, 0, 0);
+                                       (lds_void_t*)&Bs[buf][(3 * wave + i) * 8][0], 16, 0, 0);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][3];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 3; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // three-stage ring: stages s+1 and s+2 are in flight while s is computed;
-  // each stage is six direct loads per wave, so "at most 6 outstanding"
+  // each stage is five direct loads per wave, so "at most 5 outstanding"
   // means stage s+1 has landed
   load_stage(0, 0);
   if (nst > 1) load_stage(1, 1);
   if (nst > 1)
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -135,21 +135,24 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
     if (s + 2 < nst) load_stage(s + 2, (s + 2) % RSTAGES);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      bf16x8 a[4], bb[4];
+      bf16x8 a[4], bb[3];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = wm * 64 + i * 16 + r16;
         a[i] = __builtin_bit_cast(bf16x8, ld16(&As[buf][ra][((j * 4 + lg) ^ (ra & 7)) * 8]));
-        const int rb = wn * 64 + i * 16 + r16;
+      }
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int rb = wn * 48 + i * 16 + r16;
         bb[i] = __builtin_bit_cast(bf16x8, ld16(&Bs[buf][rb][((j * 4 + lg) ^ (rb & 7)) * 8]));
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_16x16x32(a[mi], bb[ni], acc[mi][ni]);
+        for (int ni = 0; ni < 3; ++ni) acc[mi][ni] = mfma_16x16x32(a[mi], bb[ni], acc[mi][ni]);
     }
     if (s + 2 < nst)
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -159,8 +162,8 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int col = col0 + wn * 64 + ni * 16 + r16;
+    for (int ni = 0; ni < 3; ++ni) {
+      const int col = col0 + wn * 48 + ni * 16 + r16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row0 + wm * 64 + mi * 16 + 4 * lg + v;

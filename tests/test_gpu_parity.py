@@ -204,6 +204,34 @@ def test_full_size_a3b_pp8192_sampled():
     gate(f64_of_bf16(out)[rows], ref["out"], "out rows")
 
 
+def test_max_T_sampled():
+    """The largest call the size limits allow at the a3b_pp8192 shape:
+    174,762 tokens, whose h (T*k*I*2 bytes) is just below 2^31, so the
+    GEMMs' 32-bit buffer offsets run up to their limit. Routing and the
+    permutation bit-exact, sampled output rows (the first, the last, and
+    rows near the end) against the oracle, teacher-forced on the GPU logits."""
+    T = ((1 << 31) - 1) // (8 * 768 * 2)
+    cfg = replace(CONFIGS["a3b_pp8192"], T=T)
+    li = make_layer(cfg, device=DEV)
+    x = make_tokens(cfg, device=DEV)
+    shape = qm.shape_of(cfg)
+    out = qm.MoELayer(cfg, li, DEV, T).forward(x)
+    logits, ids, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None, want_logits=True)
+    counts, offsets, sp, inv = qm.moe_permute(shape, ids)
+    torch.cuda.synchronize()
+    L = logits.cpu().numpy()
+    ids_ref, _ = oracle.select_topk(L, cfg.k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    c, o, s, i = oracle.permute(ids_ref, cfg.E)
+    assert np.array_equal(counts.cpu().numpy(), c) and np.array_equal(sp.cpu().numpy(), s)
+    assert np.array_equal(inv.cpu().numpy(), i) and np.array_equal(offsets.cpu().numpy(), o)
+    rows = np.random.default_rng(1).choice(T, 24, replace=False)
+    rows = np.concatenate([rows, [0, T - 2, T - 1]])
+    cpu = li.to("cpu")
+    ref = oracle.moe_layer_rows(bits(x), rows, cpu, cfg.k, cfg.G, cfg.quant, logits32_rows=L[rows])
+    gate(f64_of_bf16(out)[rows], ref["out"], "out rows (max T)")
+
+
 def test_determinism_bitwise():
     cfg = CONFIGS["a3b_pp512"]
     li, cpu, x = setup(cfg)
