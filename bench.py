@@ -87,6 +87,8 @@ def parse():
                     help="expert route: fp16 matrix cores (default) or the integer route")
     ap.add_argument("--stream-hot", type=int, default=-1,
                     help="stream the experts from host memory, keeping this many on the GPU")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the bf16 matmul and copy ceilings measured after the timing")
     ap.add_argument("--copy-stream", action="store_true",
                     help="with --stream-hot: copy on a second stream, overlapping the kernels")
     ap.add_argument("--stage-experts", type=int, default=32,
@@ -181,17 +183,80 @@ def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False, mixed=Non
             oracle.moe_layer(xb, cpu, cfg.k, cfg.G, cfg.quant)
         dt += time.perf_counter() - t0
         passes += 1
+    gemm_only = None
+    if not i8 and mixed is None:
+        # the same oracle with every expert's dequantized matrices prepared
+        # before the clock starts: route, permute, the experts' products and
+        # the combine (median of 3 passes)
+        mo = oracle.moe_oracle
+        w = mo._weights_dict(cpu)
+        mats = {e: mo._expert_mats(w, e, cfg.G, cfg.quant) for e in range(cfg.E)}
+        shared = (mo._expert_mats(w, None, cfg.G, cfg.quant, prefix="s")
+                  if w["s13"] is not None else None)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            xf = oracle.bf16_to_f64(xb)
+            L = mo.router_logits(xf, w["w_router"], w["router_bias"])
+            ids, tw = oracle.select_topk(L.astype(np.float32), cfg.k)
+            counts, offsets, sp, inv = oracle.permute(ids, cfg.E)
+            y_perm = np.zeros((len(sp), cfg.H))
+            for e in range(cfg.E):
+                lo, hi = int(offsets[e]), int(offsets[e + 1])
+                if lo < hi:
+                    y_perm[lo:hi] = mo.swiglu_expert(xf[np.asarray(sp[lo:hi]) // cfg.k], *mats[e])[1]
+            ys = sw = None
+            if shared is not None:
+                sw = mo.shared_gate(xf, w["shared_gate"])
+                ys = mo.swiglu_expert(xf, *shared)[1]
+            mo.combine(y_perm, inv, tw, ys, sw, None)
+            times.append(time.perf_counter() - t0)
+        t_med = sorted(times)[1]
+        gemm_only = {"value": round(x.shape[0] / t_med, 2), "unit": "tokens/s",
+                     "sample": "the whole batch with the experts' dequantized fp64 matrices "
+                               f"prepared beforehand, median of 3 passes ({t_med:.2f} s)"}
     return {
         "value": round(passes * x.shape[0] / dt, 2),
         "unit": "tokens/s",
         "cores": blas_threads or cores,
         "kind": "oracle",
+        "gemm_only": gemm_only,
         "sample": f"the whole {x.shape[0]}-token batch, {passes} passes of the float64 numpy "
                   f"oracle{' (integer route)' if i8 else (' (mixed widths)' if mixed else '')} "
                   f"(dequantize all experts + route + "
                   f"experts + combine), {dt:.1f} s in "
-                  f"total; {cores} cores visible, BLAS threads {blas_threads}",
+                  f"total; {cores} cores in the affinity mask (os.cpu_count() "
+                  f"{os.cpu_count()}), BLAS threads {blas_threads}",
     }
+
+
+def ceilings(dev):
+    """Achievable rates on this machine, as context for the roofline fractions: a
+    large bf16 matrix product (torch/hipBLASLt) and a 1 GiB device copy."""
+    import torch
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    src = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_mm = rate(lambda: torch.matmul(a, b, out=c), 20)
+    t_cp = rate(lambda: dst.copy_(src), 20)
+    return {"bf16_matmul_8192_tflops": round(2.0 * n ** 3 / t_mm / 1e12, 1),
+            "copy_1gib_gbs": round(2.0 * src.numel() * 4 / t_cp / 1e9, 1)}
 
 
 def stack_cpu_baseline(cfg, layers_cpu, x, rows=32, layers=2):
@@ -386,6 +451,20 @@ def main():
             times.append(e0.elapsed_time(e1))
         graph_ms = sorted(times)[len(times) // 2]
 
+    # the spread of single steps: K more steps, an event between consecutive
+    # ones (no synchronization inside the loop)
+    step_pct = None
+    if not cold:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+        evs[0].record(st)
+        for i in range(a.steps):
+            step()
+            evs[i + 1].record(st)
+        torch.cuda.synchronize()
+        d = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps))
+        q = lambda f: d[min(len(d) - 1, int(f * len(d)))]
+        step_pct = [round(q(0.1), 4), round(q(0.5), 4), round(q(0.9), 4)]
+
     # per-kernel durations: the same K steps again with HIP events around
     # every kernel launch (recorded on the launch stream by the library)
     launches_per_step = 16 * max(1, cfg.n_layers) * max(1, -(-T // (cfg.chunk or T)))
@@ -495,6 +574,8 @@ def main():
         "layer_hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4),
         "kernel_us": kernels,
         "wall_s_timed": round(t_wall, 3),
+        "step_ms_p10_p50_p90": step_pct,
+        "ceilings": ceilings(dev) if not a.no_ceilings else None,
         "roofline": roofline,
         "cpu_baseline": None,
     }
