@@ -267,11 +267,11 @@ static moe_status_t check_experts(const Shape& s, const moe_experts_t* w) {
 static moe_status_t route_impl(const Shape& s, int64_t T, const uint16_t* x, const float* wr,
                                const float* bias, const float* sg, float* logits,
                                int32_t* ids, float* tw, float* sw, uint16_t* split,
-                               float* partial, hipStream_t st) {
+                               float* partial, uint16_t* x16, hipStream_t st) {
   if (!router_uses_gemv((int)T))
     QMOE_HIP(launch_router_split(wr, sg, s.E, s.H, split, st), "router_split launch");
   QMOE_HIP(launch_router_topk(x, wr, sg, split, partial, bias, (int)T, s.H, s.E, s.k, logits, ids,
-                              tw, sw, st),
+                              tw, sw, x16, st),
            "router launch");
   return MOE_OK;
 }
@@ -280,7 +280,8 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
                              const moe_experts_t* w, const int32_t* counts,
                              const int32_t* offsets, const int32_t* sorted, uint16_t* yperm,
                              uint16_t* ysh, uint16_t* x16, uint16_t* h, uint16_t* hs,
-                             hipStream_t st) {
+                             bool x16_ready, hipStream_t st) {
+  // x16_ready: x16 already holds x in fp16 kperm order (written by the router GEMM)
   const int P = (int)(T * s.k);
   GroupedGemm g{};
   g.A = x16;
@@ -306,7 +307,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   if (x_direct) {
     g.A = x;
     g.a_bf16 = true;
-  } else {
+  } else if (!x16_ready) {
     QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
   }
   // A shared expert of the routed experts' shape runs as one more group of
@@ -372,7 +373,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
     gs.expect_rows = (int)T;
     if (!fold_gu) {
       if (gs.a_bf16 && !gemm_streams(gs, true)) {
-        QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+        if (!x16_ready) QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
         gs.A = x16;
         gs.a_bf16 = false;
       }
@@ -468,9 +469,9 @@ static moe_status_t ffn_mixed_impl(const Shape& s, int64_t T, const uint16_t* x,
                                    const int32_t* ebits, const int32_t* eslot,
                                    const int32_t* counts, const int32_t* offsets,
                                    const int32_t* sorted, uint16_t* yperm, uint16_t* x16,
-                                   uint16_t* h, hipStream_t st) {
+                                   uint16_t* h, bool x16_ready, hipStream_t st) {
   const int P = (int)(T * s.k);
-  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
+  if (!x16_ready) QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
   GroupedGemm g{};
   g.A = x16;
   g.gather = sorted;
@@ -596,7 +597,7 @@ moe_status_t moe_route(const moe_shape_t* shape, int64_t T, const uint16_t* x,
   return route_impl(s, T, x, w_router, router_bias, shared_gate, logits, topk_ids, topk_w,
                     shared_w, reinterpret_cast<uint16_t*>(wsb),
                     reinterpret_cast<float*>(wsb + al(router_split_bytes(s.E, sr.Is > 0, s.H))),
-                    stream);
+                    nullptr, stream);
 }
 
 moe_status_t moe_permute(const moe_shape_t* shape, int64_t T, const int32_t* topk_ids,
@@ -652,7 +653,7 @@ moe_status_t moe_expert_ffn(const moe_shape_t* shape, int64_t T, const uint16_t*
   uint16_t* h = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2));
   uint16_t* hs = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2) + al(P * s.I * 2));
   return ffn_impl(s, T, x, experts, counts, offsets, sorted_pairs, y_perm, y_shared, x16, h,
-                  hs, stream);
+                  hs, false, stream);
 }
 
 moe_status_t moe_combine(const moe_shape_t* shape, int64_t T, const uint16_t* y_perm,
@@ -726,12 +727,13 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
              "router launch");
   } else {
     st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
-                    partial, stream);
+                    partial, x16, stream);
     if (st != MOE_OK) return st;
     QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
              "permute launch");
   }
-  st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs, stream);
+  st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs,
+                !router_uses_gemv((int)T), stream);
   if (st != MOE_OK) return st;
   QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");
@@ -817,7 +819,7 @@ moe_status_t moe_layer_forward_i8(const moe_shape_t* shape, int64_t T, const uin
              "router launch");
   } else {
     st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
-                    partial, stream);
+                    partial, nullptr, stream);
     if (st != MOE_OK) return st;
     QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
              "permute launch");
@@ -854,7 +856,7 @@ moe_status_t moe_expert_ffn_mixed(const moe_shape_t* shape, int64_t T, const uin
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
   uint16_t* h = reinterpret_cast<uint16_t*>(base + al((size_t)T * s.H * 2));
   return ffn_mixed_impl(s, T, x, tiers, n_tiers, expert_bits, expert_slot, counts, offsets,
-                        sorted_pairs, y_perm, x16, h, stream);
+                        sorted_pairs, y_perm, x16, h, false, stream);
 }
 
 moe_status_t moe_layer_forward_mixed(const moe_shape_t* shape, int64_t T, const uint16_t* x,
@@ -899,13 +901,13 @@ moe_status_t moe_layer_forward_mixed(const moe_shape_t* shape, int64_t T, const 
              "router launch");
   } else {
     st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
-                    partial, stream);
+                    partial, x16, stream);
     if (st != MOE_OK) return st;
     QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
              "permute launch");
   }
   st = ffn_mixed_impl(s, T, x, tiers, n_tiers, expert_bits, expert_slot, counts, offsets, sorted,
-                      yperm, x16, h, stream);
+                      yperm, x16, h, !router_uses_gemv((int)T), stream);
   if (st != MOE_OK) return st;
   QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");
@@ -1034,12 +1036,14 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
              "router launch");
   } else {
     st = route_impl(s, T, x, w_router, router_bias, nullptr, nullptr, ids, tw, nullptr, split,
-                    partial, stream);
+                    partial, x16, stream);
     if (st != MOE_OK) return st;
     QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
              "permute launch");
   }
-  QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, stream), "x_to_f16 launch");
+  // (the router GEMM wrote x16 already; the matrix-vector router does not)
+  if (router_uses_gemv((int)T))
+    QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, stream), "x_to_f16 launch");
   const int P = (int)(T * s.k);
   GroupedGemm g{};
   g.A = x16;

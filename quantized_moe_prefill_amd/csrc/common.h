@@ -47,6 +47,17 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
+// Eight bf16 values (x0..x7, two per word) -> fp16 in kperm chunk order
+// (positions 0..7 hold x0, x4, x1, x5, x2, x6, x3, x7); exact for |x| < 65504.
+__device__ __forceinline__ u32x4 bf16x8_to_f16_kperm(u32x4 d) {
+  u32x4 o;
+  o[0] = pack_f16x2(bf16lo(d[0]), bf16lo(d[2]));  // x0, x4
+  o[1] = pack_f16x2(bf16hi(d[0]), bf16hi(d[2]));  // x1, x5
+  o[2] = pack_f16x2(bf16lo(d[1]), bf16lo(d[3]));  // x2, x6
+  o[3] = pack_f16x2(bf16hi(d[1]), bf16hi(d[3]));  // x3, x7
+  return o;
+}
+
 // D = A(16x32) * B(32x16) + C on the bf16 matrix cores, fp32 accumulation.
 // Operand layout per lane l: A row l%16 / B column l%16, eight consecutive K
 // values starting at 8*(l/16). Result: lane l holds rows 4*(l/16)+0..3 of

@@ -64,13 +64,7 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
                                                        int64_t n_chunks) {
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n_chunks;
        c += (int64_t)gridDim.x * 256) {
-    const u32x4 d = ld16(x + c * 8);  // (x0,x1) (x2,x3) (x4,x5) (x6,x7)
-    u32x4 o;
-    o[0] = pack_f16x2(bf16lo(d[0]), bf16lo(d[2]));  // x0, x4
-    o[1] = pack_f16x2(bf16hi(d[0]), bf16hi(d[2]));  // x1, x5
-    o[2] = pack_f16x2(bf16lo(d[1]), bf16lo(d[3]));  // x2, x6
-    o[3] = pack_f16x2(bf16hi(d[1]), bf16hi(d[3]));  // x3, x7
-    st16(out + c * 8, o);
+    st16(out + c * 8, bf16x8_to_f16_kperm(ld16(x + c * 8)));
   }
 }
 

@@ -31,11 +31,13 @@ hipError_t launch_router_split(const float* w_router, const float* shared_gate, 
 constexpr int kRouterGemvT = 16;
 bool router_uses_gemv(int T);
 // router GEMM (or matrix-vector product) into `partial`, then per-token
-// logits, top-k and softmax; `split` is only read when !router_uses_gemv(T)
+// logits, top-k and softmax; `split` is only read when !router_uses_gemv(T).
+// x16 (optional, GEMM path only): also written with x in fp16 kperm chunk
+// order, as launch_x_to_f16 would.
 hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const float* shared_gate,
                               const uint16_t* split, float* partial, const float* bias, int T,
                               int H, int E, int k, float* logits, int32_t* ids, float* topk_w,
-                              float* shared_w, hipStream_t s);
+                              float* shared_w, uint16_t* x16, hipStream_t s);
 
 // At most kRouterGemvT tokens: router logits, top-k and softmax, and the
 // grouping by expert (as launch_permute), in two launches.

@@ -32,7 +32,6 @@ namespace {
 constexpr int RBM = 128;   // tokens per GEMM tile
 constexpr int RBN = 192;   // output columns (split rows) per tile: 3 x 128 experts = 2 tiles
 constexpr int RBK = 64;    // K per stage
-constexpr int RSTAGES = 3;
 constexpr int RTHREADS = 512;
 
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
@@ -64,12 +63,22 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // Dense bf16 GEMM P = x * Wsplit^T over one K slice. LDS rows are 64 bf16
 // (128 B, eight 16-byte chunks); chunk c of row r sits in slot c ^ (r & 7),
 // which keeps the 16-row fragment reads conflict-free and lets one direct
-// load fill eight whole rows.
+// load fill eight whole rows. With x16 set, the workgroups of column tile 0
+// also write their rows' fp16 copy in kperm chunk order (the expert GEMMs'
+// operand, what x_to_f16 computes) from the tiles they stage anyway.
 __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ P,
-    int T, int H, int N, int n_mt, int n_nt, int ksplit) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[RSTAGES][RBM][RBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[RSTAGES][RBN][RBK];
+    uint16_t* __restrict__ x16, int T, int H, int N, int n_mt, int n_nt, int ksplit) {
+  // a three-slot ring in separate arrays, with the stage loop unrolled by
+  // three: the compiler then sees that a stage's LDS reads never touch the
+  // slot being filled, and does not wait for those loads before reading
+  __shared__ __attribute__((aligned(16))) uint16_t As0[RBM][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[RBM][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t As2[RBM][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[RBN][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[RBN][RBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs2[RBN][RBK];
+  typedef uint16_t ARow[RBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 x 48 each
@@ -87,32 +96,43 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
 
   // direct loads: A 128 rows = 16 loads of 8 rows, B 192 rows = 24 loads;
   // wave w issues A loads 2w, 2w+1 and B loads 3w .. 3w+2 each stage
+  // (buffer loads with 32-bit offsets: the host keeps x and the split
+  // matrix below 2^31 bytes)
+  const __amdgpu_buffer_rsrc_t rX =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, N * H * 2, kRsrcWord3);
   const int lrow = lane >> 3, lslot = lane & 7;
-  const uint16_t* a_src[2];
-  const uint16_t* b_src[3];
+  uint32_t a_off[2], b_off[3];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = (2 * wave + i) * 8 + lrow;
     const int t = min(row0 + r, T - 1);
-    a_src[i] = x + (int64_t)t * H + kbeg + 8 * (lslot ^ (r & 7));
+    a_off[i] = (uint32_t)(t * H + kbeg + 8 * (lslot ^ (r & 7))) * 2u;
   }
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int r = (3 * wave + i) * 8 + lrow;
     const int n = min(col0 + r, N - 1);
-    b_src[i] = w + (int64_t)n * H + kbeg + 8 * (lslot ^ (r & 7));
+    b_off[i] = (uint32_t)(n * H + kbeg + 8 * (lslot ^ (r & 7))) * 2u;
   }
-  auto load_stage = [&](int s, int buf) {
-    const int k0 = s * RBK;
+  auto load_stage = [&](int s, ARow* __restrict__ A, ARow* __restrict__ B) {
+    const int k0 = s * RBK * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[i] + k0),
-                                       (lds_void_t*)&As[buf][(2 * wave + i) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_void_t*)&A[(2 * wave + i) * 8][0], 16,
+                                               a_off[i], k0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[i] + k0),
-                                       (lds_void_t*)&Bs[buf][(3 * wave + i) * 8][0], 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t*)&B[(3 * wave + i) * 8][0], 16,
+                                               b_off[i], k0, 0, 0);
   };
+
+  // the fp16 copy: thread t converts chunks 2 (t % 4), +1 of tile row t / 4
+  const bool write_x16 = x16 != nullptr && nt == 0;
+  const int xr = tid >> 2, xc = 2 * (tid & 3);
+  const bool xrow_ok = row0 + xr < T;
+  uint16_t* const x16_row = write_x16 ? x16 + (int64_t)(row0 + xr) * H + kbeg : nullptr;
 
   f32x4 acc[4][3];
 #pragma unroll
@@ -120,43 +140,60 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 3; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // three-stage ring: stages s+1 and s+2 are in flight while s is computed;
-  // each stage is five direct loads per wave, so "at most 5 outstanding"
-  // means stage s+1 has landed
-  load_stage(0, 0);
-  if (nst > 1) load_stage(1, 1);
-  if (nst > 1)
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s % RSTAGES;
-    if (s + 2 < nst) load_stage(s + 2, (s + 2) % RSTAGES);
+  // stage s: slot (A, B) holds it; stage s + 2 is loaded into (A2, B2) (the
+  // slot of stage s - 1, which every wave finished before the last barrier).
+  // Each stage is five direct loads per wave, so "at most 5 outstanding"
+  // after the loads of stage s + 2 means stage s + 1 has landed. Every stage
+  // issues its loads (past the last stage they load it again, into a slot
+  // no later stage reads), so the waits are the same at every stage and the
+  // compiler's own wait bookkeeping stays exact.
+  auto stage = [&](int s, const ARow* __restrict__ A, const ARow* __restrict__ B,
+                   ARow* __restrict__ A2, ARow* __restrict__ B2) {
+    load_stage(min(s + 2, nst - 1), A2, B2);
+    if (write_x16 && xrow_ok) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = xc + q;
+        st16(x16_row + s * RBK + 8 * c, bf16x8_to_f16_kperm(ld16(&A[xr][(c ^ (xr & 7)) * 8])));
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       bf16x8 a[4], bb[3];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = wm * 64 + i * 16 + r16;
-        a[i] = __builtin_bit_cast(bf16x8, ld16(&As[buf][ra][((j * 4 + lg) ^ (ra & 7)) * 8]));
+        a[i] = __builtin_bit_cast(bf16x8, ld16(&A[ra][((j * 4 + lg) ^ (ra & 7)) * 8]));
       }
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
         const int rb = wn * 48 + i * 16 + r16;
-        bb[i] = __builtin_bit_cast(bf16x8, ld16(&Bs[buf][rb][((j * 4 + lg) ^ (rb & 7)) * 8]));
+        bb[i] = __builtin_bit_cast(bf16x8, ld16(&B[rb][((j * 4 + lg) ^ (rb & 7)) * 8]));
       }
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 3; ++ni) acc[mi][ni] = mfma_16x16x32(a[mi], bb[ni], acc[mi][ni]);
     }
-    if (s + 2 < nst)
-      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // (stores of the fp16 copy count in vmcnt as well; the loads still land
+    // in issue order, so the wait below still covers stage s + 1)
+    // (the builtin, not inline asm: the compiler counts it in its own wait
+    // bookkeeping and adds no conservative waits of its own)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+    lds_barrier();
+  };
+
+  load_stage(0, As0, Bs0);
+  load_stage(min(1, nst - 1), As1, Bs1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(5));
+  lds_barrier();
+  for (int s = 0; s < nst; s += 3) {
+    stage(s, As0, Bs0, As2, Bs2);
+    if (s + 1 < nst) stage(s + 1, As1, Bs1, As0, Bs0);
+    if (s + 2 < nst) stage(s + 2, As2, Bs2, As1, Bs1);
   }
+  // the repeated loads of the last stages land before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   float* Pk = P + (int64_t)ks * T * N;
 #pragma unroll
@@ -485,7 +522,7 @@ hipError_t launch_router_split(const float* w_router, const float* shared_gate, 
 hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const float* shared_gate,
                               const uint16_t* split, float* partial, const float* bias, int T,
                               int H, int E, int k, float* logits, int32_t* ids, float* topk_w,
-                              float* shared_w, hipStream_t s) {
+                              float* shared_w, uint16_t* x16, hipStream_t s) {
   const bool has_shared = shared_gate != nullptr;
   const int Epad = router_padded_rows(E, has_shared);
   int ks = 1, planes = 1;
@@ -503,7 +540,7 @@ hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const fl
     planes = 3;
     LaunchScope ls("router_gemm", s);
     hipLaunchKernelGGL(router_gemm_kernel, dim3(n_mt * n_nt * ks), dim3(RTHREADS), 0, s, x,
-                       split, partial, T, H, N, n_mt, n_nt, ks);
+                       split, partial, x16, T, H, N, n_mt, n_nt, ks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -202,6 +202,11 @@ def test_full_size_a3b_pp8192_sampled():
     rows = np.concatenate([rows, [0, cfg.T - 1]])
     ref = oracle.moe_layer_rows(bits(x), rows, cpu, cfg.k, cfg.G, cfg.quant, logits32_rows=L[rows])
     gate(f64_of_bf16(out)[rows], ref["out"], "out rows")
+    # the fused call (whose router GEMM also writes the fp16 copy of x) gives
+    # the same bits as the separate entry points (moe_expert_ffn converts x
+    # itself)
+    g = run_pipeline(cfg, li, x)
+    assert torch.equal(out.view(torch.int16), g["out"].view(torch.int16))
 
 
 def test_max_T_sampled():
