@@ -27,7 +27,11 @@ one JSON line:
                bytes per launch from rocprofv3 counters (null until measured
                for the current kernel)
   cpu_baseline the CPU oracle (numpy float64) on the same workload on this
-               host's cores
+               host's cores; `gemm_only` times it with the dequantized expert
+               matrices prepared beforehand
+  step_ms_p10_p50_p90  the spread of single steps (an event between steps)
+  ceilings     a bf16 8192^3 torch.matmul and a 1 GiB copy on the same box,
+               as context for the fractions (--no-ceilings skips them)
 """
 from __future__ import annotations
 
