@@ -47,15 +47,14 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int BN = 64 * NWAVES;  // weight rows per tile
 constexpr int BK = 128;          // K per pipeline stage
 constexpr int NXCD = 8;
-constexpr int MSUB = BM / 16;    // 16-row sub-tiles
 constexpr int NFRAG = 4;         // 16-column fragments per wave
 constexpr int WGS_PER_CU = 1;    // persistent workgroups per CU (two waves per SIMD)
 constexpr int ASTAGES = 3;       // activation stages in the LDS ring
 constexpr int ALD = 32 / NWAVES; // direct activation loads per wave and stage (4 rows each)
 constexpr int A_STAGE_BYTES = BM * BK * 2;
 constexpr int SUB_BYTES = BM * 128;  // one wave's epilogue sub-tile (128 rows x 64 fp16)
-// two sub-tiles fit in each activation stage; Ex holds the rest
-constexpr int EX_BYTES = (NWAVES - 2 * ASTAGES) * SUB_BYTES;
+// (128-row tiles: two sub-tiles fit in each activation stage, an extra
+// region holds the rest)
 static_assert(A_STAGE_BYTES == 2 * SUB_BYTES && NWAVES > 2 * ASTAGES, "epilogue LDS layout");
 
 // bf16 activations -> fp16 in kperm chunk order (exact for |x| < 65504).
@@ -136,19 +135,34 @@ constexpr int SC_STAGE = 0, SC_TILE = 1, SC_WINDOW = 2;
 // lane's 32-element K block of a row is 4 * BITS bytes: one 16-, 12- or
 // 8-byte load per fragment and stage. MIX: one group of experts of a
 // mixed layer (the expert filter and slot map of GroupedGemm are read).
-template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = false>
+// TBM: rows per tile, 128, or 64 for layers whose experts get about 64
+// rows or fewer (a 128-row tile would be mostly padding there).
+template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = false,
+          int TBM = 128>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
+  static_assert(TBM == 128 || TBM == 64, "tile rows");
+  // this instance's tile height and what follows from it (the names hide
+  // the 128-row constants above)
+  constexpr int BM = TBM;
+  constexpr int MSUB = BM / 16;
+  constexpr int ALD = BM / 4 / NWAVES;  // direct activation loads per wave and stage
+  constexpr int A_STAGE_BYTES = BM * BK * 2;
+  // epilogue sub-tiles: gate/up BM rows x 64 B per wave; down 64-row halves
+  // x 128 B per wave. 128-row tiles put waves 0-3 in As2, 4-7 in Ex; 64-row
+  // tiles put all eight in Ex.
+  constexpr int SUBW = GATEUP ? BM * 64 : 64 * 128;
+  constexpr int EX_BYTES = BM == 128 ? (NWAVES - 2 * ASTAGES) * SUB_BYTES : NWAVES * SUBW;
   // LDS, two uses:
-  //  - K loop: a ring of three activation tiles (As0..As2), 128 rows x 128
+  //  - K loop: a ring of three activation tiles (As0..As2), BM rows x 128
   //    fp16 each, no padding; the 16-byte chunk c of row r sits in slot
   //    c ^ rowswz(r) (see rowswz), which keeps the fragment reads free of
   //    bank conflicts and lets a direct global->LDS load fill four whole rows.
   //    Separate arrays (and a K loop unrolled by three) let the compiler see
   //    that a stage's LDS reads never touch the tiles still being loaded, so
   //    it does not wait for those loads before reading;
-  //  - epilogue: each wave's output sub-tile (128 rows x 64 B for h, x 128 B
-  //    for y) in As0..As2 and Ex, so the results leave in whole 16-byte row
-  //    pieces.
+  //  - epilogue: each wave's output sub-tile (BM rows x 64 B for h, 64-row
+  //    halves x 128 B for y) in As2 and Ex, so the results leave in whole
+  //    16-byte row pieces.
   __shared__ __attribute__((aligned(16))) uint8_t As0[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
@@ -477,7 +491,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     const int ldc = ts.shared ? g.ldc2 : g.ldc;
     asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
     if (GATEUP) {
-      uint8_t* sub = (wave < 4 ? As2 : Ex) + (wave & 3) * (BM * 64);
+      uint8_t* sub = BM == 128 ? (wave < 4 ? As2 : Ex) + (wave & 3) * SUBW : Ex + wave * SUBW;
       // the 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four
       // row groups of one write land in different banks
 #pragma unroll
@@ -508,12 +522,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       // 128 B (its 64 columns) in As2 or Ex; lane (r16, lg) holds columns
       // 16 f + 4 lg .. +3 of row 16 mi + r16, and the 16-byte piece p of row
       // r sits at p ^ (r & 7)
-      uint8_t* sub = (wave < 4 ? As2 : Ex) + (wave & 3) * (64 * 128);
+      uint8_t* sub = BM == 128 ? (wave < 4 ? As2 : Ex) + (wave & 3) * SUBW : Ex + wave * SUBW;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < BM / 64; ++half) {
 #pragma unroll
-        for (int mh = 0; mh < MSUB / 2; ++mh) {
-          const int mi = half * (MSUB / 2) + mh;
+        for (int mh = 0; mh < 4; ++mh) {
+          const int mi = half * 4 + mh;
           const int rl = mh * 16 + rr;  // row within the half
 #pragma unroll
           for (int f = 0; f < NFRAG; ++f) {
@@ -652,10 +666,16 @@ int g_num_cus = 0;
 template <bool GATEUP>
 hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name) {
   const int n_ntiles = GATEUP ? cdiv(g.N / 2, BN / 2) : cdiv(g.N, BN);
+  // 64-row tiles when the experts get 64 rows each on average or fewer
+  // (grouped launches of one width, without an extra group)
+  const bool fold = g.counts != nullptr && g.rows2 > 0;
+  const bool rows64 =
+      g.counts != nullptr && !fold && g.tier == nullptr && (int64_t)g.max_rows <= 64LL * g.E;
+  const int tbm = rows64 ? 64 : BM;
   const int m_bound =
       g.counts != nullptr
-          ? cdiv(g.max_rows, BM) + g.E + (g.rows2 > 0 ? cdiv(g.rows2, BM) + 1 : 0)
-          : cdiv(g.rows_single, BM);
+          ? cdiv(g.max_rows, tbm) + g.E + (g.rows2 > 0 ? cdiv(g.rows2, tbm) + 1 : 0)
+          : cdiv(g.rows_single, tbm);
   if (m_bound <= 0) return hipSuccess;
   if (g_num_cus == 0) {
     int dev = 0;
@@ -677,7 +697,6 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   // so that the common kernels keep their registers
   const int KG = g.K / g.G;
   const bool asym = g.Wmin != nullptr;
-  const bool fold = g.counts != nullptr && g.rows2 > 0;
   const bool scl = !fold && (GATEUP ? (!asym && KG <= 16) : (asym ? KG <= 8 : KG <= 16));
   // scale windows: asymmetric experts with G = 32 whose scales do not fit
   // the tile (the shared-expert variant included)
@@ -685,6 +704,13 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
   auto go = [&](auto a, auto m, auto f) {
     constexpr bool A = decltype(a)::value, F = decltype(f)::value;
     constexpr int M = decltype(m)::value;
+    if constexpr (!F) {
+      if (rows64) {
+        hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, M, F, 4, false, 64>), grid, block, 0, s,
+                           g, n_ntiles);
+        return;
+      }
+    }
     hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, A, M, F>), grid, block, 0, s, g, n_ntiles);
   };
   const std::true_type yes{};
