@@ -666,11 +666,12 @@ int g_num_cus = 0;
 template <bool GATEUP>
 hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name) {
   const int n_ntiles = GATEUP ? cdiv(g.N / 2, BN / 2) : cdiv(g.N, BN);
-  // 64-row tiles when the experts get 64 rows each on average or fewer
-  // (grouped launches of one width, without an extra group)
+  // 64-row tiles when the experts get few rows each on average (grouped
+  // launches of one width, without an extra group): up to 128 for gate/up,
+  // 64 for down (measured at T = 512 .. 4096 on the A3B shape)
   const bool fold = g.counts != nullptr && g.rows2 > 0;
-  const bool rows64 =
-      g.counts != nullptr && !fold && g.tier == nullptr && (int64_t)g.max_rows <= 64LL * g.E;
+  const bool rows64 = g.counts != nullptr && !fold && g.tier == nullptr &&
+                      (int64_t)g.max_rows <= (GATEUP ? 128LL : 64LL) * g.E;
   const int tbm = rows64 ? 64 : BM;
   const int m_bound =
       g.counts != nullptr
