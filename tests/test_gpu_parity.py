@@ -97,6 +97,14 @@ def test_layer_parity(name):
     full_check(cfg, li, cpu, x)
 
 
+def test_layer_parity_mixed_tile_heights():
+    """T = 1536 on the A3B shape: 96 rows per expert on average, so gate/up
+    runs on 64-row tiles and down on 128-row tiles."""
+    cfg = replace(CONFIGS["a3b_pp512"], T=1536)
+    li, cpu, x = setup(cfg)
+    full_check(cfg, li, cpu, x)
+
+
 def test_tiny_random_bytes_all_nibbles():
     cfg = CONFIGS["tiny"]
     li, cpu, x = setup(cfg, random_bytes=True)
