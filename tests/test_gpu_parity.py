@@ -105,6 +105,15 @@ def test_layer_parity_mixed_tile_heights():
     full_check(cfg, li, cpu, x)
 
 
+def test_layer_parity_T4096():
+    """T = 4096 on the A3B shape (256 rows per expert on average, 128-row
+    tiles, each expert's last tile partly filled): every intermediate
+    against the oracle, and the fused call bit-equal to the entry points."""
+    cfg = replace(CONFIGS["a3b_pp512"], T=4096)
+    li, cpu, x = setup(cfg)
+    full_check(cfg, li, cpu, x)
+
+
 def test_tiny_random_bytes_all_nibbles():
     cfg = CONFIGS["tiny"]
     li, cpu, x = setup(cfg, random_bytes=True)
