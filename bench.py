@@ -311,6 +311,11 @@ def main():
 
     cfg = get_config(a.workload)
     T = a.T or cfg.T
+    if T > cfg.T:
+        # more tokens than the workload's token tensor holds: the same layer
+        # over a longer synthetic batch (drawn with the workload's seed)
+        from dataclasses import replace as _replace
+        cfg = _replace(cfg, T=T)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stacked = cfg.n_layers > 1

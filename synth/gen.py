@@ -170,6 +170,8 @@ class LayerInputs:
 def make_tokens(cfg: MoEConfig, device="cpu", rows: Optional[int] = None) -> torch.Tensor:
     """Activations [rows][H] bf16: the first `rows` rows of the config's
     full T-row token tensor (so a short sweep reuses the long batch's rows)."""
+    if rows is not None and rows > cfg.T:
+        raise ValueError(f"{cfg.name} holds {cfg.T} token rows; asked for {rows}")
     x = _randn((cfg.T, cfg.H), cfg.seed, "x", device).to(torch.bfloat16)
     if rows is not None:
         x = x[:rows].contiguous()
