@@ -134,7 +134,8 @@ moe_status_t moe_workspace_size(const moe_shape_t *shape, int64_t T, int32_t kin
  * with an exact three-term bf16 split of each fp32 router weight, summed in
  * fp32 on the matrix cores (an fp32 GEMM to within its usual error bound).
  *   x           [T][H] bf16          w_router [E][H] fp32
- *   router_bias [E] fp32 or NULL     shared_gate [H] fp32 or NULL
+ *   router_bias [E] fp32 or NULL     shared_gate [H] fp32 or NULL; only with
+ *                                    shape.shared_inter > 0 (else INVALID_ARGUMENT)
  *   logits      [T][E] fp32 or NULL: receives the (biased) logits used for selection
  *   topk_ids    [T][k] int32         topk_w [T][k] fp32
  *   shared_w    [T] fp32, required iff shared_gate != NULL

@@ -57,6 +57,7 @@ __all__ = [
     "moe_layer",
     "moe_layer_rows",
     "rmsnorm",
+    "stack_layer",
     "moe_stack",
     "silu",
     "sigmoid",
@@ -242,12 +243,13 @@ def _expert_mats(w, e, G, quant, prefix="w"):
     return W13, W2
 
 
-def expert_ffn(xf, sorted_pairs, offsets, k: int, w: dict, G: int, quant: str):
+def expert_ffn(xf, sorted_pairs, offsets, k: int, w: dict, G: int, quant: str, cache=None):
     """Run every routed expert on its rows, in expert-sorted order.
 
     Row r of expert e (offsets[e] <= r < offsets[e+1]) is the token
     sorted_pairs[r] // k. Returns (h_perm [P][I], y_perm [P][H]) float64,
-    unweighted.
+    unweighted. `cache` (a dict) keeps dequantized experts between calls on
+    the same weights.
     """
     xf = np.asarray(xf, np.float64)
     E = len(offsets) - 1
@@ -260,7 +262,12 @@ def expert_ffn(xf, sorted_pairs, offsets, k: int, w: dict, G: int, quant: str):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
             continue
-        W13, W2 = _expert_mats(w, e, G, quant)
+        if cache is None:
+            W13, W2 = _expert_mats(w, e, G, quant)
+        else:
+            if e not in cache:
+                cache[e] = _expert_mats(w, e, G, quant)
+            W13, W2 = cache[e]
         X = xf[np.asarray(sorted_pairs[a:b]) // k]
         h, y = swiglu_expert(X, W13, W2)
         h_perm[a:b] = h
@@ -268,8 +275,13 @@ def expert_ffn(xf, sorted_pairs, offsets, k: int, w: dict, G: int, quant: str):
     return h_perm, y_perm
 
 
-def shared_expert(xf, w: dict, G: int, quant: str):
-    W13, W2 = _expert_mats(w, None, G, quant, prefix="s")
+def shared_expert(xf, w: dict, G: int, quant: str, cache=None):
+    if cache is None:
+        W13, W2 = _expert_mats(w, None, G, quant, prefix="s")
+    else:
+        if "shared" not in cache:
+            cache["shared"] = _expert_mats(w, None, G, quant, prefix="s")
+        W13, W2 = cache["shared"]
     return swiglu_expert(np.asarray(xf, np.float64), W13, W2)
 
 
@@ -312,7 +324,8 @@ def _weights_dict(li) -> dict:
     return d
 
 
-def moe_layer(x_bits, li, k: int, G: int, quant: str, logits32=None, residual_bits=None):
+def moe_layer(x_bits, li, k: int, G: int, quant: str, logits32=None, residual_bits=None,
+              cache=None):
     """One MoE layer on bf16 activations x_bits [T][H] (uint16 bit patterns).
 
     If logits32 is given (fp32 [T][E]) the top-k decision is taken on those
@@ -320,7 +333,8 @@ def moe_layer(x_bits, li, k: int, G: int, quant: str, logits32=None, residual_bi
     everything after the decision is recomputed here. Returns a dict with
     every intermediate: logits (float64), logits32, ids, weights, counts,
     offsets, sorted_pairs, inv, h_perm, y_perm, shared_w, y_shared, out
-    (float64, before the final bf16 rounding).
+    (float64, before the final bf16 rounding). `cache` (a dict) keeps the
+    dequantized experts of these weights between calls.
     """
     w = _weights_dict(li)
     xf = bf16_to_f64(x_bits)
@@ -329,11 +343,11 @@ def moe_layer(x_bits, li, k: int, G: int, quant: str, logits32=None, residual_bi
     L32 = L.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
     ids, tw = select_topk(L32, k)
     counts, offsets, sorted_pairs, inv = permute(ids, E)
-    h_perm, y_perm = expert_ffn(xf, sorted_pairs, offsets, k, w, G, quant)
+    h_perm, y_perm = expert_ffn(xf, sorted_pairs, offsets, k, w, G, quant, cache=cache)
     sw = ys = hs = None
     if w["s13"] is not None:
         sw = shared_gate(xf, w["shared_gate"])
-        hs, ys = shared_expert(xf, w, G, quant)
+        hs, ys = shared_expert(xf, w, G, quant, cache=cache)
     res = bf16_to_f64(residual_bits) if residual_bits is not None else None
     out = combine(y_perm, inv, tw, ys, sw, res)
     return dict(logits=L, logits32=L32, ids=ids, weights=tw, counts=counts, offsets=offsets,
@@ -386,6 +400,16 @@ def rmsnorm(x_bits, weight, eps: float) -> np.ndarray:
     return xf * r * np.asarray(weight, np.float64)[None, :]
 
 
+def stack_layer(x_bits, li, k: int, G: int, quant: str, eps: float, cache=None):
+    """One pre-norm layer of the stack on bf16 rows x_bits:
+    x <- bf16(x + MoE(bf16(RMSNorm(x)))). Returns (new x bits, the layer's
+    moe_layer dict, which holds its routing decisions)."""
+    w = _weights_dict(li)
+    xn = round_to_bf16(rmsnorm(x_bits, w["norm_weight"], eps))
+    res = moe_layer(xn, li, k, G, quant, residual_bits=x_bits, cache=cache)
+    return round_to_bf16(res["out"]), res
+
+
 def moe_stack(x_bits, layers, k: int, G: int, quant: str, eps: float, chunk: int = 0):
     """Pre-norm stack: for each chunk of rows, for each layer l,
     x <- bf16(x + MoE_l(bf16(RMSNorm_l(x)))). Returns bf16 bits [T][H]."""
@@ -395,10 +419,7 @@ def moe_stack(x_bits, layers, k: int, G: int, quant: str, eps: float, chunk: int
     for r0 in range(0, T, chunk):
         xc = x[r0:r0 + chunk]
         for li in layers:
-            w = _weights_dict(li)
-            xn = round_to_bf16(rmsnorm(xc, w["norm_weight"], eps))
-            res = moe_layer(xn, li, k, G, quant, residual_bits=xc)
-            xc = round_to_bf16(res["out"])
+            xc, _ = stack_layer(xc, li, k, G, quant, eps)
         x[r0:r0 + chunk] = xc
     return x
 

@@ -588,15 +588,17 @@ moe_status_t moe_route(const moe_shape_t* shape, int64_t T, const uint16_t* x,
   if ((shared_gate == nullptr) != (shared_w == nullptr))
     return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate and shared_w go together");
   QMOE_OPTIONAL(shared_w, "shared_w");
-  // the router pads for a shared-gate row whenever the shape has a shared expert
-  Shape sr = s;
-  sr.Is = shared_gate != nullptr ? 1 : 0;
-  st = check_ws(ws, ws_bytes, route_ws(sr, T));
+  // the shared gate belongs to a shape with a shared expert (as in
+  // moe_layer_forward), so the MOE_WS_ROUTE size, which pads the split router
+  // matrix for the gate row exactly when shared_inter > 0, always suffices
+  if (shared_gate != nullptr && s.Is == 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate given but shared_inter == 0");
+  st = check_ws(ws, ws_bytes, route_ws(s, T));
   if (st != MOE_OK) return st;
   auto* wsb = static_cast<uint8_t*>(ws);
   return route_impl(s, T, x, w_router, router_bias, shared_gate, logits, topk_ids, topk_w,
                     shared_w, reinterpret_cast<uint16_t*>(wsb),
-                    reinterpret_cast<float*>(wsb + al(router_split_bytes(s.E, sr.Is > 0, s.H))),
+                    reinterpret_cast<float*>(wsb + al(router_split_bytes(s.E, s.Is > 0, s.H))),
                     nullptr, stream);
 }
 

@@ -41,14 +41,24 @@ __device__ __forceinline__ float f16lo(uint32_t w) {
 __device__ __forceinline__ float f16hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
-// Two fp32 -> packed fp16 pair (round to nearest even).
+// Largest finite fp16 value.
+constexpr float kF16Max = 65504.0f;
+
+// Two fp32 -> packed fp16 pair (round to nearest even), saturating: values
+// beyond the fp16 range become +-65504 instead of infinity (one v_med3_f32
+// each; the identity on every value that rounds to a finite fp16, so results
+// in range are unchanged). Every fp16 intermediate of the layer (the fp16
+// copy of x, h, y_perm, y_shared) is stored through this.
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -kF16Max, kF16Max);
+  b = __builtin_amdgcn_fmed3f(b, -kF16Max, kF16Max);
   f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 // Eight bf16 values (x0..x7, two per word) -> fp16 in kperm chunk order
-// (positions 0..7 hold x0, x4, x1, x5, x2, x6, x3, x7); exact for |x| < 65504.
+// (positions 0..7 hold x0, x4, x1, x5, x2, x6, x3, x7); exact for
+// 2^-14 <= |x| <= 65504 (and zero), saturating beyond.
 __device__ __forceinline__ u32x4 bf16x8_to_f16_kperm(u32x4 d) {
   u32x4 o;
   o[0] = pack_f16x2(bf16lo(d[0]), bf16lo(d[2]));  // x0, x4

@@ -640,8 +640,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         if (kt + 2 < nk) stage(kt + 2, As2, As1, false);
       }
     }
-    // the repeated loads of the last stages land before the ring is reused
+    // The last stage's repeated activation load targets ring slot
+    // (nk + 1) % 3, which is As2 when nk % 3 == 1, and waves 0-3 of the
+    // 128-row instance write their epilogue sub-tiles into As2. Each wave's
+    // own wait covers only its own loads, so every wave waits for all of its
+    // loads and then meets the others at a barrier: after it, no direct
+    // global->LDS load of this tile is still in flight anywhere in the
+    // workgroup, and the epilogue's LDS writes cannot be overwritten.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
 
     const int next = tile + wgs_per_xcd;
     const bool has_next = next < t_end;

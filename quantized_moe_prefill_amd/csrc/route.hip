@@ -10,7 +10,7 @@
 //  router_split : Wr (+ shared gate row) -> Wsplit [3*Epad][H] bf16 (the three
 //                 terms are separate rows, so the product is one dense GEMM)
 //  router_gemm  : P[ks][t][n] = sum over the ks-th K slice of x[t] . Wsplit[n],
-//                 fp32; 128 x 256 tiles, 8 waves, a three-stage ring of
+//                 fp32; 128 x 192 tiles, 8 waves, a three-stage ring of
 //                 direct global->LDS loads; the K dimension is split across
 //                 workgroups when there are too few token tiles to fill the GPU
 //  router_select: L[t,e] = sum_ks ((P[e] + P[Epad+e]) + P[2Epad+e]) + b[e] in a

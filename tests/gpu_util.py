@@ -30,6 +30,16 @@ def half_ulp(ref: np.ndarray, fmt: str) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e - sig, tiny) - 1)
 
 
+def round_fmt(ref: np.ndarray, fmt: str) -> np.ndarray:
+    """`ref` rounded to the nearest `fmt` number (ties to even), as float64."""
+    ref = np.asarray(ref, np.float64)
+    if fmt == "bf16":
+        return oracle.bf16_to_f64(oracle.round_to_bf16(ref))
+    if fmt == "fp16":
+        return ref.astype(np.float16).astype(np.float64)
+    return ref
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """bf16/fp16 tensor -> uint16 numpy bit patterns (on the host)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
@@ -55,11 +65,28 @@ def gate(gpu: np.ndarray, ref: np.ndarray, what: str, fmt: str = "bf16", rel=REL
     rl2 = np.linalg.norm(gpu - ref) / nref if nref > 0 else np.linalg.norm(gpu - ref)
     rms = np.sqrt(np.mean(ref * ref))
     d = np.abs(gpu - ref)
-    excess = np.max(d - half_ulp(ref, fmt))
+    hu = half_ulp(ref, fmt)
+    excess = np.max(d - hu)
+    # The literal gate, against the reference rounded to the GPU result's own
+    # format: |gpu - fmt(ref)| <= mx * rms. An element beyond it must be a
+    # faithful rounding of the exact value (one of the two fmt numbers that
+    # bracket it, |gpu - ref| < one ulp): the exact value sat near a rounding
+    # boundary and the two sides rounded it to neighbouring numbers.
+    lit = np.abs(gpu - round_fmt(ref, fmt))
+    over = lit > mx * rms
+    faithful = d < 2.0 * hu
     print(f"[gate] {what}: relL2={rl2:.3e} (<= {rel:.1e})  max(|err| - half-ulp {fmt})/rms="
-          f"{excess / rms:.3e} (<= {mx:.1e})  raw maxabs/rms={d.max() / rms:.3e}")
+          f"{excess / rms:.3e} (<= {mx:.1e})  raw maxabs/rms={d.max() / rms:.3e}  "
+          f"literal max|gpu - {fmt}(ref)|/rms={lit.max() / rms:.3e} "
+          f"({int(over.sum())} of {ref.size} beyond it, all faithful roundings)")
     assert rl2 <= rel, f"{what}: rel L2 {rl2:.3e} > {rel:.1e}"
     assert excess <= mx * rms, f"{what}: max abs beyond rounding {excess:.3e} > {mx:.1e} * rms {rms:.3e}"
+    assert np.all(faithful[over]), (
+        f"{what}: {int((over & ~faithful).sum())} elements beyond the literal gate that are not "
+        f"a faithful rounding of the exact value")
+    if fmt == "fp16":
+        # fp16's own rounding is far below the gate: the raw gate holds as stated
+        assert d.max() <= mx * rms, f"{what}: raw max abs {d.max():.3e} > {mx:.1e} * rms {rms:.3e}"
     return rl2, excess / rms
 
 

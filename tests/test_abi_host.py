@@ -127,6 +127,11 @@ def test_route_validation_before_launch():
     assert L.moe_route(ctypes.byref(s), 4, FAKE + 2, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
     # shared_gate without shared_w
     assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    # shared_gate on a shape without a shared expert (its MOE_WS_ROUTE size
+    # has no room for the gate row)
+    assert s.shared_inter == 0
+    assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert b"shared_inter" in L.moe_last_error()
     # workspace too small / missing
     assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, None, None, FAKE, FAKE, None, FAKE, 16, None) == N.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_route(ctypes.byref(s), 4, FAKE, FAKE, None, None, None, FAKE, FAKE, None, None, 0, None) == N.MOE_ERR_INVALID_ARGUMENT

@@ -6,8 +6,11 @@ within the floating-point gates of tests/gpu_util.py. The int8 h is
 teacher-forced: its codes are decided on the GPU's fp16 h (itself gated
 against the oracle's), as the top-k choice is taken on the GPU's logits,
 because an h computed in another summation order can round to a different
-fp16 value and move a code by one step. Without the forcing the relative
-L2 gate still applies. The route's own distance from the exact layer (the
+fp16 value and move a code by one step. The forcing is bounded, not
+assumed: the codes of the GPU's h and of the oracle's own h are compared,
+every difference must be one step and at most a 1e-3 fraction may differ.
+Without the forcing the relative L2 gate still applies (its max-abs is
+printed). The route's own distance from the exact layer (the
 8-bit rounding of x and h) is checked against the floating-point oracle
 with its own, looser bound."""
 from dataclasses import replace
@@ -30,6 +33,13 @@ DEV = "cuda:0"
 # Gaussian x, a few % for the heavier-tailed h); the oracle measures 1.5-2.5 %
 # relative L2 on these layers.
 ROUTE_REL_L2 = 5e-2
+
+# The GPU's fp16 h comes from fp32 sums in another order than the oracle's
+# float64 ones; where the two round h to different fp16 values (about one
+# element in a few thousand) a code of h can move by one step. Bound on the
+# fraction of h codes that differ between the GPU's h and the oracle's own,
+# each by at most one step.
+H_CODE_FRAC = 1e-3
 
 _CACHE = {}
 
@@ -62,6 +72,7 @@ def i8_check(cfg, li, cpu, x, route_err=True):
     assert np.array_equal(sp.cpu().numpy(), own["sorted_pairs"])
     h_gpu = f64_of_f16(h)
     gate(h_gpu, own["h16"], "h (int8 route)", fmt="fp16")
+    check_h_codes(h_gpu, own)
     ref = oracle.moe_layer_i8(bits(x), cpu, cfg.k, cfg.G, logits32=L, h16_forced=h_gpu)
     gate(f64_of_f16(y_perm), ref["y_perm"], "y_perm (int8 route, h forced)", fmt="fp16")
     gate(f64_of_bf16(out), ref["out"], "out (int8 route, h forced)")
@@ -74,6 +85,22 @@ def i8_check(cfg, li, cpu, x, route_err=True):
         print(f"[route] int8 route vs exact layer: relL2 {rel:.3e} (<= {ROUTE_REL_L2:.0e})")
         assert rel <= ROUTE_REL_L2
     return out
+
+
+def check_h_codes(h_gpu, own):
+    """The codes of the GPU's h (quantized as the GPU does, which
+    test_quantize_rows_bit_exact pins bit for bit) against the codes of the
+    oracle's own h: every difference is one step, and few differ."""
+    q_gpu, s_gpu = oracle.quantize_rows_i8(np.asarray(h_gpu, np.float64).astype(np.float32))
+    dq = np.abs(q_gpu.astype(np.int32) - own["hq"].astype(np.int32))
+    n_codes = int(np.count_nonzero(dq))
+    n_h = int(np.count_nonzero(np.asarray(h_gpu) != own["h16"]))
+    n_rows = int(np.count_nonzero(s_gpu.view(np.uint32) != own["sh"].view(np.uint32)))
+    print(f"[h codes] {n_codes} of {dq.size} codes differ (max step {int(dq.max()) if dq.size else 0}); "
+          f"{n_h} fp16 h values differ; {n_rows} of {len(s_gpu)} row scales differ")
+    if dq.size:
+        assert dq.max() <= 1, "an h code differs by more than one step"
+    assert n_codes <= H_CODE_FRAC * dq.size, f"{n_codes} h codes differ (> {H_CODE_FRAC:.0e})"
 
 
 def test_quantize_rows_bit_exact():
@@ -138,31 +165,14 @@ def test_i8_skewed_routing_empty_experts():
     assert out.shape == (cfg.T, cfg.H)
 
 
-def test_i8_full_size_a3b_pp8192_sampled():
-    """The bench workload at full size through moe_layer_forward_i8: sampled
-    token outputs against the oracle's integer route, teacher-forced on the
-    GPU logits."""
+def test_i8_full_size_a3b_pp8192():
+    """The bench workload at full size through the integer route: every row
+    of h, y_perm and out against the oracle's integer route (teacher-forced
+    on the GPU logits), the h codes bounded, the layer call bit-equal to the
+    entry points, and the route's distance from the exact layer."""
     cfg = CONFIGS["a3b_pp8192"]
     li, cpu, x = setup(cfg)
-    shape = qm.shape_of(cfg)
-    ex = qm.Experts(li)
-    out = qm.moe_layer_forward_i8(shape, x, li.w_router, li.router_bias, ex)
-    logits, ids, tw, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None, want_logits=True)
-    counts, offsets, sp, inv = qm.moe_permute(shape, ids)
-    y_perm, h = qm.moe_expert_ffn_i8(shape, x, ex, counts, offsets, sp, want_h=True)
-    out2 = qm.moe_combine(shape, y_perm, inv, tw)
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-    L = logits.cpu().numpy()
-    rows = np.random.default_rng(1).choice(cfg.T, 48, replace=False)
-    rows = np.concatenate([rows, [0, cfg.T - 1]])
-    inv_np = inv.cpu().numpy().reshape(cfg.T, cfg.k)
-    h_rows = f64_of_f16(h[torch.from_numpy(inv_np[rows].reshape(-1)).to(DEV)])
-    h_rows = h_rows.reshape(len(rows), cfg.k, cfg.I)
-    ref = oracle.moe_layer_rows_i8(bits(x), rows, cpu, cfg.k, cfg.G, logits32_rows=L[rows],
-                                   h16_rows=h_rows)
-    gate(h_rows.reshape(-1, cfg.I), ref["h16"].reshape(-1, cfg.I), "h rows (int8 route)", fmt="fp16")
-    gate(f64_of_bf16(out)[rows], ref["out"], "out rows (int8 route, h forced)")
+    i8_check(cfg, li, cpu, x)
 
 
 def test_i8_determinism_bitwise():

@@ -102,3 +102,96 @@ def test_stack_full_size_two_layers_sampled():
         n = x_in.shape[0]
         rows = np.concatenate([rng.choice(n, 24, replace=False), [0, n - 1]])
         check_layer(cfg, cpu_layers[l], x_in, xn, logits, x_out, rows=rows)
+
+
+@pytest.mark.timeout(1200)
+def test_stack40_full_depth():
+    """The stacked configuration at full size and depth: 40 layers (H=2048,
+    256 experts, top-8, I=512 + shared 512, asymmetric G=32, Zipf-biased
+    routing), 16,384 rows in two chunks of 8192, chunk-major on the GPU.
+
+    Every (chunk, layer) is checked on all its rows, teacher-forced (the
+    oracle takes the GPU's bf16 layer input, its normed input and its fp32
+    logits): RMSNorm within one bf16 ulp; the layer's MoE part alone (the
+    same layer call without the residual, bf16) and the layer output
+    x + MoE(RMSNorm(x)) through the floating-point gates. End to end, the
+    GPU stack is compared with the oracle's own stack, which routes on its
+    own logits at every layer: relative L2, max-abs and the number of
+    (token, slot) selections that differ are reported (a near-tie in one
+    layer legitimately changes a token's later path), with loose bounds."""
+    cfg = CONFIGS["stack40"]
+    shape = qm.shape_of(cfg)
+    nl, ch = cfg.n_layers, cfg.chunk
+    layers = [make_stack_layer(cfg, l, device=DEV) for l in range(nl)]
+    x0 = make_tokens(cfg, device=DEV)
+    stack = qm.MoEStack(cfg, layers, DEV, eps=cfg.rms_eps, chunk=ch)
+    moe_only = torch.empty((ch, cfg.H), dtype=torch.bfloat16, device=DEV)
+
+    # GPU, chunk-major; each layer's input, normed input, logits, ids and
+    # MoE-only output kept on the host
+    x = x0.clone()
+    rec = {}
+    n_chunks = cfg.T // ch
+    for ci in range(n_chunks):
+        xc = x[ci * ch:(ci + 1) * ch]
+        for l, layer in enumerate(stack.layers):
+            x_in = bits(xc)
+            xn = qm.moe_rmsnorm(xc, layer.li.norm_weight, stack.eps)
+            logits, ids, _, _ = qm.moe_route(shape, xn, layer.li.w_router, layer.li.router_bias,
+                                             layer.li.shared_gate, want_logits=True)
+            layer.forward(xn, out=moe_only)
+            stack.layer_step(layer, xc)
+            rec[(ci, l)] = (x_in, bits(xn), logits.cpu().numpy(), ids.cpu().numpy(),
+                            bits(moe_only))
+        print(f"[stack40] GPU chunk {ci} done", flush=True)
+    torch.cuda.synchronize()
+    x_final = bits(x)
+    # the stack's own driver gives the same bits as the recorded sequence
+    xd = stack.forward(x0.clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(xd), x_final)
+    del xd
+
+    # oracle, layer by layer: teacher-forced checks of both chunks, then one
+    # step of the oracle's own chain over all rows (rows do not interact)
+    xo = bits(x0)
+    slot_flips = set_flips = 0
+    worst_moe = worst_out = 0.0
+    for l in range(nl):
+        cpu = layers[l].to("cpu")
+        cache = {}
+        for ci in range(n_chunks):
+            x_in, xn, L, ids, moe = rec[(ci, l)]
+            x_out = rec[(ci, l + 1)][0] if l + 1 < nl else x_final[ci * ch:(ci + 1) * ch]
+            ref_n = oracle.rmsnorm(x_in, cpu.norm_weight.numpy(), cfg.rms_eps)
+            got_n = oracle.bf16_to_f64(xn)
+            assert np.all(np.abs(got_n - ref_n) <= 2.0 ** -8 * np.abs(ref_n) * 1.01 + 1e-30), (l, ci)
+            r = oracle.moe_layer(xn, cpu, cfg.k, cfg.G, cfg.quant, logits32=L, cache=cache)
+            assert np.array_equal(ids, r["ids"]), (l, ci)
+            _, m = gate(oracle.bf16_to_f64(moe), r["out"], f"layer {l} chunk {ci} MoE part")
+            _, o = gate(oracle.bf16_to_f64(x_out), r["out"] + oracle.bf16_to_f64(x_in),
+                        f"layer {l} chunk {ci} output")
+            worst_moe, worst_out = max(worst_moe, m), max(worst_out, o)
+            del r
+        xo, r = oracle.stack_layer(xo, cpu, cfg.k, cfg.G, cfg.quant, cfg.rms_eps, cache=cache)
+        gpu_ids = np.concatenate([rec[(ci, l)][3] for ci in range(n_chunks)])
+        slot_flips += int(np.count_nonzero(gpu_ids != r["ids"]))
+        set_flips += int(np.count_nonzero(np.sort(gpu_ids, axis=1) != np.sort(r["ids"], axis=1)))
+        del r, cache, cpu
+        for ci in range(n_chunks):
+            rec[(ci, l)] = None
+        print(f"[stack40] layer {l} checked; selections differing so far: {slot_flips} "
+              f"(token, slot), {set_flips} by set", flush=True)
+
+    got = oracle.bf16_to_f64(x_final)
+    ref = oracle.bf16_to_f64(xo)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    rms = np.sqrt(np.mean(ref * ref))
+    mx = np.max(np.abs(got - ref)) / rms
+    n_sel = cfg.T * cfg.k * nl
+    print(f"[stack40 end-to-end] relL2={rel:.3e} maxabs/rms={mx:.3e}; per-layer worst "
+          f"max-abs beyond rounding/rms: MoE part {worst_moe:.3e}, output {worst_out:.3e}; "
+          f"(token, slot) selections differing from the oracle's own routing: {slot_flips} of "
+          f"{n_sel} ({set_flips} by set)")
+    assert rel <= 5e-3
+    assert slot_flips <= 1e-3 * n_sel
