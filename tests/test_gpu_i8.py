@@ -8,7 +8,7 @@ against the oracle's), as the top-k choice is taken on the GPU's logits,
 because an h computed in another summation order can round to a different
 fp16 value and move a code by one step. The forcing is bounded, not
 assumed: the codes of the GPU's h and of the oracle's own h are compared,
-every difference must be one step and at most a 1e-3 fraction may differ.
+every difference must be one step and at most a 5e-3 fraction may differ.
 Without the forcing the relative L2 gate still applies (its max-abs is
 printed). The route's own distance from the exact layer (the
 8-bit rounding of x and h) is checked against the floating-point oracle
@@ -35,11 +35,14 @@ DEV = "cuda:0"
 ROUTE_REL_L2 = 5e-2
 
 # The GPU's fp16 h comes from fp32 sums in another order than the oracle's
-# float64 ones; where the two round h to different fp16 values (about one
-# element in a few thousand) a code of h can move by one step. Bound on the
-# fraction of h codes that differ between the GPU's h and the oracle's own,
-# each by at most one step.
-H_CODE_FRAC = 1e-3
+# float64 ones (and from the offset-float group sums, about 1e-4 relative),
+# so about one h value in six rounds to the neighbouring fp16 number. One
+# fp16 ulp of h moves its code by 127 * 2^-11 * |h| / max|h| < 0.07 of a
+# step, so a code changes only where the value sat within that distance of
+# a rounding boundary, and then by one step: a few codes in a thousand at
+# most (1e-3 measured on these layers). Bound on the fraction of h codes that
+# differ between the GPU's h and the oracle's own:
+H_CODE_FRAC = 5e-3
 
 _CACHE = {}
 
