@@ -5,11 +5,13 @@
                                           8-bit activations on the int8 matrix cores,
                                           gate/up roofline against the int8 peak
     python bench.py --tiers 4:32,3:48,2:48 mixed-width experts (moe_layer_forward_mixed):
-                                          the experts that receive the most rows of
-                                          the batch get the first width, and so on
+                                          the experts that receive the most rows of a
+                                          calibration batch (another seed) get the
+                                          first width, and so on
     python bench.py --stream-hot 32       host-resident experts streamed over PCIe
                                           (moe_layer_forward_streamed): the 32 experts
-                                          that receive the most rows stay on the GPU;
+                                          that receive the most rows of the calibration
+                                          batch stay on the GPU;
                                           --stage-experts sets the staging size,
                                           --copy-stream overlaps copies and kernels
     python bench.py --calib-copy ...      also run a 1 GiB device copy (counter scale)
@@ -30,6 +32,10 @@ one JSON line:
                host's cores; `gemm_only` times it with the dequantized expert
                matrices prepared beforehand
   step_ms_p10_p50_p90  the spread of single steps (an event between steps)
+  regimes      (default workload) the weight-streaming sweep T = 1, 4, 16 with
+               the Infinity Cache evicted before each step, eager and as a
+               replayed HIP graph, against 8 TB/s; and the skewed shared-expert
+               layer (T = 4096) against the MFMA peak (--no-regimes skips them)
   ceilings     a bf16 8192^3 torch.matmul and a 1 GiB copy on the same box,
                as context for the fractions (--no-ceilings skips them)
 """
@@ -99,6 +105,9 @@ def parse():
                     help="experts the staging buffer holds (two chunks of half of it)")
     ap.add_argument("--tiers", default="",
                     help="mixed widths, e.g. 4:32,3:48,2:48 (bits:experts, hottest first)")
+    ap.add_argument("--no-regimes", action="store_true",
+                    help="skip the T=1/4/16 sweep and the skewed shared-expert layer that the "
+                         "default headline run adds as extra fields")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one elementwise kernel that reads and writes 1 GiB "
                          "(counter calibration)")
@@ -295,6 +304,94 @@ def stack_cpu_baseline(cfg, layers_cpu, x, rows=32, layers=2):
     }
 
 
+def regimes(cfg, li, x, dev, steps):
+    """Driver-visible figures of the other regimes, measured after the
+    headline: the weight-streaming sweep (the first T = 1, 4, 16 rows of the
+    headline batch on the same weights; each step timed on its own after
+    evicting the Infinity Cache, eagerly and as a replayed HIP graph) and the
+    skewed shared-expert layer (T = 4096, 256 experts, asymmetric G = 32).
+    Algorithmic bytes of a sweep step: the packed weights (+ scales) of the
+    experts that receive rows, the router matrix, x in and out."""
+    import torch
+
+    import quantized_moe_prefill_amd as qm
+    from synth import get_config, make_layer, make_tokens
+
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn, evict):
+        times = []
+        for _ in range(steps):
+            if evict:
+                torch.sum(flush, dim=0, out=flush_sum)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    res = {}
+    shape = qm.shape_of(cfg)
+    for T in cfg.sweep_T:
+        layer = qm.MoELayer(cfg, li, dev, T)
+        xt = x[:T]
+        o = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            layer.forward(xt, out=o)
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        ms = timed(step, True)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            step()
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        gms = timed(graph.replay, True)
+        _, ids, _, _ = qm.moe_route(shape, xt, li.w_router, li.router_bias, None)
+        active = int(torch.unique(ids).numel())
+        nbytes = active * cfg.expert_bytes() + cfg.E * cfg.H * 4 + 2 * T * cfg.H * 2
+        res[f"T{T}"] = {"ms": round(ms, 4), "graph_ms": round(gms, 4),
+                        "tokens_per_s": round(T / (ms * 1e-3), 1), "active_experts": active,
+                        "hbm_bytes": nbytes, "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "graph_hbm_frac": round(nbytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del graph
+    cfg3 = get_config("skew_shared")
+    li3 = make_layer(cfg3, device=dev)
+    x3 = make_tokens(cfg3, device=dev)
+    layer3 = qm.MoELayer(cfg3, li3, dev, cfg3.T)
+    o3 = torch.empty((cfg3.T, cfg3.H), dtype=torch.bfloat16, device=dev)
+    for _ in range(20):
+        layer3.forward(x3, out=o3)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        layer3.forward(x3, out=o3)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms3 = e0.elapsed_time(e1) / steps
+    res["skew_shared"] = {"ms": round(ms3, 4), "tokens_per_s": round(cfg3.T / (ms3 * 1e-3), 1),
+                          "T": cfg3.T, "mfma_frac": round(cfg3.mfma_flops() / (ms3 * 1e-3) / 1e12
+                                                          / PEAK_BF16_TFLOPS, 4)}
+    res["note"] = ("T1/T4/T16: the first T rows of the headline batch, median of K steps each "
+                   "timed after evicting the Infinity Cache (eager, and a replayed HIP graph); "
+                   "hbm_frac = algorithmic bytes (active experts + router + x + out) / time / "
+                   "8 TB/s. skew_shared: T=4096, 256 experts, top-8, asym G=32, shared expert, "
+                   "Zipf router bias; mfma_frac of the 2.5 PFLOP/s dense fp16/bf16 peak")
+    return res
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -350,10 +447,20 @@ def main():
         out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
         mixed = None
         sx = None
+        # routing statistics for choosing hot (or wider) experts come from a
+        # calibration batch of other tokens (another seed), routed by the
+        # same router, never from the timed batch itself
+        calib_seed = cfg.seed + 1
+
+        def calib_load():
+            from dataclasses import replace as _replace
+            shape = qm.shape_of(cfg)
+            xc = make_tokens(_replace(cfg, seed=calib_seed), device=dev, rows=T)
+            _, ids0, _, _ = qm.moe_route(shape, xc, li.w_router, li.router_bias, None)
+            return torch.bincount(ids0.flatten().long(), minlength=cfg.E).cpu()
         if streamed:
             shape = qm.shape_of(cfg)
-            _, ids0, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None)
-            load = torch.bincount(ids0.flatten().long(), minlength=cfg.E).cpu()
+            load = calib_load()
             hot = torch.argsort(-load, stable=True).tolist()[:a.stream_hot]
             sx = qm.StreamedExperts(li, hot, dev)
             stage = torch.empty(qm.moe_stream_stage_bytes(shape, a.stage_experts), dtype=torch.uint8,
@@ -368,10 +475,9 @@ def main():
                                               out=out, ws=ws, copy_stream=cstream)
         elif tiers:
             from synth.mixed import make_mixed_layer
-            # widths by how many rows each expert receives in this batch
+            # widths by how many rows each expert receives in the calibration batch
             shape = qm.shape_of(cfg)
-            _, ids0, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None)
-            load = torch.bincount(ids0.flatten().long(), minlength=cfg.E).cpu()
+            load = calib_load()
             order = torch.argsort(-load, stable=True).tolist()
             widths = [4] * cfg.E
             pos = 0
@@ -588,6 +694,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if (not a.no_regimes and cfg.name == "a3b_pp8192" and T == cfg.T and not
+            (i8 or tiers or streamed)):
+        rec["regimes"] = regimes(cfg, li, x, dev, a.steps)
+    if streamed or tiers:
+        rec["calibration"] = (f"hot / wider experts chosen by their row counts in a separate "
+                              f"calibration batch of {T} tokens drawn with seed {calib_seed} "
+                              f"(the timed batch uses seed {cfg.seed})")
     if streamed:
         cb = sx.cold_bytes()
         rec["streamed"] = {"cold_experts": sx.n_cold, "cold_bytes": cb,

@@ -168,11 +168,16 @@ moe_status_t moe_permute(const moe_shape_t *shape, int64_t T, const int32_t *top
  *   y_perm[r] = h W_down^T                       (unweighted, fp16 [P][H])
  * The shared expert (if present) runs the same FFN on every token into
  * y_shared [T][H] fp16 (required iff shape.shared_inter > 0).
- * Numerics: activations are converted exactly to fp16 (|x| must be below
- * 65504; magnitudes under 2^-14 keep fewer bits), weights are dequantized in
- * registers to fp16 (q * scale, or q * scale + min, rounded once), both
- * products run on the fp16 matrix cores with fp32 accumulation, and h is
- * rounded to fp16 between them. counts/offsets/sorted_pairs are
+ * Numerics: activations are converted exactly to fp16 (for |x| <= 65504;
+ * magnitudes under 2^-14 keep fewer bits), weights are dequantized in
+ * registers to fp16 (q * scale, or q * scale + min, rounded once; every
+ * dequantized weight must be finite in fp16), both products run on the fp16
+ * matrix cores with fp32 accumulation, and h is rounded to fp16 between
+ * them. fp16 range: every fp16 value the layer stores (the copy of x, h,
+ * y_perm, y_shared) saturates to +-65504 instead of becoming infinite, so
+ * the result stays finite; for a token whose x, h or y leaves the fp16
+ * range the result is then not the layer's value (other tokens are
+ * unaffected: tokens do not interact). counts/offsets/sorted_pairs are
  * moe_permute's outputs. */
 moe_status_t moe_expert_ffn(const moe_shape_t *shape, int64_t T, const uint16_t *x,
                             const moe_experts_t *experts, const int32_t *counts,
@@ -192,7 +197,7 @@ moe_status_t moe_combine(const moe_shape_t *shape, int64_t T, const uint16_t *y_
 
 /* The whole layer: route -> permute -> experts -> combine, all on `stream`,
  * with every intermediate in ws (>= moe_workspace_size(MOE_WS_LAYER)).
- * x [T][H] bf16 (|x| < 65504, see moe_expert_ffn), out [T][H] bf16.
+ * x [T][H] bf16 (fp16 range: see moe_expert_ffn), out [T][H] bf16.
  * shared_gate is required iff shape.shared_inter > 0. residual may be NULL
  * and may alias out. No device-to-host transfer happens. */
 moe_status_t moe_layer_forward(const moe_shape_t *shape, int64_t T, const uint16_t *x,
