@@ -206,6 +206,30 @@ moe_status_t moe_layer_forward(const moe_shape_t *shape, int64_t T, const uint16
                                const uint16_t *residual, uint16_t *out, void *ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* Size of the library's static workspace (bytes, per GPU). */
+#define MOE_STATIC_WS_BYTES (128u << 20)
+
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, results and
+ * kernels as moe_layer_forward (the same bits), with every intermediate in
+ * a fixed array inside the library: MOE_STATIC_WS_BYTES of device memory,
+ * one copy per GPU the library runs on, held until the process ends. The
+ * call allocates nothing. Limit: calls whose moe_workspace_size(MOE_WS_LAYER)
+ * exceeds MOE_STATIC_WS_BYTES return MOE_ERR_UNSUPPORTED before anything is
+ * launched (2,392 tokens at H = 2048, E = 128, k = 8, I = 768; 2,302 at
+ * H = 2048, E = 256, k = 8, I = 512 with a shared expert of 512; split
+ * longer batches). Every call on one GPU uses that GPU's one array, and
+ * nothing in it has to start at zero: calls that overlap on one GPU
+ * (concurrent streams, other threads) race on it and must be serialized by
+ * the caller. The first call on a GPU looks up that GPU's copy of the array
+ * (MOE_ERR_HIP if the lookup fails). */
+moe_status_t moe_layer_forward_static(const moe_shape_t *shape, int64_t T, const uint16_t *x,
+                                      const float *w_router, const float *router_bias,
+                                      const float *shared_gate, const moe_experts_t *experts,
+                                      const uint16_t *residual, uint16_t *out,
+                                      hipStream_t stream);
+
 /* ---- integer route: 8-bit activations x symmetric 4-bit experts ----------
  * The pages admit an integer MoE prefill route for the symmetric expert file
  * only (hipfire 0.4.3 benchmarks page, "Read this before comparing columns":

@@ -27,6 +27,8 @@ MOE_WS_EXPERT_FFN = 3
 MOE_WS_LAYER_I8 = 4
 MOE_WS_EXPERT_FFN_I8 = 5
 
+MOE_STATIC_WS_BYTES = 128 << 20   # the static workspace of moe_layer_forward_static
+
 # Every symbol include/moe.h declares.
 EXPORTED = [
     "moe_abi_version",
@@ -37,6 +39,7 @@ EXPORTED = [
     "moe_expert_ffn",
     "moe_combine",
     "moe_layer_forward",
+    "moe_layer_forward_static",
     "moe_quantize_rows_i8",
     "moe_expert_ffn_i8",
     "moe_layer_forward_i8",
@@ -117,6 +120,8 @@ def lib():
     L.moe_combine.argtypes = [sp, i64, P, P, P, P, P, P, P, P]
     L.moe_layer_forward.restype = st
     L.moe_layer_forward.argtypes = [sp, i64, P, P, P, P, ep, P, P, P, ctypes.c_size_t, P]
+    L.moe_layer_forward_static.restype = st
+    L.moe_layer_forward_static.argtypes = [sp, i64, P, P, P, P, ep, P, P, P]
     L.moe_quantize_rows_i8.restype = st
     L.moe_quantize_rows_i8.argtypes = [i64, i64, P, P, P, P]
     L.moe_expert_ffn_i8.restype = st

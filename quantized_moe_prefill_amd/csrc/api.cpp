@@ -533,6 +533,108 @@ static size_t stage_slot_bytes(const StageLayout& L, int n) {
   return al(L.w13 * n) + al(L.s13 * n) + al(L.w2 * n) + al(L.s2 * n);
 }
 
+
+// Arguments of moe_layer_forward and moe_layer_forward_static (everything
+// but the workspace).
+static moe_status_t check_layer_args(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                     const float* w_router, const float* router_bias,
+                                     const float* shared_gate, const moe_experts_t* experts,
+                                     const uint16_t* residual, uint16_t* out, Shape* sp) {
+  Shape& s = *sp;
+  moe_status_t st = check_shape(shape, T, &s);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  QMOE_REQUIRE(x, "x");
+  QMOE_REQUIRE(w_router, "w_router");
+  QMOE_REQUIRE(out, "out");
+  QMOE_OPTIONAL(router_bias, "router_bias");
+  QMOE_OPTIONAL(residual, "residual");
+  st = check_experts(s, experts);
+  if (st != MOE_OK) return st;
+  if (s.Is > 0) {
+    QMOE_REQUIRE(shared_gate, "shared_gate");
+  } else if (shared_gate != nullptr) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate given but shared_inter == 0");
+  }
+  return MOE_OK;
+}
+
+// The layer on a validated call, with scratch carved from `b` (at least
+// layer_layout(s, T).total bytes).
+static moe_status_t layer_run(const Shape& s, int64_t T, const uint16_t* x,
+                              const float* w_router, const float* router_bias,
+                              const float* shared_gate, const moe_experts_t* experts,
+                              const uint16_t* residual, uint16_t* out, uint8_t* b,
+                              hipStream_t stream) {
+  moe_status_t st;
+  const Layout L = layer_layout(s, T);
+  auto* split = reinterpret_cast<uint16_t*>(b + L.split);
+  auto* partial = reinterpret_cast<float*>(b + L.partial);
+  auto* hist = reinterpret_cast<int32_t*>(b + L.hist);
+  auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
+  auto* tw = reinterpret_cast<float*>(b + L.tw);
+  auto* sw = s.Is > 0 ? reinterpret_cast<float*>(b + L.sw) : nullptr;
+  auto* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  auto* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  auto* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  auto* inv = reinterpret_cast<int32_t*>(b + L.inv);
+  auto* x16 = reinterpret_cast<uint16_t*>(b + L.x16);
+  auto* h = reinterpret_cast<uint16_t*>(b + L.h);
+  auto* hs = reinterpret_cast<uint16_t*>(b + L.hs);
+  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
+  auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
+
+  if (router_uses_gemv((int)T)) {
+    // a few tokens: the router product, then top-k and grouping in one workgroup
+    QMOE_HIP(launch_route_permute_small(x, w_router, shared_gate, partial, router_bias, (int)T,
+                                        s.H, s.E, s.k, ids, tw, sw, counts, offsets, sorted, inv,
+                                        stream),
+             "router launch");
+  } else {
+    st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
+                    partial, x16, stream);
+    if (st != MOE_OK) return st;
+    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
+             "permute launch");
+  }
+  st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs,
+                !router_uses_gemv((int)T), stream);
+  if (st != MOE_OK) return st;
+  QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
+           "combine launch");
+  return MOE_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// static workspace of moe_layer_forward_static
+// ---------------------------------------------------------------------------
+
+// One array per GPU the library runs on, held until the process ends. In
+// host code `scratch` is only a stand-in for the symbol: the device address
+// of each GPU's copy comes from hipGetSymbolAddress with that GPU current.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WS_BYTES];
+
+static std::mutex g_scratch_mu;
+static std::vector<uint8_t*> g_scratch_dev;  // device address per device index
+
+// The current device's copy of `scratch`, looked up once per device.
+static moe_status_t static_workspace(uint8_t** out) {
+  int dev = 0;
+  QMOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_dev.size()) g_scratch_dev.resize(dev + 1, nullptr);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    QMOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(MOE_ERR_HIP, "static workspace: unexpected device address %p", p);
+    g_scratch_dev[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 }  // namespace qmoe
 
 using namespace qmoe;
@@ -686,60 +788,35 @@ moe_status_t moe_layer_forward(const moe_shape_t* shape, int64_t T, const uint16
                                const uint16_t* residual, uint16_t* out, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
   Shape s;
-  moe_status_t st = check_shape(shape, T, &s);
+  moe_status_t st = check_layer_args(shape, T, x, w_router, router_bias, shared_gate, experts,
+                                     residual, out, &s);
+  if (st != MOE_OK || T == 0) return st;
+  st = check_ws(ws, ws_bytes, layer_layout(s, T).total);
   if (st != MOE_OK) return st;
-  if (T == 0) return MOE_OK;
-  QMOE_REQUIRE(x, "x");
-  QMOE_REQUIRE(w_router, "w_router");
-  QMOE_REQUIRE(out, "out");
-  QMOE_OPTIONAL(router_bias, "router_bias");
-  QMOE_OPTIONAL(residual, "residual");
-  st = check_experts(s, experts);
-  if (st != MOE_OK) return st;
-  if (s.Is > 0) {
-    QMOE_REQUIRE(shared_gate, "shared_gate");
-  } else if (shared_gate != nullptr) {
-    return fail(MOE_ERR_INVALID_ARGUMENT, "shared_gate given but shared_inter == 0");
-  }
-  const Layout L = layer_layout(s, T);
-  st = check_ws(ws, ws_bytes, L.total);
-  if (st != MOE_OK) return st;
-  uint8_t* b = static_cast<uint8_t*>(ws);
-  auto* split = reinterpret_cast<uint16_t*>(b + L.split);
-  auto* partial = reinterpret_cast<float*>(b + L.partial);
-  auto* hist = reinterpret_cast<int32_t*>(b + L.hist);
-  auto* ids = reinterpret_cast<int32_t*>(b + L.ids);
-  auto* tw = reinterpret_cast<float*>(b + L.tw);
-  auto* sw = s.Is > 0 ? reinterpret_cast<float*>(b + L.sw) : nullptr;
-  auto* counts = reinterpret_cast<int32_t*>(b + L.counts);
-  auto* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
-  auto* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
-  auto* inv = reinterpret_cast<int32_t*>(b + L.inv);
-  auto* x16 = reinterpret_cast<uint16_t*>(b + L.x16);
-  auto* h = reinterpret_cast<uint16_t*>(b + L.h);
-  auto* hs = reinterpret_cast<uint16_t*>(b + L.hs);
-  auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
-  auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
+  return layer_run(s, T, x, w_router, router_bias, shared_gate, experts, residual, out,
+                   static_cast<uint8_t*>(ws), stream);
+}
 
-  if (router_uses_gemv((int)T)) {
-    // a few tokens: the router product, then top-k and grouping in one workgroup
-    QMOE_HIP(launch_route_permute_small(x, w_router, shared_gate, partial, router_bias, (int)T,
-                                        s.H, s.E, s.k, ids, tw, sw, counts, offsets, sorted, inv,
-                                        stream),
-             "router launch");
-  } else {
-    st = route_impl(s, T, x, w_router, router_bias, shared_gate, nullptr, ids, tw, sw, split,
-                    partial, x16, stream);
-    if (st != MOE_OK) return st;
-    QMOE_HIP(launch_permute(ids, (int)(T * s.k), s.E, counts, offsets, sorted, inv, hist, stream),
-             "permute launch");
-  }
-  st = ffn_impl(s, T, x, experts, counts, offsets, sorted, yperm, ysh, x16, h, hs,
-                !router_uses_gemv((int)T), stream);
+moe_status_t moe_layer_forward_static(const moe_shape_t* shape, int64_t T, const uint16_t* x,
+                                      const float* w_router, const float* router_bias,
+                                      const float* shared_gate, const moe_experts_t* experts,
+                                      const uint16_t* residual, uint16_t* out,
+                                      hipStream_t stream) {
+  Shape s;
+  moe_status_t st = check_layer_args(shape, T, x, w_router, router_bias, shared_gate, experts,
+                                     residual, out, &s);
+  if (st != MOE_OK || T == 0) return st;
+  const size_t need = layer_layout(s, T).total;
+  if (need > (size_t)MOE_STATIC_WS_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of workspace; the static workspace holds %zu "
+                "(use moe_layer_forward with a caller workspace, or fewer tokens per call)",
+                need, (size_t)MOE_STATIC_WS_BYTES);
+  uint8_t* ws = nullptr;
+  st = static_workspace(&ws);
   if (st != MOE_OK) return st;
-  QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
-           "combine launch");
-  return MOE_OK;
+  return layer_run(s, T, x, w_router, router_bias, shared_gate, experts, residual, out, ws,
+                   stream);
 }
 
 moe_status_t moe_quantize_rows_i8(int64_t rows, int64_t cols, const uint16_t* x, int8_t* q,

@@ -165,6 +165,23 @@ def moe_layer_forward(shape, x, w_router, router_bias, shared_gate, experts: Exp
     return out
 
 
+def moe_layer_forward_static(shape, x, w_router, router_bias, shared_gate, experts: Experts,
+                             residual=None, out=None):
+    """moe_layer_forward with its intermediates in the library's static
+    per-GPU workspace (no workspace argument; the call allocates nothing
+    besides `out` when it is not given)."""
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, shape.hidden), dtype=torch.bfloat16, device=dev)
+    N.check(N.lib().moe_layer_forward_static(
+        ctypes.byref(shape), T, _ptr(x, "x", _U16, dev), _ptr(w_router, "w_router", (torch.float32,), dev),
+        _ptr(router_bias, "router_bias", (torch.float32,), dev),
+        _ptr(shared_gate, "shared_gate", (torch.float32,), dev), experts.ref(),
+        _ptr(residual, "residual", _U16, dev), _ptr(out, "out", _U16, dev), _stream(dev)))
+    return out
+
+
 def moe_quantize_rows_i8(x):
     """bf16 rows [R][C] -> (int8 codes [R][C], fp32 scales [R])."""
     R, C = x.shape

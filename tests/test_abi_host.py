@@ -272,3 +272,25 @@ def test_streamed_validation_before_launch():
     assert call(ws_bytes=need - 1) == N.MOE_ERR_WORKSPACE_TOO_SMALL
     bad = (ctypes.c_int32 * E)(*([0] + [-1] * (E - 1)))
     assert call(hot_slot=bad, hot_count=0) == N.MOE_ERR_INVALID_ARGUMENT  # slot 0 of an empty hot set
+
+
+def test_static_layer_validation_before_launch():
+    """moe_layer_forward_static validates on the host like moe_layer_forward
+    and refuses a call whose workspace would not fit its static array, all
+    before touching a device."""
+    L = _lib()
+    s = _shape()  # H = 2048, E = 128, k = 8, I = 768
+    n = ctypes.c_size_t(0)
+    assert L.moe_layer_forward_static(ctypes.byref(s), 0, None, None, None, None, None, None, None, None) == N.MOE_OK
+    # missing x
+    ex = N.MoeExperts(FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, None, None, None)
+    assert L.moe_layer_forward_static(ctypes.byref(s), 4, None, FAKE, None, None, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
+    # shared gate on a shape without a shared expert
+    assert L.moe_layer_forward_static(ctypes.byref(s), 4, FAKE, FAKE, None, FAKE, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
+    # the largest T whose layer workspace fits, and the next one
+    assert N.MOE_STATIC_WS_BYTES == 128 << 20
+    for T in (2392, 2393):
+        assert L.moe_workspace_size(ctypes.byref(s), T, N.MOE_WS_LAYER, ctypes.byref(n)) == N.MOE_OK
+        assert (n.value <= N.MOE_STATIC_WS_BYTES) == (T == 2392)
+    assert L.moe_layer_forward_static(ctypes.byref(s), 2393, FAKE, FAKE, None, None, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert b"static workspace" in L.moe_last_error()
