@@ -18,6 +18,8 @@
     python bench.py --pmc-summary FETCH.csv WRITE.csv
                                           HBM bytes per launch from two rocprofv3
                                           --pmc runs (FETCH_SIZE, WRITE_SIZE)
+    python bench.py --pmc-table A.csv ... per-kernel averages of every counter of
+                                          rocprofv3 --pmc runs
 
 One step = one moe_layer_forward (route, permute, gate/up + SwiGLU, down,
 combine) over the workload's batch, with all inputs resident in HBM. Prints
@@ -113,6 +115,9 @@ def parse():
                          "(counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 counter_collection.csv files and exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar="CSV",
+                    help="per-kernel averages of every counter in rocprofv3 "
+                         "counter_collection.csv files, and exit")
     return ap.parse_args()
 
 
@@ -167,6 +172,38 @@ def pmc_summary(fetch_csv: str, write_csv: str) -> None:
               f"{w if w is not None else float('nan'):12.1f} {tot if tot else float('nan'):14.4g}")
     print(f"gemm source hash {gemm_source_hash()}, integer-route gemm source hash "
           f"{gemm_source_hash(I8_SOURCES)}")
+
+
+def pmc_table(csvs) -> None:
+    """Per-kernel averages (over dispatches) of every counter in one or more
+    rocprofv3 counter_collection.csv files, and ratios of them: non-MFMA
+    VALU and LDS instructions per MFMA instruction (SQ_INSTS_VALU counts the
+    MFMAs too)."""
+    import collections
+    import csv
+    import re
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csvs:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                name = re.sub(r"\(.*", "", name).replace("void ", "").strip()
+                if "MulFunctor" in name or "at::" in name:
+                    continue
+                per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for k in sorted(per):
+        avg = {c: sum(v) / len(v) for c, v in per[k].items()}
+        n = max(len(v) for v in per[k].values())
+        print(f"{k}  ({n} dispatches)")
+        for c in sorted(avg):
+            print(f"    {c:32s} {avg[c]:16.4g}")
+        mf = avg.get("SQ_INSTS_MFMA")
+        if mf:
+            if "SQ_INSTS_VALU" in avg:
+                print(f"    {'non-MFMA VALU per MFMA':32s} {(avg['SQ_INSTS_VALU'] - mf) / mf:16.3f}")
+            if "SQ_INSTS_LDS" in avg:
+                print(f"    {'LDS instructions per MFMA':32s} {avg['SQ_INSTS_LDS'] / mf:16.3f}")
 
 
 def cpu_baseline(cfg, li, x, min_seconds=10.0, max_passes=8, i8=False, mixed=None):
@@ -396,6 +433,9 @@ def main():
     a = parse()
     if a.pmc_summary:
         pmc_summary(*a.pmc_summary)
+        return
+    if a.pmc_table:
+        pmc_table(a.pmc_table)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the MoE layer is "

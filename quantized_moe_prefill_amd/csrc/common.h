@@ -56,6 +56,14 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about one fp32
+// ulp) in place of an IEEE division, which compiles to a ten-instruction
+// sequence; every caller rounds the result to fp16. Large |z| behaves:
+// e^-z overflows to infinity and the reciprocal to zero for very negative z.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
+
 // Eight bf16 values (x0..x7, two per word) -> fp16 in kperm chunk order
 // (positions 0..7 hold x0, x4, x1, x5, x2, x6, x3, x7); exact for
 // 2^-14 <= |x| <= 65504 (and zero), saturating beyond.

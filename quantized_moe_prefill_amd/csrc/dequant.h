@@ -10,25 +10,53 @@
 namespace qmoe {
 
 // Eight consecutive 4-bit weights (one 32-bit word) of one row -> eight fp16
-// weights in the kperm chunk order. OR-ing a nibble n into the fp16 pattern
-// 0x6400 gives exactly 1024 + n; subtracting 1032 (symmetric) or 1024
-// (asymmetric) is exact, and the final multiply (or fused multiply-add with
-// the min) rounds once.
-template <bool ASYM>
+// weights in the kperm chunk order: output word i holds the pair of elements
+// (i, i + 4), i.e. nibble i of the word's low and high halves. A nibble ORed
+// into the low four mantissa bits of the fp16 pattern 0x6400 gives exactly
+// 1024 + n; ORed into mantissa bits 4-7 of 0x5400 (exponent 6, so those bits
+// count in units of one) it gives exactly 64 + n. So nibbles 0 and 1 of each
+// half need no shift and nibbles 2 and 3 one shift of the word by 8:
+// thirteen instructions per word instead of fifteen. Subtracting 1032 or 72
+// (symmetric) or 1024 or 64 (asymmetric) is exact, and the final multiply
+// (or fused multiply-add with the min) rounds once. ONE_SHIFT = false gives
+// the form with a shift per nibble (the same values, one fewer live
+// register), for kernels that are at their register limit.
+template <bool ASYM, bool ONE_SHIFT = true>
 __device__ __forceinline__ f16x8 dequant8_f16(uint32_t w, f16x2 s2, f16x2 m2) {
-  const f16x2 off = ASYM ? f16x2{(_Float16)1024.0f, (_Float16)1024.0f}
-                         : f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
-  // the two constants live in registers so that mask-and-or is a single
-  // v_and_or_b32 (VOP3 takes no literal and at most one scalar operand on
-  // gfx9): the mask in a scalar register, the fp16 pattern in a vector one
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
-  uint32_t magic = 0x64006400u;
-  asm("" : "+v"(magic));
+  if constexpr (!ONE_SHIFT) {
+    const f16x2 off = ASYM ? f16x2{(_Float16)1024.0f, (_Float16)1024.0f}
+                           : f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000f000fu);
+    uint32_t magic = 0x64006400u;
+    asm("" : "+v"(magic));
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t t = ((w >> (4 * i)) & mask) | magic;  // (1024 + n_i, 1024 + n_{i+4})
+      const f16x2 n = __builtin_bit_cast(f16x2, t) - off;
+      const f16x2 v = ASYM ? __builtin_elementwise_fma(n, s2, m2) : n * s2;
+      o[i] = __builtin_bit_cast(uint32_t, v);
+    }
+    return __builtin_bit_cast(f16x8, o);
+  }
+  const f16x2 off_lo = ASYM ? f16x2{(_Float16)1024.0f, (_Float16)1024.0f}
+                            : f16x2{(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 off_hi = ASYM ? f16x2{(_Float16)64.0f, (_Float16)64.0f}
+                            : f16x2{(_Float16)72.0f, (_Float16)72.0f};
+  // the masks live in scalar registers and the fp16 patterns in vector ones,
+  // so that each mask-and-or is a single v_and_or_b32 (VOP3 takes no literal
+  // and at most one scalar operand on gfx9)
+  const uint32_t mask_lo = __builtin_amdgcn_readfirstlane(0x000f000fu);
+  const uint32_t mask_hi = __builtin_amdgcn_readfirstlane(0x00f000f0u);
+  uint32_t magic_lo = 0x64006400u, magic_hi = 0x54005400u;
+  asm("" : "+v"(magic_lo), "+v"(magic_hi));
+  const uint32_t w8 = w >> 8;
+  const uint32_t t[4] = {(w & mask_lo) | magic_lo, (w & mask_hi) | magic_hi,
+                         (w8 & mask_lo) | magic_lo, (w8 & mask_hi) | magic_hi};
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((w >> (4 * i)) & mask) | magic;  // (1024 + n_i, 1024 + n_{i+4})
-    const f16x2 n = __builtin_bit_cast(f16x2, t) - off;
+    const f16x2 n = __builtin_bit_cast(f16x2, t[i]) - ((i & 1) ? off_hi : off_lo);
     const f16x2 v = ASYM ? __builtin_elementwise_fma(n, s2, m2) : n * s2;
     o[i] = __builtin_bit_cast(uint32_t, v);
   }

@@ -67,7 +67,6 @@ __global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restric
   }
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
 
 // Slot swizzle of the activation tiles: chunk c of row r sits in slot
 // c ^ rowswz(r), the row's low four bits with their two halves swapped. A
@@ -406,7 +405,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // chunk c (elements 8c .. 8c+7 of the lane's 32-element K block) of one
   // fragment's packed weights -> eight fp16 weights
   auto dequant_chunk = [&](const WV& w, int c, f16x2 s2, f16x2 m2) {
-    if constexpr (BITS == 4) return dequant8_f16<ASYM>(w[c], s2, m2);
+    // (the down GEMM keeps the shift-per-nibble form: with the one-shift
+    // form its 128-row instance spills)
+    if constexpr (BITS == 4) return dequant8_f16<ASYM, GATEUP>(w[c], s2, m2);
     else if constexpr (BITS == 2) return dequant8_f16_b2(w[c >> 1], c & 1, s2);
     else return dequant8_f16_b3(w[c >> 1], w[2], c, s2);
   };
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int rl = mi * 16 + rq + v;
-            const float h = silu(acc[mi][j][v]) * acc[mi][j + 2][v];
+            const float h = silu_f32(acc[mi][j][v]) * acc[mi][j + 2][v];
             const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
             *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
                 (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);

@@ -128,7 +128,6 @@ struct TileI8 {
   uint32_t sc_src[2];  // byte offsets of the two scale slots' sources
 };
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
 
 // Eight packed codes (one word, byte j = elements 2j | 2j+1 << 4) -> two
 // words of int8 values 16 (n - 8): elements 0,2,4,6 and 1,3,5,7.
@@ -364,7 +363,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_i8_kernel(GemmI8 g, i
           for (int v = 0; v < 4; ++v) {
             const int rl = mi * 16 + rq + v;
             const float s = rsc[rl];
-            const float h = silu_f(s * acc[mi][j][v]) * (s * acc[mi][j + 2][v]);
+            const float h = silu_f32(s * acc[mi][j][v]) * (s * acc[mi][j + 2][v]);
             const int piece = (col >> 3) ^ ((rl >> 2) & 3);
             *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (col & 7) * 2) =
                 (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);

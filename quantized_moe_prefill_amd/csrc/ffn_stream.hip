@@ -284,7 +284,7 @@ __global__ __launch_bounds__(STHREADS, SWG_PER_CU) void expert_stream_kernel(Gro
         sum8(NF / 2 + (q >> 1), t, q & 1, uv);
         float hv[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) hv[c] = gv[c] / (1.f + __expf(-gv[c])) * uv[c];
+        for (int c = 0; c < 8; ++c) hv[c] = silu_f32(gv[c]) * uv[c];
         // kperm order inside the chunk: positions 0..7 hold columns 0,4,1,5,2,6,3,7
         u32x4 o;
 #pragma unroll

@@ -1,9 +1,10 @@
 """GPU checks of moe_layer_forward_streamed: cold experts in pinned host
 memory copied over PCIe into a staging buffer chunk by chunk, hot experts on
-the device. The expert GEMMs are the same kernels on the same tiles, so above
-16 tokens the output must equal moe_layer_forward's with every expert on the
-device bit for bit; at 16 tokens or fewer (where moe_layer_forward takes the
-weight-streaming kernels) it is gated against the oracle."""
+the device. Where moe_layer_forward runs the same tiled kernels (above 16
+tokens, and below the wide-tile kernel's average of 256 rows per expert)
+the output must equal its output bit for bit; elsewhere (at most 16 tokens:
+the weight-streaming kernels; the a3b_pp8192 batch: the wide-tile kernels)
+both are gated against the oracle."""
 from dataclasses import replace
 
 import numpy as np
@@ -45,9 +46,17 @@ def test_streamed_equals_resident_bitwise(name, hot, stage_experts):
 
 
 def test_streamed_full_size_a3b_pp8192():
+    """The bench batch with 32 hot experts: every output row against the
+    oracle (teacher-forced on the GPU logits), as is the resident layer's."""
     cfg = CONFIGS["a3b_pp8192"]
-    _, _, out, ref = run(cfg, list(range(32)), 24)
-    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    li, x, out, res = run(cfg, list(range(32)), 24)
+    shape = qm.shape_of(cfg)
+    logits, _, _, _ = qm.moe_route(shape, x, li.w_router, li.router_bias, None, want_logits=True)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(bits(x), li.to("cpu"), cfg.k, cfg.G, cfg.quant,
+                           logits32=logits.cpu().numpy())
+    gate(f64_of_bf16(out), ref["out"], "out (streamed, T=8192)")
+    gate(f64_of_bf16(res), ref["out"], "out (resident, T=8192)")
 
 
 @pytest.mark.parametrize("T", [1, 16])
