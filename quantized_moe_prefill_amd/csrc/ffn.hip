@@ -15,7 +15,8 @@
 // bytes = 32 K values per lane per fragment and stage, one stage ahead) and
 // dequantizes them in registers, so no weight is dequantized twice and no
 // weight touches LDS. v_mfma_f32_16x16x32_f16 with fp32 accumulators; the
-// results leave through a per-wave LDS sub-tile as 16-byte row pieces.
+// results leave through a per-wave LDS sub-tile as 16-byte row pieces
+// (gate/up with 3- or 2-bit weights: straight from the accumulators).
 //
 // The gate/up kernel pairs gate and up rows of the same intermediate columns
 // in one wave, so h = silu(g) * u is formed in registers and written once.
@@ -171,6 +172,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // each stage dequantizes the next stage's first K step (symmetric experts:
   // with a min per group the extra live registers spill)
   constexpr bool XDQ = !ASYM;
+  // Gate/up with 3- or 2-bit weights writes h straight from the accumulators
+  // (the LDS-staged epilogue below needs registers that the wider dequant of
+  // those widths already takes: the 3-bit instance spilled 45 of them and ran
+  // 1.4x slower); 4-bit gate/up and every down GEMM stage their results
+  // through the LDS, which leaves as whole row spans and measured faster.
+  constexpr bool DIRECT = GATEUP && BITS != 4;
   // a lane's packed weights of one fragment and stage: 4 * BITS bytes
   typedef uint32_t WV __attribute__((ext_vector_type(BITS)));
   __shared__ __attribute__((aligned(16))) uint8_t Sc[SCM != SC_STAGE ? NWAVES * SC_WAVE : 16];
@@ -250,11 +257,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     lg = lane_o >> 4;
   };
   refresh_lane();
-  auto frow = [&](int f) { return GATEUP ? 16 * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f; };
+  // Matrix-core row r of fragment f is weight row c0 + frow(f) + prow(r).
+  // With DIRECT the gate and up fragments interleave their rows in pairs:
+  // lane (r16, lg) ends with rows 4 lg .. 4 lg + 3 of each fragment, and
+  // fragments 0, 1 (gate; 2, 3 up) then give it positions
+  // 8 lg + 4 (f % 2) + 0..3 of the wave's 32 h columns in kperm chunk order,
+  // i.e. natural columns 8 lg + kperm(4 (f % 2) + 0..3) (kperm(4 + p) =
+  // kperm(p) + 2): eight consecutive h values, one 16-byte piece.
+  auto frow = [&](int f) {
+    return GATEUP ? (DIRECT ? 2 : 16) * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f;
+  };
+  auto prow = [&](int r) { return DIRECT ? 8 * (r >> 2) + kperm(r & 3) : r; };
 
   // Fragment f of a wave covers weight rows c0 + frow(f) + 0..15 of
-  // the expert (gate/up: fragments 0, 1 are gate columns c0 + 16 f, 2, 3 the
-  // up rows of the same columns). Lane (r16, lg) reads row r16 of each
+  // the expert (gate/up: fragments 0, 1 are gate columns, 2, 3 the up rows
+  // of the same columns). Lane (r16, lg) reads row prow(r16) of each
   // fragment, K values [32 lg, 32 lg + 32) of every stage (16 bytes), which
   // is also the K range its A fragments cover, so the two operands agree
   // without any reordering: one per-lane offset plus a uniform offset per
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // the expert's index in the weight tensors (a mixed layer's width
     // tensors hold only that width's experts)
     if (MIX) e = g.slot[e];
-    const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + r16;
+    const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + prow(r16);
     ts.b_lane = (uint32_t)wrow0 * wrow_bytes + lg * 4 * BITS;
     ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
     if (WIN) {
@@ -371,7 +388,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   auto read_win = [&](int kt, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-      const int off = (16 * f + r16) * 16 + (4 * (kt & 1) + lg) * 2;
+      const int wr = GATEUP ? (f >= 2 ? 32 : 0) + (DIRECT ? 2 : 16) * (f & 1) : 16 * f;
+      const int off = (wr + prow(r16)) * 16 + (4 * (kt & 1) + lg) * 2;
       rs[f] = *reinterpret_cast<const uint16_t*>(sc_wave + off);
       rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(sc_wave + SC_SLOT + off) : 0u;
     }
@@ -393,7 +411,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     const int grp = (lg * 32 + kt * BK) / g.G;
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-      const int row = GATEUP ? 16 * (f & 1) + r16 : 16 * f + r16;
+      const int row = (GATEUP ? (DIRECT ? 2 : 16) * (f & 1) : 16 * f) + prow(r16);
       const int off = (GATEUP && f >= 2 ? SC_SLOT : 0) + (row * KG + grp) * 2;
       rs[f] = *reinterpret_cast<const uint16_t*>(scw + off);
       rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(scw + SC_SLOT + off) : 0u;
@@ -416,9 +434,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // 16-row sub-tiles. Two waves share each SIMD, so the hardware interleaves
   // one wave's dequant and LDS reads with the other's MFMAs. Every sub-tile
   // is computed; rows past the end of an expert hold finite data whose
-  // results are never stored. The down GEMM swaps the operands
-  // (C^T = W A^T), so each lane ends up with four consecutive output
-  // columns of one row.
+  // results are never stored. The down GEMM (and DIRECT gate/up) swaps the
+  // operands (C^T = W A^T), so each lane ends up with four output columns of
+  // one row.
   auto compute_stage = [&](const uint8_t* __restrict__ as_base, const WV* cb, const uint32_t* rs,
                            const uint32_t* rm, f16x8* b, const WV* cbn, uint32_t* rsn,
                            uint32_t* rmn, int kt) {
@@ -467,8 +485,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         if (mi + 1 < MSUB) an = read_a(j, mi + 1);
 #pragma unroll
         for (int f = 0; f < NFRAG; ++f)
-          acc[mi][f] = GATEUP ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
-                              : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
+          acc[mi][f] = GATEUP && !DIRECT ? mfma_16x16x32_f16(a, b[f], acc[mi][f])
+                                         : mfma_16x16x32_f16(b[f], a, acc[mi][f]);
         if (mi < NFRAG) {
           if (j < 3) bn[mi] = dequant_chunk(cb[mi], j + 1, cs[mi], cm[mi]);
           else if (XDQ) bn[mi] = dequant_chunk(cbn[mi], 0, csn[mi], cmn[mi]);
@@ -491,7 +509,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     uint16_t* const C = ts.shared ? g.C2 : g.C;
     const int ldc = ts.shared ? g.ldc2 : g.ldc;
     asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
-    if (GATEUP) {
+    if (DIRECT) {
+      // eight consecutive h values of row 16 mi + r16 per lane (see frow):
+      // one 16-byte piece, 64 contiguous bytes of each of 16 rows per store
+      uint16_t* const crow = C + (int64_t)(row0 + rr) * ldc + ts.c0 + 2 * rq;
+#pragma unroll
+      for (int mi = 0; mi < MSUB; ++mi) {
+        float h[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          h[v] = silu_f32(acc[mi][v >> 2][v & 3]) * acc[mi][2 + (v >> 2)][v & 3];
+        const u32x4 d = {pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3]), pack_f16x2(h[4], h[5]),
+                         pack_f16x2(h[6], h[7])};
+        if (ts.cvalid && mi * 16 + rr < rows) st16(crow + (int64_t)(mi * 16) * ldc, d);
+      }
+    } else if (GATEUP) {
       uint8_t* sub = BM == 128 ? (wave < 4 ? As2 : Ex) + (wave & 3) * SUBW : Ex + wave * SUBW;
       // the 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four
       // row groups of one write land in different banks
@@ -553,9 +585,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     }
   };
 
-  // ---- persistent loop. K loop: activations two stages ahead in the LDS
-  // ring, weights one stage ahead in registers. Within a stage the weight
-  // loads are issued before the activation loads, so "at most ALD loads
+  // ---- persistent loop. K loop: weights one stage ahead in registers
+  // (issued at the top of each stage), activations into the ring slot two
+  // stages ahead (issued at the end of each stage), so "at most ALD loads
   // outstanding" at the end of stage s means: stage s+1's activations and
   // weights have landed (loads complete in issue order). Every stage issues
   // the same loads (past the last stage they repeat it, into a slot nobody
@@ -602,14 +634,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       uint32_t rsn[NFRAG], rmn[NFRAG];
       load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
       if (WIN && odd) load_win(cur, (kt + 1) >> 1);
-      load_a(cur, min(kt + 2, klast), nxt2);
-      // issue the loads here, a whole stage before they are needed: left to
-      // itself the scheduler sinks them to the end of the stage (to shorten
-      // register lifetimes), right before the wait for them
+      // issue the weight loads here, a whole stage before they are needed:
+      // left to itself the scheduler sinks them to the end of the stage (to
+      // shorten register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
       if (XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
       compute_stage(curs, cb, rs, rm, b0, cbn, rsn, rmn, kt);
       if (!XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
+      // The activation loads go last: their direct writes into the LDS then
+      // land while the stage ends and the next one starts, not in the middle
+      // of this stage's fragment reads (issued at the top of the stage they
+      // cost gate/up 1-3 % and down 2-4 %). They still have a whole stage to
+      // land, and being the last loads issued, "at most ALD outstanding"
+      // below still means this stage's weights have arrived.
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(cur, min(kt + 2, klast), nxt2);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       // (after the wait: a window refilled in this stage has landed)
       if (!XDQ && WIN) read_win(kt + 1, rsn, rmn);
@@ -647,9 +686,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     // own wait covers only its own loads, so every wave waits for all of its
     // loads and then meets the others at a barrier: after it, no direct
     // global->LDS load of this tile is still in flight anywhere in the
-    // workgroup, and the epilogue's LDS writes cannot be overwritten.
+    // workgroup, and the epilogue's LDS writes cannot be overwritten. (A
+    // DIRECT epilogue writes no LDS; its wave still waits for its own last
+    // load, which targets rows of the ring it loads again next.)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    lds_barrier();
+    if (!DIRECT) lds_barrier();
 
     const int next = tile + wgs_per_xcd;
     const bool has_next = next < t_end;
