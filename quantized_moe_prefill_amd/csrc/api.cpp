@@ -584,6 +584,55 @@ static moe_status_t layer_run(const Shape& s, int64_t T, const uint16_t* x,
   auto* yperm = reinterpret_cast<uint16_t*>(b + L.yperm);
   auto* ysh = s.Is > 0 ? reinterpret_cast<uint16_t*>(b + L.ysh) : nullptr;
 
+  if (router_uses_gemv((int)T) && (s.Is == 0 || shared_gate != nullptr) &&
+      small_layer_supported((int)T, s.H, s.I, s.Is, s.E, s.k, s.G)) {
+    // a few tokens: router logits, then top-k, grouping and gate/up in one
+    // launch, down in another (both with the shared expert), then combine
+    QMOE_HIP(launch_router_gemv(x, w_router, s.Is > 0 ? shared_gate : nullptr, (int)T, s.H, s.E,
+                                partial, stream),
+             "router launch");
+    SmallLayer a{};
+    a.x = x;
+    a.bias = router_bias;
+    a.w13 = experts->w13;
+    a.w13_scale = experts->w13_scale;
+    a.w13_min = s.asym ? experts->w13_min : nullptr;
+    a.w2 = experts->w2;
+    a.w2_scale = experts->w2_scale;
+    a.w2_min = s.asym ? experts->w2_min : nullptr;
+    a.s13 = experts->s13;
+    a.s13_scale = experts->s13_scale;
+    a.s13_min = s.asym ? experts->s13_min : nullptr;
+    a.s2 = experts->s2;
+    a.s2_scale = experts->s2_scale;
+    a.s2_min = s.asym ? experts->s2_min : nullptr;
+    a.T = (int)T;
+    a.H = s.H;
+    a.E = s.E;
+    a.k = s.k;
+    a.I = s.I;
+    a.G = s.G;
+    a.has_shared = s.Is > 0 ? 1 : 0;
+    a.Epad = router_padded_rows(s.E, s.Is > 0);
+    a.nbits = 0;
+    while ((1 << a.nbits) < s.E) ++a.nbits;
+    a.logits = partial;
+    a.h = h;
+    a.hs = hs;
+    a.yperm = yperm;
+    a.ysh = ysh;
+    a.ids = ids;
+    a.inv = inv;
+    a.sorted = sorted;
+    a.counts = counts;
+    a.offsets = offsets;
+    a.tw = tw;
+    a.sw = sw;
+    QMOE_HIP(launch_small_experts(a, stream), "expert launches");
+    QMOE_HIP(launch_combine(yperm, inv, tw, ysh, sw, residual, out, (int)T, s.H, s.k, stream),
+             "combine launch");
+    return MOE_OK;
+  }
   if (router_uses_gemv((int)T)) {
     // a few tokens: the router product, then top-k and grouping in one workgroup
     QMOE_HIP(launch_route_permute_small(x, w_router, shared_gate, partial, router_bias, (int)T,

@@ -105,6 +105,22 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// a[i] += w * (element i of eight bf16 / fp16 values)
+__device__ __forceinline__ void acc8_bf16(float* a, u32x4 v, float w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = fmaf(w, bf16lo(v[i]), a[2 * i]);
+    a[2 * i + 1] = fmaf(w, bf16hi(v[i]), a[2 * i + 1]);
+  }
+}
+__device__ __forceinline__ void acc8_f16(float* a, u32x4 v, float w) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[2 * i] = fmaf(w, f16lo(v[i]), a[2 * i]);
+    a[2 * i + 1] = fmaf(w, f16hi(v[i]), a[2 * i + 1]);
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -10,21 +10,6 @@ namespace qmoe {
 
 namespace {
 
-__device__ __forceinline__ void acc8_bf16(float* a, u32x4 v, float w) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[2 * i] = fmaf(w, bf16lo(v[i]), a[2 * i]);
-    a[2 * i + 1] = fmaf(w, bf16hi(v[i]), a[2 * i + 1]);
-  }
-}
-__device__ __forceinline__ void acc8_f16(float* a, u32x4 v, float w) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[2 * i] = fmaf(w, f16lo(v[i]), a[2 * i]);
-    a[2 * i + 1] = fmaf(w, f16hi(v[i]), a[2 * i + 1]);
-  }
-}
-
 // out[t] = sum_j w[t,j] y_perm[inv[t*k+j]] (+ sw[t] y_sh[t]) (+ res[t]);
 // y_perm and y_sh are fp16, res and out bf16.
 template <int K>

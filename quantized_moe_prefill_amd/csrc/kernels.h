@@ -125,6 +125,35 @@ bool stream_supported(const GroupedGemm& g, bool gateup);
 bool gemm_streams(const GroupedGemm& g, bool gateup);
 hipError_t launch_stream(const GroupedGemm& g, bool gateup, hipStream_t s, const char* name);
 
+// ---- the layer's experts for a few tokens (small.hip) -----------------
+struct SmallLayer {
+  const uint16_t* x;         // bf16 [T][H]
+  const float* bias;         // fp32 [E] router bias or NULL
+  // experts as in moe_experts_t (mins NULL: symmetric)
+  const uint8_t *w13, *w2, *s13, *s2;
+  const uint16_t *w13_scale, *w13_min, *w2_scale, *w2_min;
+  const uint16_t *s13_scale, *s13_min, *s2_scale, *s2_min;
+  int T, H, E, k, I, G, has_shared, Epad, nbits;
+  const float* logits;       // [T][Epad] fp32 (router_gemv; column E: the shared gate)
+  // outputs: h [T k][I], hs [T][I], yperm [T k][H], ysh [T][H] (fp16), and
+  // the selection and grouping (ids, tw, inv, sorted [T k], sw [T],
+  // counts [E], offsets [E + 1]) as route / permute write them
+  uint16_t *h, *hs, *yperm, *ysh;
+  int32_t *ids, *inv, *sorted, *counts, *offsets;
+  float *tw, *sw;
+};
+// shapes these kernels cover (T <= kRouterGemvT, k <= 8, E <= 256, G 32 or
+// 128, a shared expert of the routed experts' width, H and I whose
+// weight-streaming tilings they instantiate); the rest take the separate
+// routing and streaming kernels
+bool small_layer_supported(int T, int H, int I, int Is, int E, int k, int G);
+// Two launches, after the router logits: top-k, grouping and gate/up (with
+// the shared expert), then down (with the shared expert).
+hipError_t launch_small_experts(const SmallLayer& a, hipStream_t s);
+// The router logits alone for at most kRouterGemvT tokens (one plane, [T][Epad]).
+hipError_t launch_router_gemv(const uint16_t* x, const float* w_router, const float* shared_gate,
+                              int T, int H, int E, float* partial, hipStream_t s);
+
 // ---- integer route: 8-bit activations x symmetric 4-bit weights --------
 // Per-row 8-bit quantization of bf16 (or fp16) rows [rows][cols], cols % 8
 // == 0: q = rint(v * (127 / a)), s = a / 127, a = max |v| of the row (rows

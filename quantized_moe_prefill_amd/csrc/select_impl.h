@@ -1,0 +1,205 @@
+// Device code of the router shared by the router kernels and the fused
+// small-batch layer kernel: the top-k and softmax of one token's logits
+// (16 lanes per token) and one router row's fp32 products with a few tokens.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace qmoe {
+
+// (value, index) order used by the selection: larger value first, then the
+// lower index. idx < 0 marks "nothing".
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  return va > vb || (va == vb && ia < ib);
+}
+
+// DPP row patterns: after xor-1, xor-2 (quad_perm), half-mirror and mirror
+// exchanges every lane of a 16-lane row has combined all 16 lanes.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& bv, int& bi) {
+  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(bv)));
+  const int oi = dpp<CTRL>(bi);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float x) {
+  return x + __int_as_float(dpp<CTRL>(__float_as_int(x)));
+}
+
+// 16 lanes per token (16 tokens per 256-thread workgroup). Lane r holds the
+// logits of experts 64*i + 4*r + c (i < Q/4, c < 4). Each of the k rounds
+// takes the lane-local best, reduces it over the row with DPP exchanges and
+// retires the winner; lane j keeps round j's winner for the softmax.
+// Logits, top-k and softmax of token t (16 lanes per token: lane r of the
+// group); the selected ids also go to lds_ids[t * k + j] if it is given.
+template <int Q>
+__device__ __forceinline__ void select_token(
+    const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
+    const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out, int t,
+    int32_t* lds_ids, float* lds_w = nullptr, float* lds_sw = nullptr) {
+  // (any of the global outputs may be null; the LDS copies go where given)
+  auto put_sw = [&](float v) {
+    if (sw_out != nullptr) sw_out[t] = v;
+    if (lds_sw != nullptr) lds_sw[t] = v;
+  };
+  const int r = threadIdx.x & 15;
+  const bool live = t < T;
+  const int tt = live ? t : T - 1;
+  const int N = planes * Epad;
+
+  float v[Q];
+#pragma unroll
+  for (int i = 0; i < Q / 4; ++i) {
+    const int e0 = 64 * i + 4 * r;
+    f32x4 l = {0.f, 0.f, 0.f, 0.f};
+    if (e0 < Epad) {
+      if (planes == 1) {
+        l = *reinterpret_cast<const f32x4*>(P + (int64_t)tt * N + e0);
+      } else {
+        for (int s = 0; s < ksplit; ++s) {
+          const float* p = P + ((int64_t)s * T + tt) * N + e0;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(p + Epad);
+          const f32x4 c = *reinterpret_cast<const f32x4*>(p + 2 * Epad);
+          l += (a + b) + c;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = e0 + c;
+      float x = l[c];
+      if (e < E) {
+        if (bias != nullptr) x += bias[e];
+        if (logits_out != nullptr && live) logits_out[(int64_t)t * E + e] = x;
+      } else if (e == E && has_shared && live) {
+        put_sw(1.f / (1.f + expf(-x)));
+      }
+      v[4 * i + c] = x;
+    }
+  }
+  // the shared-gate column past the last lane's range (E a multiple of 64)
+  if (has_shared && E >= 16 * Q && r == 0 && live) {
+    float x = 0.f;
+    if (planes == 1) {
+      x = P[(int64_t)tt * N + E];
+    } else {
+      for (int s = 0; s < ksplit; ++s) {
+        const float* p = P + ((int64_t)s * T + tt) * N + E;
+        x += (p[0] + p[Epad]) + p[2 * Epad];
+      }
+    }
+    put_sw(1.f / (1.f + expf(-x)));
+  }
+
+  uint32_t avail = 0;  // bit q: v[q] is a candidate
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    if (64 * (q >> 2) + 4 * r + (q & 3) < E) avail |= 1u << q;
+
+  float m0 = 0.f, selv = 0.f;
+  int seli = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.f;
+    int bi = -1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = 64 * (q >> 2) + 4 * r + (q & 3);
+      if (((avail >> q) & 1) && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
+    }
+    best_step<kDppXor1>(bv, bi);
+    best_step<kDppXor2>(bv, bi);
+    best_step<kDppHalfMirror>(bv, bi);
+    best_step<kDppMirror>(bv, bi);
+    if (j == 0) m0 = bv;
+    if (r == j) { selv = bv; seli = bi; }
+    if (((bi & 63) >> 2) == r) avail &= ~(1u << (4 * (bi >> 6) + (bi & 3)));
+  }
+  // softmax over the k winners (the largest is round 0's)
+  const float ex = r < k ? expf(selv - m0) : 0.f;
+  float sum = sum_step<kDppXor1>(ex);
+  sum = sum_step<kDppXor2>(sum);
+  sum = sum_step<kDppHalfMirror>(sum);
+  sum = sum_step<kDppMirror>(sum);
+  if (live && r < k) {
+    const float wt = ex * (1.f / sum);
+    if (ids_out != nullptr) ids_out[(int64_t)t * k + r] = seli;
+    if (w_out != nullptr) w_out[(int64_t)t * k + r] = wt;
+    if (lds_ids != nullptr) lds_ids[t * k + r] = seli;
+    if (lds_w != nullptr) lds_w[t * k + r] = wt;
+  }
+}
+
+// L[t][n] = sum_h f32(x[t][h]) * w[n][h] for the E router rows and the
+// shared-gate row (n = E), T <= kRouterGemvT tokens. One workgroup per row
+// n; wave w takes the K quarter [w H/4, (w + 1) H/4), lane l the values 8 l
+// .. 8 l + 7 of every 512-wide piece of it, reading the fp32 row and every
+// token's bf16 values straight from memory. The per-lane sums are reduced
+// across the wave, then across the four waves, in a fixed order.
+// (256 threads; part: LDS scratch of the four waves' sums)
+__device__ __forceinline__ void router_row(const uint16_t* __restrict__ x,
+                                           const float* __restrict__ wr,
+                                           const float* __restrict__ sg, int T, int H, int E,
+                                           int Epad, int n, float* __restrict__ out,
+                                           float (*part)[kRouterGemvT]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rows = E + (sg != nullptr ? 1 : 0);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, kRsrcWord3);
+  float acc[kRouterGemvT];
+#pragma unroll
+  for (int t = 0; t < kRouterGemvT; ++t) acc[t] = 0.f;
+  if (n < rows) {
+    const float* wrow = n < E ? wr + (int64_t)n * H : sg;  // n == E: the shared gate
+    const int kq = H / 4;
+    for (int c = 0; c < kq; c += 512) {
+      const int k = wave * kq + c + 8 * lane;
+      if (c + 8 * lane < kq) {
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + k);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + k + 4);
+        u32x4 xv[kRouterGemvT];
+#pragma unroll
+        for (int t = 0; t < kRouterGemvT; ++t) {
+          // past the last token: past the end of x, which reads zero
+          const uint32_t off = t < T ? (uint32_t)(t * H + k) * 2u : 0x7ffffff0u;
+          xv[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        }
+#pragma unroll
+        for (int t = 0; t < kRouterGemvT; ++t) {
+          float a = acc[t];
+          a = fmaf(bf16lo(xv[t][0]), w0[0], a);
+          a = fmaf(bf16hi(xv[t][0]), w0[1], a);
+          a = fmaf(bf16lo(xv[t][1]), w0[2], a);
+          a = fmaf(bf16hi(xv[t][1]), w0[3], a);
+          a = fmaf(bf16lo(xv[t][2]), w1[0], a);
+          a = fmaf(bf16hi(xv[t][2]), w1[1], a);
+          a = fmaf(bf16lo(xv[t][3]), w1[2], a);
+          a = fmaf(bf16hi(xv[t][3]), w1[3], a);
+          acc[t] = a;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouterGemvT; ++t) acc[t] = wave_sum(acc[t]);
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < kRouterGemvT; ++t) part[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (tid < T) out[(int64_t)tid * Epad + n] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
+}  // namespace qmoe
