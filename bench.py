@@ -84,6 +84,7 @@ CALIB_BYTES = 1 << 30
 # (Evicting by writing instead leaves the cache full of dirty lines whose
 # write-back then halves the read bandwidth of the timed step.)
 STREAM_T = 16
+RAMP_S = 0.2   # seconds of untimed steps before the warm-up ones (clock ramp)
 FLUSH_BYTES = 1 << 30
 
 
@@ -547,6 +548,17 @@ def main():
                 layer.forward(x, out=out)
     torch.cuda.synchronize()
 
+    # Clock ramp: the GPU takes tens of milliseconds of sustained work to reach
+    # its steady clock, longer than a few warm-up steps of a sub-millisecond
+    # layer. Untimed steps for about RAMP_S seconds first (the same work as a
+    # step), then the W warm-up steps, then the K timed ones.
+    ramp_steps, t_ramp = 0, time.perf_counter()
+    per = 1 if stacked else 10
+    while time.perf_counter() - t_ramp < RAMP_S:
+        for _ in range(per):
+            step()
+        ramp_steps += per
+        torch.cuda.synchronize()
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -706,6 +718,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "clock_ramp_steps": ramp_steps,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",

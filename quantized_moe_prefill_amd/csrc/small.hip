@@ -24,7 +24,7 @@
 // on MI355X every agent-scope release writes back and every acquire
 // invalidates an XCD's whole L2, and with one per work item the layer took
 // 4-7x longer than separate launches, whose boundaries do that once.)
-#include "permute_impl.h"  // PMAXE
+#include "permute_impl.h"  // PMAXE, expert_scan
 #include "select_impl.h"
 #include "stream_impl.h"
 
@@ -41,30 +41,42 @@ template <int Q>
 __device__ __forceinline__ int small_list(const SmallLayer& a, int32_t* s_ids, float* s_tw,
                                           float* s_sw, int* s_inv, int* s_tok, int* s_tok_sh,
                                           int* s_grp, int* s_rows, int* s_row0, int* s_off,
-                                          int* s_cnt, int32_t* g_counts, int32_t* g_offsets) {
+                                          int* s_cnt, int* s_cnt_e, int* s_cnt_w0, int* s_wave,
+                                          int32_t* g_counts, int32_t* g_offsets) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, k = a.k, E = a.E, P = T * k;
-  if (tid >= P && tid < kRouterGemvT * 8) s_ids[tid] = -1;
+  if (tid < PMAXE) {
+    s_cnt_e[tid] = 0;
+    s_cnt_w0[tid] = 0;
+  }
   select_token<Q>(a.logits, 1, 1, T, E, a.Epad, k, a.bias, a.has_shared, nullptr, nullptr,
                   nullptr, nullptr, tid >> 4, s_ids, s_tw, s_sw);
   __syncthreads();
   // The grouping of the pairs by expert, stable (pair order within an
-  // expert), as the permutation kernels compute it; with at most 128 pairs
-  // each one's sorted row is simply counted: the pairs of lower experts plus
-  // the earlier pairs of its own (every lane reads the same id: broadcast).
-  // (s_ids is padded with -1 to a multiple of 4 ids and read 4 at a time)
-  const int P4 = (P + 3) >> 2;
-  const int4* ids4 = reinterpret_cast<const int4*>(s_ids);
-  int total = 0, off = 0;
+  // expert), as the permutation kernels compute it. At most 128 pairs, in
+  // waves 0 and 1: per-expert counts by LDS atomic adds (the totals do not
+  // depend on their order), offsets by a scan over the experts, and each
+  // pair's rank among the earlier pairs of its expert from one ballot per
+  // id bit (the lanes of its wave with the same id) plus, in wave 1, wave
+  // 0's count of that id.
+  int e = -1;
+  if (tid < P) {
+    e = s_ids[tid];
+    atomicAdd(&s_cnt_e[e], 1);
+    if (wave == 0) atomicAdd(&s_cnt_w0[e], 1);
+  }
+  uint64_t same = __ballot(tid < P);
+  for (int bit = 0; bit < a.nbits; ++bit) {
+    const bool on = tid < P && ((e >> bit) & 1);
+    const uint64_t bb = __ballot(on);
+    same &= on ? bb : ~bb;
+  }
+  const int rank = lanes_below(same);
+  __syncthreads();
+  const int total = tid < E ? s_cnt_e[tid] : 0;
+  const int off = expert_scan(total, s_wave);
   if (tid < E) {
-#pragma unroll 8
-    for (int q = 0; q < P4; ++q) {
-      const int4 v = ids4[q];
-      total += (v.x == tid) + (v.y == tid) + (v.z == tid) + (v.w == tid);
-      off += (v.x >= 0 && v.x < tid) + (v.y >= 0 && v.y < tid) + (v.z >= 0 && v.z < tid) +
-             (v.w >= 0 && v.w < tid);
-    }
     s_off[tid] = off;
     if (g_counts != nullptr) {
       g_counts[tid] = total;
@@ -72,18 +84,9 @@ __device__ __forceinline__ int small_list(const SmallLayer& a, int32_t* s_ids, f
       if (tid == E - 1) g_offsets[E] = off + total;
     }
   }
+  __syncthreads();
   if (tid < P) {
-    const int e = s_ids[tid];
-    int pos = 0;
-#pragma unroll 8
-    for (int q = 0; q < P4; ++q) {
-      const int4 v = ids4[q];
-      const int b = 4 * q;
-      pos += (v.x >= 0 && (v.x < e || (v.x == e && b < tid))) +
-             (v.y >= 0 && (v.y < e || (v.y == e && b + 1 < tid))) +
-             (v.z >= 0 && (v.z < e || (v.z == e && b + 2 < tid))) +
-             (v.w >= 0 && (v.w < e || (v.w == e && b + 3 < tid)));
-    }
+    const int pos = s_off[e] + (wave == 1 ? s_cnt_w0[e] : 0) + rank;
     s_inv[tid] = pos;
     s_tok[pos] = tid / k;
   }
@@ -127,13 +130,14 @@ __global__ __launch_bounds__(STHREADS, 2) void small_gateup_kernel(SmallLayer a)
   __shared__ __attribute__((aligned(16))) int32_t s_ids[kRouterGemvT * 8];
   __shared__ float s_tw[kRouterGemvT * 8], s_sw[kRouterGemvT];
   __shared__ int s_inv[kRouterGemvT * 8];
-  __shared__ int s_off[PMAXE];
-  __shared__ int s_cnt[SWAVES];
+  __shared__ int s_off[PMAXE], s_cnt_e[PMAXE], s_cnt_w0[PMAXE];
+  __shared__ int s_cnt[SWAVES], s_wave[SWAVES];
 
   const int tid = threadIdx.x;
   const bool first = blockIdx.x == 0;
   const int n_act = small_list<Q>(a, s_ids, s_tw, s_sw, s_inv, s_tok, s_tok_sh, s_grp, s_rows,
-                                  s_row0, s_off, s_cnt, first ? a.counts : nullptr, a.offsets);
+                                  s_row0, s_off, s_cnt, s_cnt_e, s_cnt_w0, s_wave,
+                                  first ? a.counts : nullptr, a.offsets);
   const int T = a.T, k = a.k, P = T * k;
   if (first) {
     // the selection and grouping for the down and combine launches
@@ -277,11 +281,17 @@ hipError_t launch_small_inst(const SmallLayer& a, hipStream_t s) {
   {
     constexpr int NFG = NSG == 1 ? 4 : 2;
     LaunchScope ls("gateup_gemm", s);
-    // (16 logits per selection lane cover E <= 256; the top-k does not
-    // depend on how the logits are dealt to the lanes)
-    auto kern = small_gateup_kernel<ASYM, G, NSG, 16>;
-    hipLaunchKernelGGL(kern, dim3(small_grid(kern, (int64_t)slots * (a.I / (8 * NFG)))),
-                       dim3(STHREADS), 0, s, a);
+    // (8 logits per selection lane cover E <= 128, 16 E <= 256: each round
+    // of the top-k costs in proportion)
+    if (a.E <= 128) {
+      auto kern = small_gateup_kernel<ASYM, G, NSG, 8>;
+      hipLaunchKernelGGL(kern, dim3(small_grid(kern, (int64_t)slots * (a.I / (8 * NFG)))),
+                         dim3(STHREADS), 0, s, a);
+    } else {
+      auto kern = small_gateup_kernel<ASYM, G, NSG, 16>;
+      hipLaunchKernelGGL(kern, dim3(small_grid(kern, (int64_t)slots * (a.I / (8 * NFG)))),
+                         dim3(STHREADS), 0, s, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
