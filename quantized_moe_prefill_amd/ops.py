@@ -438,3 +438,21 @@ class MoEStack:
             for layer in self.layers:
                 self.layer_step(layer, xc)
         return x
+
+    def capture(self, x: torch.Tensor) -> "torch.cuda.CUDAGraph":
+        """The whole stack on the buffer x, captured once as a HIP graph:
+        graph.replay() then applies all the layers to x's current contents in
+        place, without a launch per kernel (every step only enqueues kernels
+        on the current stream: no allocation, memset or host sync). x must
+        stay allocated, and its contents are consumed by the warm-up run."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward(x)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x)
+        torch.cuda.synchronize()
+        return graph

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import quantized_moe_prefill_amd as qm
-from synth import CONFIGS, make_layer, make_tokens
+from synth import CONFIGS, make_layer, make_stack_layer, make_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -52,3 +52,31 @@ def test_layer_graph_replay(name, T):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(bits16(out), bits16(ref)), f"replay {i} differs from the eager call"
+
+
+def test_stack_graph_replay():
+    """Eight layers of the stack40 shape (256 experts, asymmetric G = 32,
+    shared expert, RMSNorm + residual) on 16 tokens, captured once with
+    MoEStack.capture: every replay, on fresh input contents with eager work
+    in between, gives the bits of the eager stack."""
+    cfg = replace(CONFIGS["stack40"], T=16, n_layers=8)
+    layers = [make_stack_layer(cfg, l, device=DEV) for l in range(cfg.n_layers)]
+    stack = qm.MoEStack(cfg, layers, DEV, eps=cfg.rms_eps, chunk=16)
+    x = make_tokens(cfg, device=DEV, rows=16)
+    x2 = make_tokens(replace(cfg, seed=cfg.seed + 1), device=DEV, rows=16)
+    ref1 = stack.forward(x.clone())
+    ref2 = stack.forward(x2.clone())
+    torch.cuda.synchronize()
+    assert not torch.equal(bits16(ref1), bits16(ref2))
+    buf = x.clone()
+    graph = stack.capture(buf)
+    for i in range(4):
+        src, ref = (x, ref1) if i % 2 == 0 else (x2, ref2)
+        buf.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits16(buf), bits16(ref)), f"replay {i} differs from the eager stack"
+        # eager work on the same layers between replays
+        stack.forward(x2.clone())
+        torch.cuda.synchronize()
