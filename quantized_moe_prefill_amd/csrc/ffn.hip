@@ -98,18 +98,15 @@ __device__ __forceinline__ void gather_rows(const GroupedGemm& g, int row0, int 
   }
 }
 
-// What one tile of the expert GEMM needs besides the shared setup: its
-// rows, this lane's activation sources and weight offsets. (At namespace
-// scope: a class local to a kernel template keeps the compiler from emitting
-// the kernel's host-side launch stub.)
-struct GemmTile {
-  int row0, rows, c0;
-  bool cvalid;
-  int shared;  // the tile belongs to the extra group (uniform)
-  uint32_t a_off[ALD];  // byte offsets of this lane's activation loads
-  uint32_t b_lane, s_lane;
-  uint32_t sc_src[2];  // scale tiles in LDS: byte offsets of the two 1 KB sources
-  uint32_t win_lane;   // scale windows: byte offset of this lane's row's groups
+// The uniform description of one tile: a block of BM sorted rows of one
+// expert (or of the extra group) times one N tile. (At namespace scope: a
+// class local to a kernel template keeps the compiler from emitting the
+// kernel's host-side launch stub.)
+struct TileU {
+  int row0, rows;  // first sorted row of the block and its valid rows
+  int e;           // the expert's index in the weight tensors (0: extra group)
+  int shared;      // the tile belongs to the extra group
+  int c0;          // this wave's first weight row (gate/up: h column) in it
 };
 
 // Scales (and mins) of a tile in LDS: each wave's rows take two 1 KB slots,
@@ -141,17 +138,16 @@ template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = f
           int TBM = 128>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   static_assert(TBM == 128 || TBM == 64, "tile rows");
+  static_assert(TBM / 4 / NWAVES <= 4, "activation loads per wave");
   // this instance's tile height and what follows from it (the names hide
   // the 128-row constants above)
   constexpr int BM = TBM;
   constexpr int MSUB = BM / 16;
   constexpr int ALD = BM / 4 / NWAVES;  // direct activation loads per wave and stage
   constexpr int A_STAGE_BYTES = BM * BK * 2;
-  // epilogue sub-tiles: gate/up BM rows x 64 B per wave; down 64-row halves
-  // x 128 B per wave. 128-row tiles put waves 0-3 in As2, 4-7 in Ex; 64-row
-  // tiles put all eight in Ex.
-  constexpr int SUBW = GATEUP ? BM * 64 : 64 * 128;
-  constexpr int EX_BYTES = BM == 128 ? (NWAVES - 2 * ASTAGES) * SUB_BYTES : NWAVES * SUBW;
+  // epilogue: a 4 KB sub-tile per wave, filled and emptied in passes of 64
+  // rows x 64 B (h) or 32 rows x 128 B (y)
+  constexpr int SUBW = 4096;
   // LDS, two uses:
   //  - K loop: a ring of three activation tiles (As0..As2), BM rows x 128
   //    fp16 each, no padding; the 16-byte chunk c of row r sits in slot
@@ -159,14 +155,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   //    bank conflicts and lets a direct global->LDS load fill four whole rows.
   //    Separate arrays (and a K loop unrolled by three) let the compiler see
   //    that a stage's LDS reads never touch the tiles still being loaded, so
-  //    it does not wait for those loads before reading;
-  //  - epilogue: each wave's output sub-tile (BM rows x 64 B for h, 64-row
-  //    halves x 128 B for y) in As2 and Ex, so the results leave in whole
-  //    16-byte row pieces.
+  //    it does not wait for those loads before reading. The ring runs on
+  //    across tiles: a tile's first stage sits in the slot after its
+  //    predecessor's last;
+  //  - epilogue: each wave's output sub-tile in Ex, which no direct load
+  //    ever targets, so that the results leave as 16-byte row pieces while
+  //    the next tile's first stages are already landing in the ring.
   __shared__ __attribute__((aligned(16))) uint8_t As0[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As1[A_STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t As2[A_STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t Ex[EX_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t Ex[NWAVES * SUBW];
   constexpr bool SCL = SCM == SC_TILE;
   constexpr bool WIN = SCM == SC_WINDOW;
   // each stage dequantizes the next stage's first K step (symmetric experts:
@@ -182,12 +180,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   typedef uint32_t WV __attribute__((ext_vector_type(BITS)));
   __shared__ __attribute__((aligned(16))) uint8_t Sc[SCM != SC_STAGE ? NWAVES * SC_WAVE : 16];
   __shared__ int s_scan[258];
+  // per group: first sorted row and row count (tile decoding without global
+  // loads), and a mixed layer's weight slot
+  __shared__ int s_offs[257];
+  __shared__ int s_cnts[257];
+  __shared__ int s_slot[MIX ? 256 : 1];
+  // the gathered activation rows of the next tile, 64 per wave (a direct
+  // 4-byte-per-lane load of the gather map; each wave reads its own)
+  __shared__ __attribute__((aligned(16))) int s_gidx[NWAVES][64];
   __shared__ int s_wave[NWAVES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = g.K, N = g.N;
   const int KG = K / g.G;
   const int nk = K / BK;
+  const int Nc = GATEUP ? N / 2 : N;  // columns of the output
 
   // ---- tile list: per-expert tile prefix (tiles of BM rows) ----
   int n_mtiles;
@@ -195,8 +203,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   const int ngrp = g.E + (has2 ? 1 : 0);
   if (g.counts != nullptr) {
     // (a launch for one width of a mixed layer takes only that width's experts)
-    const int c = tid < g.E ? ((!MIX || g.tier[tid] == g.tier_id) ? g.counts[tid] : 0)
+    const int cnt = tid < g.E ? g.counts[tid] : 0;
+    const int c = tid < g.E ? ((!MIX || g.tier[tid] == g.tier_id) ? cnt : 0)
                             : (has2 && tid == g.E ? g.rows2 : 0);
+    if (tid < g.E) {
+      s_offs[tid] = g.offsets[tid];
+      s_cnts[tid] = cnt;
+      if (MIX) s_slot[tid] = g.slot[tid];
+    }
     int incl = (c + BM - 1) / BM;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -234,6 +248,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       __builtin_amdgcn_make_buffer_rsrc((void*)g.Wscale, 0, n_groups * N * KG * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ASYM ? g.Wmin : g.Wscale), 0, n_groups * N * KG * 2, kRsrcWord3);
+  // the gather map: max_rows entries
+  const __amdgpu_buffer_rsrc_t rG = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.gather, 0, g.gather != nullptr ? g.max_rows * 4 : 0, kRsrcWord3);
   const int s_step = (BK / g.G) * 2;  // scale bytes per stage along a row
   // the extra group's operands (one expert)
   const __amdgpu_buffer_rsrc_t rA2 =
@@ -269,17 +286,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   };
   auto prow = [&](int r) { return DIRECT ? 8 * (r >> 2) + kperm(r & 3) : r; };
 
-  // Fragment f of a wave covers weight rows c0 + frow(f) + 0..15 of
-  // the expert (gate/up: fragments 0, 1 are gate columns, 2, 3 the up rows
-  // of the same columns). Lane (r16, lg) reads row prow(r16) of each
-  // fragment, K values [32 lg, 32 lg + 32) of every stage (16 bytes), which
-  // is also the K range its A fragments cover, so the two operands agree
-  // without any reordering: one per-lane offset plus a uniform offset per
-  // fragment and stage.
-  auto setup = [&](int tile, GemmTile& ts) {
+  // ---- a tile: decoding, and this lane's load offsets ----
+  auto decode = [&](int tile) {
     const int mtile = tile / n_ntiles;
     const int ntile = tile - mtile * n_ntiles;
-    int e;
+    int e = 0, shared = 0, row0, rows;
     if (g.counts != nullptr) {
       // largest e with s_scan[e] <= mtile (binary search over the prefixes)
       int lo = 0, hi = ngrp;  // s_scan[lo] <= mtile < s_scan[hi]
@@ -289,81 +300,120 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       }
       e = lo;
       const int local = mtile - s_scan[e];
-      ts.shared = FOLD ? __builtin_amdgcn_readfirstlane(e == g.E ? 1 : 0) : 0;
-      if (ts.shared) {
+      shared = FOLD && e == g.E ? 1 : 0;
+      if (shared) {
         e = 0;
-        ts.row0 = local * BM;
-        ts.rows = min(BM, g.rows2 - ts.row0);
+        row0 = local * BM;
+        rows = min(BM, g.rows2 - row0);
       } else {
-        ts.row0 = g.offsets[e] + local * BM;
-        ts.rows = min(BM, g.counts[e] - local * BM);
+        row0 = s_offs[e] + local * BM;
+        rows = min(BM, s_cnts[e] - local * BM);
+        // (the expert's index in the weight tensors: a mixed layer's width
+        // tensors hold only that width's experts)
+        if (MIX) e = s_slot[e];
       }
     } else {
-      e = 0;
-      ts.shared = 0;
-      ts.row0 = mtile * BM;
-      ts.rows = min(BM, g.rows_single - ts.row0);
+      row0 = mtile * BM;
+      rows = min(BM, g.rows_single - row0);
     }
-    // load i of wave w fills rows 4 (ALD w + i) .. +3; lane l covers row
-    // 4 (ALD w + i) + l/16, LDS slot l%16, i.e. source chunk (l%16) ^ rowswz(row)
+    TileU t;
+    t.row0 = __builtin_amdgcn_readfirstlane(row0);
+    t.rows = __builtin_amdgcn_readfirstlane(rows);
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.shared = __builtin_amdgcn_readfirstlane(shared);
+    t.c0 = __builtin_amdgcn_readfirstlane(GATEUP ? ntile * (BN / 2) + wave * 32
+                                                 : ntile * BN + wave * 64);
+    return t;
+  };
+  // the first weight row of the wave's rows of tile t (uniform)
+  auto wrow_first = [&](const TileU& t) { return t.e * N + (t.c0 < Nc ? t.c0 : 0); };
+  // Load i of wave w fills rows 4 (ALD w + i) .. +3; lane l covers row
+  // 4 (ALD w + i) + l/16, LDS slot l%16, i.e. source chunk (l%16) ^ rowswz(row).
+  auto a_offset = [&](int src, int i) {
+    const int r = 4 * (ALD * wave + i) + lg;
+    return (uint32_t)(src * (K / 8) + (r16 ^ rowswz(r))) * 16u;
+  };
+  // the activation offsets of tile t from gathers straight from memory
+  // (rows past the expert's end read the tile's first row: finite data
+  // whose outputs are never stored)
+  auto aoff_mem = [&](const TileU& t, uint32_t* ao) {
     int src[ALD];
-    gather_rows<ALD>(g, ts.row0, ts.rows, 4 * ALD * wave + lg, 4, src, ts.shared != 0);
+    gather_rows<ALD>(g, t.row0, t.rows, 4 * ALD * wave + lg, 4, src, t.shared != 0);
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) ao[i] = a_offset(src[i], i);
+  };
+  // the gather map entries of tile t's rows of this wave into s_gidx[wave]
+  auto load_gidx = [&](const TileU& t) {
+    if (g.gather != nullptr && !t.shared)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rG, (lds_void_t*)&s_gidx[wave][0], 4,
+                                               (uint32_t)lane_o * 4u,
+                                               (t.row0 + 4 * ALD * wave) * 4, 0, 0);
+  };
+  // the activation offsets of tile t from s_gidx (rows past the expert's
+  // end read activation row 0 when gathered, the tile's first row if not)
+  auto aoff_lds = [&](const TileU& t, uint32_t* ao) {
+    const bool gath = g.gather != nullptr && !t.shared;
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
       const int r = 4 * (ALD * wave + i) + lg;
-      ts.a_off[i] = (uint32_t)(src[i] * (K / 8) + (r16 ^ rowswz(r))) * 16u;
+      int src;
+      if (gath) src = r < t.rows ? s_gidx[wave][4 * i + lg] / g.gather_div : 0;
+      else src = t.row0 + (r < t.rows ? r : 0);
+      ao[i] = a_offset(src, i);
     }
-    ts.c0 = GATEUP ? ntile * (BN / 2) + wave * 32 : ntile * BN + wave * 64;
-    ts.cvalid = ts.c0 < (GATEUP ? N / 2 : N);
-    // the expert's index in the weight tensors (a mixed layer's width
-    // tensors hold only that width's experts)
-    if (MIX) e = g.slot[e];
-    const int wrow0 = e * N + (ts.cvalid ? ts.c0 : 0) + prow(r16);
-    ts.b_lane = (uint32_t)wrow0 * wrow_bytes + lg * 4 * BITS;
-    ts.s_lane = ((uint32_t)wrow0 * KG + (lg * 32) / g.G) * 2;
+  };
+  // ---- loads. The load state names the tile whose activations (ash, aoff)
+  // and weights (wsh, bl, sl, wl) are loaded next: the current tile's until
+  // its last stages switch them to the next tile's. ----
+  // byte offsets of this lane's activation loads (the first ALD; a
+  // fixed-size array: one sized by the template's ALD, captured by the
+  // lambdas below, keeps the compiler from emitting the host-side launch
+  // stub)
+  uint32_t aoff[4];
+  uint32_t bl = 0;     // this lane's packed weights
+  uint32_t sl = 0;     // SC_STAGE: this lane's scales
+  uint32_t wl = 0;     // SC_WINDOW: this lane's row's scale groups
+  int ash = 0, wsh = 0;
+  auto set_w = [&](const TileU& t) {
+    const int wr0 = wrow_first(t);
+    bl = (uint32_t)(wr0 + prow(r16)) * wrow_bytes + lg * 4 * BITS;
+    if (SCM == SC_STAGE) sl = ((uint32_t)(wr0 + prow(r16)) * KG + (lg * 32) / g.G) * 2;
     if (WIN) {
       // lane l loads the window of the wave's weight row l: gate/up lanes
       // 0-31 the gate rows c0 + l, 32-63 the up rows of the same columns
       const int l = lane_o;
       const int wr = GATEUP ? (l < 32 ? l : N / 2 + l - 32) : l;
-      ts.win_lane = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0) + wr) * KG * 2;
+      wl = (uint32_t)(wr0 + wr) * KG * 2;
     }
-    if (SCL) {
-      const uint32_t r0 = (uint32_t)(e * N + (ts.cvalid ? ts.c0 : 0));  // e = 0 for the extra group
-      const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
-      ts.sc_src[0] = s0;
-      ts.sc_src[1] = GATEUP ? __builtin_amdgcn_readfirstlane((r0 + N / 2) * KG * 2)
-                            : (ASYM ? s0 : s0 + SC_SLOT);
-    }
+    wsh = t.shared;
   };
-  auto load_a = [&](const GemmTile& ts, int kt, uint8_t* __restrict__ dst) {
+  auto load_a = [&](int kt, uint8_t* __restrict__ dst) {
 #pragma unroll
     for (int i = 0; i < ALD; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ts.shared ? rA2 : rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, ts.a_off[i],
+          ash ? rA2 : rA, (lds_void_t*)(dst + 4 * (ALD * wave + i) * BK * 2), 16, aoff[i],
           kt * BK * 2, 0, 0);
   };
   // weights and the group's scale (and min) of stage kt into registers
-  auto load_b = [&](const GemmTile& ts, int kt, WV* cb, uint32_t* rs, uint32_t* rm) {
+  auto load_b = [&](int kt, WV* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
       const int so = frow(f) * wrow_bytes + kt * (BK / 8 * BITS);
       if constexpr (BITS == 4) {
         cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              ts.shared ? rW2 : rW, ts.b_lane, so, 0));
+                                              wsh ? rW2 : rW, bl, so, 0));
       } else if constexpr (BITS == 3) {
-        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b96(rW, ts.b_lane, so, 0));
+        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b96(rW, bl, so, 0));
       } else {
-        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(rW, ts.b_lane, so, 0));
+        cb[f] = __builtin_bit_cast(WV, __builtin_amdgcn_raw_buffer_load_b64(rW, bl, so, 0));
       }
     }
     if (SCM == SC_STAGE) {
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
         const int so = frow(f) * KG * 2 + kt * s_step;
-        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(ts.shared ? rS2 : rS, ts.s_lane, so, 0);
-        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ts.shared ? rM2 : rM,
-                                                                     ts.s_lane, so, 0)
+        rs[f] = __builtin_amdgcn_raw_buffer_load_b16(wsh ? rS2 : rS, sl, so, 0);
+        rm[f] = ASYM ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(wsh ? rM2 : rM, sl, so, 0)
                      : 0u;
       }
     }
@@ -372,14 +422,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // read other rows' scales or zeros, never used)
   uint8_t* const sc_wave = Sc + wave * SC_WAVE;
   // the scale (and min) window w (K stages 2w, 2w+1) of the wave's rows
-  auto load_win = [&](const GemmTile& ts, int w) {
+  auto load_win = [&](int w) {
     if (WIN) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.shared ? rS2 : rS, (lds_void_t*)sc_wave, 16,
-                                               ts.win_lane, w * 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsh ? rS2 : rS, (lds_void_t*)sc_wave, 16, wl,
+                                               w * 16, 0, 0);
       if (ASYM)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ts.shared ? rM2 : rM,
-                                                 (lds_void_t*)(sc_wave + SC_SLOT), 16,
-                                                 ts.win_lane, w * 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wsh ? rM2 : rM, (lds_void_t*)(sc_wave + SC_SLOT),
+                                                 16, wl, w * 16, 0, 0);
     }
   };
   // the scales (and mins) of stage kt from the current window: fragment f's
@@ -394,16 +443,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       rm[f] = ASYM ? *reinterpret_cast<const uint16_t*>(sc_wave + SC_SLOT + off) : 0u;
     }
   };
-  auto load_sc = [&](const GemmTile& ts) {
-    if (WIN) load_win(ts, 0);
+  // tile t's scale tile (SC_TILE) into the wave's slots
+  auto load_sc_tile = [&](const TileU& t) {
     if (SCL) {
+      const uint32_t r0 = (uint32_t)wrow_first(t);  // e = 0 for the extra group
+      const uint32_t s0 = __builtin_amdgcn_readfirstlane(r0 * KG * 2);
+      const uint32_t s1 = GATEUP ? __builtin_amdgcn_readfirstlane((r0 + N / 2) * KG * 2)
+                                 : (ASYM ? s0 : s0 + SC_SLOT);
       const uint32_t lo = (uint32_t)lane_o * 16u;
-      const __amdgpu_buffer_rsrc_t s_r = ts.shared ? rS2 : rS;
-      const __amdgpu_buffer_rsrc_t m_r = ts.shared ? rM2 : rM;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, (lds_void_t*)sc_wave, 16, lo, ts.sc_src[0], 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ASYM && !GATEUP ? m_r : s_r,
-                                               (lds_void_t*)(sc_wave + SC_SLOT), 16, lo,
-                                               ts.sc_src[1], 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.shared ? rS2 : rS, (lds_void_t*)sc_wave, 16, lo,
+                                               s0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ASYM && !GATEUP ? (t.shared ? rM2 : rM)
+                                                               : (t.shared ? rS2 : rS),
+                                               (lds_void_t*)(sc_wave + SC_SLOT), 16, lo, s1, 0, 0);
     }
   };
   // the scales (and mins) of stage kt from the wave's scale tile
@@ -419,6 +471,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   };
 
   f32x4 acc[MSUB][NFRAG];
+
 
   // chunk c (elements 8c .. 8c+7 of the lane's 32-element K block) of one
   // fragment's packed weights -> eight fp16 weights
@@ -439,7 +492,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // one row.
   auto compute_stage = [&](const uint8_t* __restrict__ as_base, const WV* cb, const uint32_t* rs,
                            const uint32_t* rm, f16x8* b, const WV* cbn, uint32_t* rsn,
-                           uint32_t* rmn, int kt) {
+                           uint32_t* rmn, int nkt) {
     f16x2 cs[NFRAG], cm[NFRAG];
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
@@ -470,7 +523,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         if (WIN) {
           // the window refilled in this stage has landed
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
-          read_win(kt + 1, rsn, rmn);
+          read_win(nkt, rsn, rmn);
         }
 #pragma unroll
         for (int f = 0; f < NFRAG; ++f) {
@@ -500,19 +553,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     }
   };
 
-  // Epilogue. Gate/up: h = silu(g) * u, stored as fp16 in kperm chunk order
-  // through this wave's LDS sub-tile (128 rows x 64 B, in As2 or Ex, which
-  // the next tile's first two stages leave alone) so that it leaves as
-  // 16-byte row pieces. Down: the same, in two halves of 64 rows.
-  auto epilogue = [&](const GemmTile& ts) {
-    int rq = 4 * lg, rr = r16, row0 = ts.row0, rows = ts.rows;
-    uint16_t* const C = ts.shared ? g.C2 : g.C;
-    const int ldc = ts.shared ? g.ldc2 : g.ldc;
+  // Epilogue, from the wave's 4 KB sub-tile in Ex. Gate/up: h = silu(g) * u,
+  // stored as fp16 in kperm chunk order, in passes of 64 rows x 64 B so that
+  // it leaves as 16-byte row pieces (3- and 2-bit: straight from the
+  // accumulators). Down: y in passes of 32 rows x 128 B. No barrier: the
+  // sub-tile is the wave's own, and the stores drain while the next tile's
+  // first stage runs.
+  auto epilogue = [&](const TileU& t) {
+    int rq = 4 * lg, rr = r16, row0 = t.row0, rows = t.rows;
+    uint16_t* const C = t.shared ? g.C2 : g.C;
+    const int ldc = t.shared ? g.ldc2 : g.ldc;
+    const bool cvalid = t.c0 < Nc;
     asm volatile("" : "+v"(rq), "+v"(rr), "+v"(row0), "+v"(rows));
     if (DIRECT) {
       // eight consecutive h values of row 16 mi + r16 per lane (see frow):
       // one 16-byte piece, 64 contiguous bytes of each of 16 rows per store
-      uint16_t* const crow = C + (int64_t)(row0 + rr) * ldc + ts.c0 + 2 * rq;
+      uint16_t* const crow = C + (int64_t)(row0 + rr) * ldc + t.c0 + 2 * rq;
 #pragma unroll
       for (int mi = 0; mi < MSUB; ++mi) {
         float h[8];
@@ -521,47 +577,50 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
           h[v] = silu_f32(acc[mi][v >> 2][v & 3]) * acc[mi][2 + (v >> 2)][v & 3];
         const u32x4 d = {pack_f16x2(h[0], h[1]), pack_f16x2(h[2], h[3]), pack_f16x2(h[4], h[5]),
                          pack_f16x2(h[6], h[7])};
-        if (ts.cvalid && mi * 16 + rr < rows) st16(crow + (int64_t)(mi * 16) * ldc, d);
+        if (cvalid && mi * 16 + rr < rows) st16(crow + (int64_t)(mi * 16) * ldc, d);
       }
     } else if (GATEUP) {
-      uint8_t* sub = BM == 128 ? (wave < 4 ? As2 : Ex) + (wave & 3) * SUBW : Ex + wave * SUBW;
+      uint8_t* const sub = Ex + wave * SUBW;
       // the 16-byte piece p of row r sits at p ^ ((r >> 2) & 3), so the four
       // row groups of one write land in different banks
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pc = 8 * (r16 >> 3) + kpos(r16 & 7);  // column in its pair of pieces
+      for (int ps = 0; ps < BM / 64; ++ps) {
 #pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi)
+        for (int j = 0; j < 2; ++j) {
+          const int pc = 8 * (r16 >> 3) + kpos(r16 & 7);  // column in its pair of pieces
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rl = mi * 16 + rq + v;
-            const float h = silu_f32(acc[mi][j][v]) * acc[mi][j + 2][v];
-            const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
-            *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
-                (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
-          }
-      }
-      lds_wave_sync();
-      // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
+          for (int mh = 0; mh < 4; ++mh)
 #pragma unroll
-      for (int q = 0; q < BM / 16; ++q) {
-        const int rl = q * 16 + (lane_o >> 2);
-        const int p = lane_o & 3;
-        const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
-        if (ts.cvalid && rl < rows) st16(C + (int64_t)(row0 + rl) * ldc + ts.c0 + p * 8, d);
+            for (int v = 0; v < 4; ++v) {
+              const int mi = 4 * ps + mh;
+              const int rl = mh * 16 + rq + v;
+              const float h = silu_f32(acc[mi][j][v]) * acc[mi][j + 2][v];
+              const int piece = (2 * j + (pc >> 3)) ^ ((rl >> 2) & 3);
+              *reinterpret_cast<uint16_t*>(sub + rl * 64 + piece * 16 + (pc & 7) * 2) =
+                  (uint16_t)(pack_f16x2(h, 0.f) & 0xffffu);
+            }
+        }
+        lds_wave_sync();
+        // 16 rows x 64 bytes per wave-wide read: lane -> row lane/4, piece lane%4
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rl = q * 16 + (lane_o >> 2);
+          const int p = lane_o & 3;
+          const u32x4 d = ld16(sub + rl * 64 + (p ^ ((rl >> 2) & 3)) * 16);
+          const int row = ps * 64 + rl;
+          if (cvalid && row < rows) st16(C + (int64_t)(row0 + row) * ldc + t.c0 + p * 8, d);
+        }
       }
     } else {
-      // y in two halves of 64 rows: this wave's half sub-tile is 64 rows x
-      // 128 B (its 64 columns) in As2 or Ex; lane (r16, lg) holds columns
-      // 16 f + 4 lg .. +3 of row 16 mi + r16, and the 16-byte piece p of row
-      // r sits at p ^ (r & 7)
-      uint8_t* sub = BM == 128 ? (wave < 4 ? As2 : Ex) + (wave & 3) * SUBW : Ex + wave * SUBW;
+      // lane (r16, lg) holds columns 16 f + 4 lg .. +3 of row 16 mi + r16;
+      // the 16-byte piece p of row r of a pass sits at p ^ (r & 7)
+      uint8_t* const sub = Ex + wave * SUBW;
 #pragma unroll
-      for (int half = 0; half < BM / 64; ++half) {
+      for (int ps = 0; ps < BM / 32; ++ps) {
 #pragma unroll
-        for (int mh = 0; mh < 4; ++mh) {
-          const int mi = half * 4 + mh;
-          const int rl = mh * 16 + rr;  // row within the half
+        for (int mh = 0; mh < 2; ++mh) {
+          const int mi = ps * 2 + mh;
+          const int rl = mh * 16 + rr;  // row within the pass
 #pragma unroll
           for (int f = 0; f < NFRAG; ++f) {
             uint2 d;
@@ -574,12 +633,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         lds_wave_sync();
         // 8 rows x 128 bytes per wave-wide read: lane -> row lane/8, piece lane%8
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 4; ++q) {
           const int rl = q * 8 + (lane_o >> 3);
           const int p = lane_o & 7;
           const u32x4 d = ld16(sub + rl * 128 + (p ^ (rl & 7)) * 16);
-          const int row = half * 64 + rl;
-          if (ts.cvalid && row < rows) st16(C + (int64_t)(row0 + row) * ldc + ts.c0 + p * 8, d);
+          const int row = ps * 32 + rl;
+          if (cvalid && row < rows) st16(C + (int64_t)(row0 + row) * ldc + t.c0 + p * 8, d);
         }
       }
     }
@@ -589,29 +648,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   // (issued at the top of each stage), activations into the ring slot two
   // stages ahead (issued at the end of each stage), so "at most ALD loads
   // outstanding" at the end of stage s means: stage s+1's activations and
-  // weights have landed (loads complete in issue order). Every stage issues
-  // the same loads (past the last stage they repeat it, into a slot nobody
-  // reads), so the waits are the same at every stage and the compiler's own
-  // wait bookkeeping stays exact. The next tile's first two stages are loaded
-  // while this tile's epilogue runs: weights and stage 0 before it, stage 1
-  // after its stores, so that "at most ALD outstanding" again means stage 0
-  // has landed.
+  // weights have landed (loads complete in issue order). With at least three
+  // stages per tile the pipeline runs on across tiles: the last two stages
+  // of a tile load the next tile's first two (its activations into the next
+  // ring slots, its weights and scales into registers and the wave's scale
+  // slots), so a tile starts with its first stage in place and its
+  // predecessor's stores still draining. Past the workgroup's last tile, and
+  // for shorter K, the last stages repeat their own loads instead (into ring
+  // slots nobody reads), so the waits are the same at every stage and the
+  // compiler's own wait bookkeeping stays exact; with shorter K each tile
+  // then starts from scratch.
   int tile = t_begin + wg_in_xcd;
   if (tile >= t_end) return;
   const int klast = nk - 1;
-  GemmTile cur;
-  setup(tile, cur);
+  // (not with 3- or 2-bit weights: the wider dequant leaves no registers
+  // for the next tile's load state)
+  const bool xt = BITS == 4 && nk >= 3;
+  TileU cu = decode(tile);
+  int ntile_id = tile + wgs_per_xcd;
+  bool has_next = ntile_id < t_end;
+  TileU nx = cu;
+  if (has_next) nx = decode(ntile_id);
   WV cb[NFRAG];
   uint32_t rs[NFRAG], rm[NFRAG];
   f16x8 b0[NFRAG];  // dequantized weights of a stage's first K step
-  load_sc(cur);
-  load_b(cur, 0, cb, rs, rm);
-  load_a(cur, 0, As0);
-  load_a(cur, min(1, klast), As1);
-  while (true) {
-    refresh_lane();
+  // a tile's first two stages from scratch (the first tile; every tile if
+  // nk < 3), into ring slots 0 and 1
+  auto start_plain = [&](const TileU& t, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1) {
+    aoff_mem(t, aoff);
+    ash = t.shared;
+    set_w(t);
+    load_sc_tile(t);
+    load_win(0);
+    load_b(0, cb, rs, rm);
+    load_a(0, s0);
+    load_a(min(1, klast), s1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
-    lds_barrier();  // stage 0 in every wave; the previous epilogue is done with the LDS
+    lds_barrier();  // stage 0 in every wave
+  };
+  // (the next tile's gather entries first: the start's wait covers them)
+  if (xt && has_next) load_gidx(nx);
+  int ph = 0;         // ring slot of the current tile's first stage
+  bool plain = true;  // the tile starts from scratch
+  while (true) {
+    if (plain) {
+      start_plain(cu, As0, As1);
+      ph = 0;
+    }
+    refresh_lane();
     if (SCL) read_sc(sc_wave, 0, rs, rm);
     if (WIN) read_win(0, rs, rm);
     if (XDQ) {
@@ -625,22 +709,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
     for (int i = 0; i < MSUB; ++i)
 #pragma unroll
       for (int j = 0; j < NFRAG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // stage kt reads ring slot kt % 3 and loads stage kt + 2 into slot (kt + 2) % 3
-    // `odd`: kt is odd (a constant at every call), the stage that refills the
-    // scale window with that of stages kt + 1, kt + 2
-    auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2,
-                     bool odd) {
+    const bool go_next = xt && has_next;
+    // stage kt reads ring slot `curs` and loads stage kt + 2 (of this tile
+    // or, past its end, of the next) into `nxt2`
+    auto stage = [&](int kt, const uint8_t* __restrict__ curs, uint8_t* __restrict__ nxt2) {
       WV cbn[NFRAG];
       uint32_t rsn[NFRAG], rmn[NFRAG];
-      load_b(cur, min(kt + 1, klast), cbn, rsn, rmn);
-      if (WIN && odd) load_win(cur, (kt + 1) >> 1);
+      const bool wlast = kt + 1 == nk;     // the weights loaded here are the next tile's
+      const int nkt = wlast ? 0 : kt + 1;  // local index of the stage after this one
+      if (wlast && go_next) {
+        set_w(nx);
+        load_sc_tile(nx);  // the wave read its scale tile for the last time a stage ago
+      }
+      load_b(wlast ? (go_next ? 0 : klast) : kt + 1, cbn, rsn, rmn);
+      if (WIN) {
+        // windows refill at odd stages (stages kt + 1, kt + 2); the last
+        // stage fetches the next tile's first window
+        if (wlast) {
+          if (go_next) load_win(0);
+        } else if (kt & 1) {
+          load_win((kt + 1) >> 1);
+        }
+      }
       // issue the weight loads here, a whole stage before they are needed:
       // left to itself the scheduler sinks them to the end of the stage (to
       // shorten register lifetimes), right before the wait for them
       __builtin_amdgcn_sched_barrier(0);
-      if (XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
-      compute_stage(curs, cb, rs, rm, b0, cbn, rsn, rmn, kt);
-      if (!XDQ && SCL) read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
+      // (the last stage's scales are already in registers; past it the
+      // wave's slots are being refilled with the next tile's, which the
+      // tile start reads)
+      auto next_sc = [&]() {
+        if (wlast && go_next) {
+#pragma unroll
+          for (int f = 0; f < NFRAG; ++f) {
+            rsn[f] = rs[f];
+            rmn[f] = rm[f];
+          }
+        } else {
+          read_sc(sc_wave, min(kt + 1, klast), rsn, rmn);
+        }
+      };
+      if (XDQ && SCL) next_sc();
+      compute_stage(curs, cb, rs, rm, b0, cbn, rsn, rmn, nkt);
+      if (!XDQ && SCL) next_sc();
       // The activation loads go last: their direct writes into the LDS then
       // land while the stage ends and the next one starts, not in the middle
       // of this stage's fragment reads (issued at the top of the stage they
@@ -648,10 +759,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
       // land, and being the last loads issued, "at most ALD outstanding"
       // below still means this stage's weights have arrived.
       __builtin_amdgcn_sched_barrier(0);
-      load_a(cur, min(kt + 2, klast), nxt2);
+      if (kt + 2 == nk && go_next) {
+        aoff_lds(nx, aoff);
+        ash = nx.shared;
+      }
+      load_a(kt + 2 < nk ? kt + 2 : (go_next ? kt + 2 - nk : klast), nxt2);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALD));
       // (after the wait: a window refilled in this stage has landed)
-      if (!XDQ && WIN) read_win(kt + 1, rsn, rmn);
+      if (!XDQ && WIN) read_win(nkt, rsn, rmn);
       lds_barrier();
       // the hand-over of the next stage's registers stays here: moved up into
       // the stage it would wait for loads that were just issued
@@ -663,51 +778,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         rm[f] = rmn[f];
       }
     };
-    if (WIN) {
-      // unrolled by six, so that the window refills sit at fixed stages
-      for (int kt = 0; kt < nk; kt += 6) {
-        stage(kt, As0, As2, false);
-        if (kt + 1 < nk) stage(kt + 1, As1, As0, true);
-        if (kt + 2 < nk) stage(kt + 2, As2, As1, false);
-        if (kt + 3 < nk) stage(kt + 3, As0, As2, true);
-        if (kt + 4 < nk) stage(kt + 4, As1, As0, false);
-        if (kt + 5 < nk) stage(kt + 5, As2, As1, true);
+    // the three ring slots in turn, entered at the tile's first slot
+    int kt = 0;
+    for (;;) {
+      if (ph == 0) {
+        stage(kt, As0, As2);
+        ph = 1;
+        if (++kt == nk) break;
       }
-    } else {
-      for (int kt = 0; kt < nk; kt += 3) {
-        stage(kt, As0, As2, false);
-        if (kt + 1 < nk) stage(kt + 1, As1, As0, false);
-        if (kt + 2 < nk) stage(kt + 2, As2, As1, false);
+      if (ph == 1) {
+        stage(kt, As1, As0);
+        ph = 2;
+        if (++kt == nk) break;
+      }
+      if (ph == 2) {
+        stage(kt, As2, As1);
+        ph = 0;
+        if (++kt == nk) break;
       }
     }
-    // The last stage's repeated activation load targets ring slot
-    // (nk + 1) % 3, which is As2 when nk % 3 == 1, and waves 0-3 of the
-    // 128-row instance write their epilogue sub-tiles into As2. Each wave's
-    // own wait covers only its own loads, so every wave waits for all of its
-    // loads and then meets the others at a barrier: after it, no direct
-    // global->LDS load of this tile is still in flight anywhere in the
-    // workgroup, and the epilogue's LDS writes cannot be overwritten. (A
-    // DIRECT epilogue writes no LDS; its wave still waits for its own last
-    // load, which targets rows of the ring it loads again next.)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (!DIRECT) lds_barrier();
-
-    const int next = tile + wgs_per_xcd;
-    const bool has_next = next < t_end;
-    GemmTile nts;
-    refresh_lane();
-    if (has_next) {
-      setup(next, nts);
-      load_sc(nts);
-      load_b(nts, 0, cb, rs, rm);
-      load_a(nts, 0, As0);
-    }
-    epilogue(cur);
+    epilogue(cu);
     if (!has_next) break;
-    load_a(nts, min(1, klast), As1);
-    cur = nts;
-    tile = next;
+    refresh_lane();
+    tile = ntile_id;
+    cu = nx;
+    ntile_id = tile + wgs_per_xcd;
+    has_next = ntile_id < t_end;
+    if (has_next) nx = decode(ntile_id);
+    plain = !xt;
+    if (xt) {
+      // (read at the new tile's second-to-last stage, after several waits)
+      if (has_next) load_gidx(nx);
+    } else {
+      // the repeated loads of the last stages have landed everywhere
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      lds_barrier();
+    }
   }
+  // the repeated loads of the last stages land before the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 int g_num_cus = 0;

@@ -104,8 +104,15 @@ def test_stack_full_size_two_layers_sampled():
         check_layer(cfg, cpu_layers[l], x_in, xn, logits, x_out, rows=rows)
 
 
+def progress(capfd, msg):
+    """A progress line straight to the terminal, past pytest's output
+    capture: a test that runs for minutes keeps showing that it is alive."""
+    with capfd.disabled():
+        print(msg, flush=True)
+
+
 @pytest.mark.timeout(1200)
-def test_stack40_full_depth():
+def test_stack40_full_depth(capfd):
     """The stacked configuration at full size and depth: 40 layers (H=2048,
     256 experts, top-8, I=512 + shared 512, asymmetric G=32, Zipf-biased
     routing), 16,384 rows in two chunks of 8192, chunk-major on the GPU.
@@ -144,7 +151,7 @@ def test_stack40_full_depth():
             stack.layer_step(layer, xc)
             rec[(ci, l)] = (x_in, bits(xn), logits.cpu().numpy(), ids.cpu().numpy(),
                             bits(moe_only))
-        print(f"[stack40] GPU chunk {ci} done", flush=True)
+        progress(capfd, f"[stack40] GPU chunk {ci} done")
     torch.cuda.synchronize()
     x_final = bits(x)
     # the stack's own driver gives the same bits as the recorded sequence
@@ -184,8 +191,8 @@ def test_stack40_full_depth():
         del r, cache, cpu
         for ci in range(n_chunks):
             rec[(ci, l)] = None
-        print(f"[stack40] layer {l} checked; selections differing so far: {slot_flips} "
-              f"(token, slot), {set_flips} by set", flush=True)
+        progress(capfd, f"[stack40] layer {l} checked; selections differing so far: "
+                        f"{slot_flips} (token, slot), {set_flips} by set")
 
     got = oracle.bf16_to_f64(x_final)
     ref = oracle.bf16_to_f64(xo)
