@@ -217,7 +217,7 @@ moe_status_t moe_layer_forward(const moe_shape_t *shape, int64_t T, const uint16
  * one copy per GPU the library runs on, held until the process ends. The
  * call allocates nothing. Limit: calls whose moe_workspace_size(MOE_WS_LAYER)
  * exceeds MOE_STATIC_WS_BYTES return MOE_ERR_UNSUPPORTED before anything is
- * launched (2,392 tokens at H = 2048, E = 128, k = 8, I = 768; 2,302 at
+ * launched (2,583 tokens at H = 2048, E = 128, k = 8, I = 768; 2,493 at
  * H = 2048, E = 256, k = 8, I = 512 with a shared expert of 512; split
  * longer batches). Every call on one GPU uses that GPU's one array, and
  * nothing in it has to start at zero: calls that overlap on one GPU

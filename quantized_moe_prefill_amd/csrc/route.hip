@@ -7,14 +7,17 @@
 // on the matrix cores is exact and only the fp32 accumulation rounds - the
 // same error class as an fp32 GEMM, at bf16 matrix-core speed.
 //
-//  router_split : Wr (+ shared gate row) -> Wsplit [3*Epad][H] bf16 (the three
-//                 terms are separate rows, so the product is one dense GEMM)
-//  router_gemm  : P[ks][t][n] = sum over the ks-th K slice of x[t] . Wsplit[n],
-//                 fp32; 128 x 192 tiles, 8 waves, a three-stage ring of
-//                 direct global->LDS loads; the K dimension is split across
-//                 workgroups when there are too few token tiles to fill the GPU
-//  router_select: L[t,e] = sum_ks ((P[e] + P[Epad+e]) + P[2Epad+e]) + b[e] in a
-//                 fixed order, then top-k and softmax (16 lanes per token)
+//  router_split : Wr (+ shared gate row) -> Wsplit [3][Epad][H] bf16 (one
+//                 plane per term)
+//  router_gemm  : P[ks][t][e] = sum over the ks-th K slice of x[t] . (the three
+//                 terms of row e), fp32, the three terms accumulated into the
+//                 same accumulator (they are three more K steps of the same
+//                 dot product); tiles of 128 tokens x 64 router rows (192 split
+//                 rows), 8 waves, a three-stage ring of direct global->LDS
+//                 loads; the K dimension is split across workgroups when there
+//                 are too few token tiles to fill the GPU
+//  router_select: L[t,e] = sum_ks P[ks][t][e] + b[e] in plane order, then top-k
+//                 and softmax (16 lanes per token)
 //
 // For a few tokens (at most kRouterGemvT) the product is a plain fp32
 // matrix-vector product instead, router_gemv: one workgroup per router row
@@ -31,7 +34,8 @@ namespace qmoe {
 namespace {
 
 constexpr int RBM = 128;   // tokens per GEMM tile
-constexpr int RBN = 192;   // output columns (split rows) per tile: 3 x 128 experts = 2 tiles
+constexpr int RBE = 64;    // router rows per tile
+constexpr int RBN = 3 * RBE;  // split rows per tile (the three terms of each row)
 constexpr int RBK = 64;    // K per stage
 constexpr int RTHREADS = 512;
 
@@ -61,15 +65,17 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
   }
 }
 
-// Dense bf16 GEMM P = x * Wsplit^T over one K slice. LDS rows are 64 bf16
-// (128 B, eight 16-byte chunks); chunk c of row r sits in slot c ^ (r & 7),
-// which keeps the 16-row fragment reads conflict-free and lets one direct
-// load fill eight whole rows. With x16 set, the workgroups of column tile 0
-// also write their rows' fp16 copy in kperm chunk order (the expert GEMMs'
-// operand, what x_to_f16 computes) from the tiles they stage anyway.
+// bf16 GEMM P = x * (sum of the three split terms)^T over one K slice. LDS
+// rows are 64 bf16 (128 B, eight 16-byte chunks); chunk c of row r sits in
+// slot c ^ (r & 7), which keeps the 16-row fragment reads conflict-free and
+// lets one direct load fill eight whole rows. The B tile holds the three
+// terms of RBE router rows (tile row 64 term + j). With x16 set, the
+// workgroups of column tile 0 also write their rows' fp16 copy in kperm chunk
+// order (the expert GEMMs' operand, what x_to_f16 computes) from the tiles
+// they stage anyway.
 __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ P,
-    uint16_t* __restrict__ x16, int T, int H, int N, int n_mt, int n_nt, int ksplit) {
+    uint16_t* __restrict__ x16, int T, int H, int Epad, int n_mt, int n_nt, int ksplit) {
   // a three-slot ring in separate arrays, with the stage loop unrolled by
   // three: the compiler then sees that a stage's LDS reads never touch the
   // slot being filled, and does not wait for those loads before reading
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   typedef uint16_t ARow[RBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 x 48 each
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves, 64 tokens x 16 rows each
   const int r16 = lane & 15, lg = lane >> 4;
 
   int b = blockIdx.x;
@@ -90,7 +96,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   b /= ksplit;
   const int nt = b % n_nt;
   const int mt = b / n_nt;
-  const int row0 = mt * RBM, col0 = nt * RBN;
+  const int row0 = mt * RBM, col0 = nt * RBE;
   const int klen = H / ksplit;
   const int kbeg = ks * klen;
   const int nst = klen / RBK;
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   const __amdgpu_buffer_rsrc_t rX =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, T * H * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rB =
-      __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, N * H * 2, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, 0, 3 * Epad * H * 2, kRsrcWord3);
   const int lrow = lane >> 3, lslot = lane & 7;
   uint32_t a_off[2], b_off[3];
 #pragma unroll
@@ -113,9 +119,11 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   }
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
+    // tile row r: term r / 64 of router row col0 + r % 64 (rows past Epad
+    // read the last one; their sums are never stored)
     const int r = (3 * wave + i) * 8 + lrow;
-    const int n = min(col0 + r, N - 1);
-    b_off[i] = (uint32_t)(n * H + kbeg + 8 * (lslot ^ (r & 7))) * 2u;
+    const int n = min(col0 + (r & (RBE - 1)), Epad - 1);
+    b_off[i] = (uint32_t)(((r / RBE) * Epad + n) * H + kbeg + 8 * (lslot ^ (r & 7))) * 2u;
   }
   auto load_stage = [&](int s, ARow* __restrict__ A, ARow* __restrict__ B) {
     const int k0 = s * RBK * 2;
@@ -135,11 +143,9 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   const bool xrow_ok = row0 + xr < T;
   uint16_t* const x16_row = write_x16 ? x16 + (int64_t)(row0 + xr) * H + kbeg : nullptr;
 
-  f32x4 acc[4][3];
+  f32x4 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // stage s: slot (A, B) holds it; stage s + 2 is loaded into (A2, B2) (the
   // slot of stage s - 1, which every wave finished before the last barrier).
@@ -168,13 +174,14 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
-        const int rb = wn * 48 + i * 16 + r16;
+        const int rb = i * RBE + wn * 16 + r16;  // term i of the wave's rows
         bb[i] = __builtin_bit_cast(bf16x8, ld16(&B[rb][((j * 4 + lg) ^ (rb & 7)) * 8]));
       }
+      // (term-major, so consecutive products go to different accumulators)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int ti = 0; ti < 3; ++ti)
 #pragma unroll
-        for (int ni = 0; ni < 3; ++ni) acc[mi][ni] = mfma_16x16x32(a[mi], bb[ni], acc[mi][ni]);
+        for (int mi = 0; mi < 4; ++mi) acc[mi] = mfma_16x16x32(a[mi], bb[ti], acc[mi]);
     }
     // (stores of the fp16 copy count in vmcnt as well; the loads still land
     // in issue order, so the wait below still covers stage s + 1)
@@ -196,26 +203,23 @@ __global__ __launch_bounds__(RTHREADS, 1) void router_gemm_kernel(
   // the repeated loads of the last stages land before the workgroup ends
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-  float* Pk = P + (int64_t)ks * T * N;
+  float* Pk = P + (int64_t)ks * T * Epad;
+  const int col = col0 + wn * 16 + r16;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 3; ++ni) {
-      const int col = col0 + wn * 48 + ni * 16 + r16;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = row0 + wm * 64 + mi * 16 + 4 * lg + v;
-        if (row < T && col < N) Pk[(int64_t)row * N + col] = acc[mi][ni][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + wm * 64 + mi * 16 + 4 * lg + v;
+      if (row < T && col < Epad) Pk[(int64_t)row * Epad + col] = acc[mi][v];
     }
 }
 
 template <int Q>
 __global__ __launch_bounds__(256) void router_select_kernel(
-    const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
+    const float* __restrict__ P, int ksplit, int T, int E, int Epad, int k,
     const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out) {
-  select_token<Q>(P, ksplit, planes, T, E, Epad, k, bias, has_shared, logits_out, ids_out, w_out,
+  select_token<Q>(P, ksplit, T, E, Epad, k, bias, has_shared, logits_out, ids_out, w_out,
                   sw_out, blockIdx.x * 16 + (threadIdx.x >> 4), nullptr);
 }
 
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(PT) void router_select_permute_kernel(
   __shared__ int cnt[4][PMAXE];
   __shared__ int s_off[PMAXE];
   __shared__ int s_wave[4];
-  select_token<Q>(P, 1, 1, T, E, Epad, k, bias, has_shared, nullptr, ids_out, w_out, sw_out,
+  select_token<Q>(P, 1, T, E, Epad, k, bias, has_shared, nullptr, ids_out, w_out, sw_out,
                   threadIdx.x >> 4, s_ids);
   __syncthreads();
   const int Pn = T * k;
@@ -277,8 +281,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 }
 
 int router_ksplit(int T, int E, bool has_shared, int H) {
-  const int N = 3 * router_padded_rows(E, has_shared);
-  const int tiles = cdiv(T, RBM) * cdiv(N, RBN);
+  const int tiles = cdiv(T, RBM) * cdiv(router_padded_rows(E, has_shared), RBE);
   int ks = 1;
   while (ks < 16 && tiles * ks * 2 <= 256 && (H / RBK) % (ks * 2) == 0) ks *= 2;
   return ks;
@@ -335,8 +338,8 @@ size_t router_split_bytes(int E, bool has_shared, int H) {
 }
 
 size_t router_partial_bytes(int T, int E, bool has_shared, int H) {
-  const int N = 3 * router_padded_rows(E, has_shared);
-  return (size_t)router_ksplit(T, E, has_shared, H) * T * N * sizeof(float);
+  return (size_t)router_ksplit(T, E, has_shared, H) * T * router_padded_rows(E, has_shared) *
+         sizeof(float);
 }
 
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
@@ -357,7 +360,7 @@ hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const fl
                               float* shared_w, uint16_t* x16, hipStream_t s) {
   const bool has_shared = shared_gate != nullptr;
   const int Epad = router_padded_rows(E, has_shared);
-  int ks = 1, planes = 1;
+  int ks = 1;
   if (router_uses_gemv(T)) {
     // the finished fp32 logits, one plane [T][Epad]
     LaunchScope ls("router_gemm", s);
@@ -366,13 +369,11 @@ hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
-    const int N = 3 * Epad;
-    const int n_mt = cdiv(T, RBM), n_nt = cdiv(N, RBN);
+    const int n_mt = cdiv(T, RBM), n_nt = cdiv(Epad, RBE);
     ks = router_ksplit(T, E, has_shared, H);
-    planes = 3;
     LaunchScope ls("router_gemm", s);
     hipLaunchKernelGGL(router_gemm_kernel, dim3(n_mt * n_nt * ks), dim3(RTHREADS), 0, s, x,
-                       split, partial, x16, T, H, N, n_mt, n_nt, ks);
+                       split, partial, x16, T, H, Epad, n_mt, n_nt, ks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -380,13 +381,13 @@ hipError_t launch_router_topk(const uint16_t* x, const float* w_router, const fl
   const dim3 grid(cdiv(T, 16)), block(256);
   const int hs = has_shared ? 1 : 0;
   if (E <= 64)
-    hipLaunchKernelGGL(router_select_kernel<4>, grid, block, 0, s, partial, ks, planes, T, E, Epad,
+    hipLaunchKernelGGL(router_select_kernel<4>, grid, block, 0, s, partial, ks, T, E, Epad,
                        k, bias, hs, logits, ids, topk_w, shared_w);
   else if (E <= 128)
-    hipLaunchKernelGGL(router_select_kernel<8>, grid, block, 0, s, partial, ks, planes, T, E, Epad,
+    hipLaunchKernelGGL(router_select_kernel<8>, grid, block, 0, s, partial, ks, T, E, Epad,
                        k, bias, hs, logits, ids, topk_w, shared_w);
   else
-    hipLaunchKernelGGL(router_select_kernel<16>, grid, block, 0, s, partial, ks, planes, T, E,
+    hipLaunchKernelGGL(router_select_kernel<16>, grid, block, 0, s, partial, ks, T, E,
                        Epad, k, bias, hs, logits, ids, topk_w, shared_w);
   return hipGetLastError();
 }

@@ -43,9 +43,11 @@ __device__ __forceinline__ float sum_step(float x) {
 // retires the winner; lane j keeps round j's winner for the softmax.
 // Logits, top-k and softmax of token t (16 lanes per token: lane r of the
 // group); the selected ids also go to lds_ids[t * k + j] if it is given.
+// P holds ksplit planes [T][Epad] of partial sums over slices of K, added in
+// plane order.
 template <int Q>
 __device__ __forceinline__ void select_token(
-    const float* __restrict__ P, int ksplit, int planes, int T, int E, int Epad, int k,
+    const float* __restrict__ P, int ksplit, int T, int E, int Epad, int k,
     const float* __restrict__ bias, int has_shared, float* __restrict__ logits_out,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, float* __restrict__ sw_out, int t,
     int32_t* lds_ids, float* lds_w = nullptr, float* lds_sw = nullptr) {
@@ -57,7 +59,7 @@ __device__ __forceinline__ void select_token(
   const int r = threadIdx.x & 15;
   const bool live = t < T;
   const int tt = live ? t : T - 1;
-  const int N = planes * Epad;
+  const int64_t plane = (int64_t)T * Epad;
 
   float v[Q];
 #pragma unroll
@@ -65,17 +67,9 @@ __device__ __forceinline__ void select_token(
     const int e0 = 64 * i + 4 * r;
     f32x4 l = {0.f, 0.f, 0.f, 0.f};
     if (e0 < Epad) {
-      if (planes == 1) {
-        l = *reinterpret_cast<const f32x4*>(P + (int64_t)tt * N + e0);
-      } else {
-        for (int s = 0; s < ksplit; ++s) {
-          const float* p = P + ((int64_t)s * T + tt) * N + e0;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(p + Epad);
-          const f32x4 c = *reinterpret_cast<const f32x4*>(p + 2 * Epad);
-          l += (a + b) + c;
-        }
-      }
+      const float* p = P + (int64_t)tt * Epad + e0;
+      l = *reinterpret_cast<const f32x4*>(p);
+      for (int s = 1; s < ksplit; ++s) l += *reinterpret_cast<const f32x4*>(p + s * plane);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -92,15 +86,9 @@ __device__ __forceinline__ void select_token(
   }
   // the shared-gate column past the last lane's range (E a multiple of 64)
   if (has_shared && E >= 16 * Q && r == 0 && live) {
-    float x = 0.f;
-    if (planes == 1) {
-      x = P[(int64_t)tt * N + E];
-    } else {
-      for (int s = 0; s < ksplit; ++s) {
-        const float* p = P + ((int64_t)s * T + tt) * N + E;
-        x += (p[0] + p[Epad]) + p[2 * Epad];
-      }
-    }
+    const float* p = P + (int64_t)tt * Epad + E;
+    float x = p[0];
+    for (int s = 1; s < ksplit; ++s) x += p[s * plane];
     put_sw(1.f / (1.f + expf(-x)));
   }
 

@@ -50,7 +50,7 @@ __device__ __forceinline__ int small_list(const SmallLayer& a, int32_t* s_ids, f
     s_cnt_e[tid] = 0;
     s_cnt_w0[tid] = 0;
   }
-  select_token<Q>(a.logits, 1, 1, T, E, a.Epad, k, a.bias, a.has_shared, nullptr, nullptr,
+  select_token<Q>(a.logits, 1, T, E, a.Epad, k, a.bias, a.has_shared, nullptr, nullptr,
                   nullptr, nullptr, tid >> 4, s_ids, s_tw, s_sw);
   __syncthreads();
   // The grouping of the pairs by expert, stable (pair order within an

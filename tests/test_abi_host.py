@@ -289,8 +289,8 @@ def test_static_layer_validation_before_launch():
     assert L.moe_layer_forward_static(ctypes.byref(s), 4, FAKE, FAKE, None, FAKE, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_INVALID_ARGUMENT
     # the largest T whose layer workspace fits, and the next one
     assert N.MOE_STATIC_WS_BYTES == 128 << 20
-    for T in (2392, 2393):
+    for T in (2583, 2584):
         assert L.moe_workspace_size(ctypes.byref(s), T, N.MOE_WS_LAYER, ctypes.byref(n)) == N.MOE_OK
-        assert (n.value <= N.MOE_STATIC_WS_BYTES) == (T == 2392)
-    assert L.moe_layer_forward_static(ctypes.byref(s), 2393, FAKE, FAKE, None, None, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+        assert (n.value <= N.MOE_STATIC_WS_BYTES) == (T == 2583)
+    assert L.moe_layer_forward_static(ctypes.byref(s), 2584, FAKE, FAKE, None, None, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_UNSUPPORTED
     assert b"static workspace" in L.moe_last_error()
