@@ -662,13 +662,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   if (tile >= t_end) return;
   const int klast = nk - 1;
   // (not with 3- or 2-bit weights: the wider dequant leaves no registers
-  // for the next tile's load state)
-  const bool xt = BITS == 4 && nk >= 3;
+  // for the next tile's load state, and their tiles keep the plain loop)
+  constexpr bool XT = BITS == 4;
+  const bool xt = XT && nk >= 3;
   TileU cu = decode(tile);
   int ntile_id = tile + wgs_per_xcd;
   bool has_next = ntile_id < t_end;
-  TileU nx = cu;
-  if (has_next) nx = decode(ntile_id);
+  TileU nx = cu;  // the next tile (cross-tile pipeline only)
+  if (xt && has_next) nx = decode(ntile_id);
   WV cb[NFRAG];
   uint32_t rs[NFRAG], rm[NFRAG];
   f16x8 b0[NFRAG];  // dequantized weights of a stage's first K step
@@ -778,38 +779,50 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         rm[f] = rmn[f];
       }
     };
-    // the three ring slots in turn, entered at the tile's first slot
-    int kt = 0;
-    for (;;) {
-      if (ph == 0) {
+    if constexpr (XT) {
+      // the three ring slots in turn, entered at the tile's first slot
+      int kt = 0;
+      for (;;) {
+        if (ph == 0) {
+          stage(kt, As0, As2);
+          ph = 1;
+          if (++kt == nk) break;
+        }
+        if (ph == 1) {
+          stage(kt, As1, As0);
+          ph = 2;
+          if (++kt == nk) break;
+        }
+        if (ph == 2) {
+          stage(kt, As2, As1);
+          ph = 0;
+          if (++kt == nk) break;
+        }
+      }
+    } else {
+      // every tile starts in slot 0
+      for (int kt = 0; kt < nk; kt += 3) {
         stage(kt, As0, As2);
-        ph = 1;
-        if (++kt == nk) break;
-      }
-      if (ph == 1) {
-        stage(kt, As1, As0);
-        ph = 2;
-        if (++kt == nk) break;
-      }
-      if (ph == 2) {
-        stage(kt, As2, As1);
-        ph = 0;
-        if (++kt == nk) break;
+        if (kt + 1 < nk) stage(kt + 1, As1, As0);
+        if (kt + 2 < nk) stage(kt + 2, As2, As1);
       }
     }
     epilogue(cu);
     if (!has_next) break;
     refresh_lane();
     tile = ntile_id;
-    cu = nx;
     ntile_id = tile + wgs_per_xcd;
     has_next = ntile_id < t_end;
-    if (has_next) nx = decode(ntile_id);
     plain = !xt;
     if (xt) {
-      // (read at the new tile's second-to-last stage, after several waits)
-      if (has_next) load_gidx(nx);
+      cu = nx;
+      if (has_next) {
+        nx = decode(ntile_id);
+        // (read at the new tile's second-to-last stage, after several waits)
+        load_gidx(nx);
+      }
     } else {
+      cu = decode(tile);
       // the repeated loads of the last stages have landed everywhere
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       lds_barrier();
