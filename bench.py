@@ -108,6 +108,9 @@ def parse():
                     help="experts the staging buffer holds (two chunks of half of it)")
     ap.add_argument("--tiers", default="",
                     help="mixed widths, e.g. 4:32,3:48,2:48 (bits:experts, hottest first)")
+    ap.add_argument("--w-layout", choices=("tiled", "rows"), default="tiled",
+                    help="layout of the 4-bit expert weights of the fp16 route: regrouped once "
+                         "by moe_pack_w4 before the timed steps (tiled), or row-major")
     ap.add_argument("--no-regimes", action="store_true",
                     help="skip the T=1/4/16 sweep and the skewed shared-expert layer that the "
                          "default headline run adds as extra fields")
@@ -342,7 +345,7 @@ def stack_cpu_baseline(cfg, layers_cpu, x, rows=32, layers=2):
     }
 
 
-def regimes(cfg, li, x, dev, steps):
+def regimes(cfg, li, x, dev, steps, tiled):
     """Driver-visible figures of the other regimes, measured after the
     headline: the weight-streaming sweep (the first T = 1, 4, 16 rows of the
     headline batch on the same weights; each step timed on its own after
@@ -375,7 +378,7 @@ def regimes(cfg, li, x, dev, steps):
     res = {}
     shape = qm.shape_of(cfg)
     for T in cfg.sweep_T:
-        layer = qm.MoELayer(cfg, li, dev, T)
+        layer = qm.MoELayer(cfg, li, dev, T, tiled=tiled)
         xt = x[:T]
         o = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
 
@@ -408,7 +411,7 @@ def regimes(cfg, li, x, dev, steps):
     cfg3 = get_config("skew_shared")
     li3 = make_layer(cfg3, device=dev)
     x3 = make_tokens(cfg3, device=dev)
-    layer3 = qm.MoELayer(cfg3, li3, dev, cfg3.T)
+    layer3 = qm.MoELayer(cfg3, li3, dev, cfg3.T, tiled=tiled)
     o3 = torch.empty((cfg3.T, cfg3.H), dtype=torch.bfloat16, device=dev)
     for _ in range(20):
         layer3.forward(x3, out=o3)
@@ -460,6 +463,8 @@ def main():
     i8 = a.route == "i8"
     tiers = [(int(b), int(n)) for b, n in (t.split(":") for t in a.tiers.split(","))] if a.tiers else []
     streamed = a.stream_hot >= 0
+    # (the integer, mixed-width and host-streamed routes read row-major weights only)
+    tiled = a.w_layout == "tiled" and not (i8 or tiers or streamed)
     if streamed and (i8 or tiers or stacked or cfg.quant != "sym" or cfg.shared_I):
         print("streamed experts need one layer of symmetric experts without a shared expert",
               file=sys.stderr)
@@ -476,7 +481,8 @@ def main():
     x = make_tokens(cfg, device=dev, rows=T)
     if stacked:
         layers = [make_stack_layer(cfg, l, device=dev) for l in range(cfg.n_layers)]
-        stack = qm.MoEStack(cfg, layers, dev, eps=cfg.rms_eps, chunk=min(cfg.chunk or T, T))
+        stack = qm.MoEStack(cfg, layers, dev, eps=cfg.rms_eps, chunk=min(cfg.chunk or T, T),
+                            tiled=tiled)
         xs = torch.empty_like(x)
 
         def step():
@@ -542,7 +548,7 @@ def main():
                 qm.moe_layer_forward_i8(shape, x, li.w_router, li.router_bias, experts, out=out,
                                         ws=ws)
         else:
-            layer = qm.MoELayer(cfg, li, dev, T)
+            layer = qm.MoELayer(cfg, li, dev, T, tiled=tiled)
 
             def step():
                 layer.forward(x, out=out)
@@ -751,6 +757,8 @@ def main():
                       ("fp16, mixed widths " + a.tiers if tiers else
                        (f"fp16, {cfg.E - a.stream_hot} experts streamed from host memory, "
                         f"{a.stream_hot} on the GPU" if streamed else "fp16"))),
+            "weights": ("4-bit matrices regrouped once into the tiled layout (moe_pack_w4) "
+                        "before the timed steps" if tiled else "row-major 4-bit matrices"),
         },
         "layer_tflops": round(layer_tflops, 1),
         "layer_mfma_frac": round(layer_tflops / peak, 4),
@@ -766,7 +774,7 @@ def main():
     }
     if (not a.no_regimes and cfg.name == "a3b_pp8192" and T == cfg.T and not
             (i8 or tiers or streamed)):
-        rec["regimes"] = regimes(cfg, li, x, dev, a.steps)
+        rec["regimes"] = regimes(cfg, li, x, dev, a.steps, tiled)
     if streamed or tiers:
         rec["calibration"] = (f"hot / wider experts chosen by their row counts in a separate "
                               f"calibration batch of {T} tokens drawn with seed {calib_seed} "

@@ -75,6 +75,18 @@ typedef enum {
  *   MOE_Q4_ASYM: w = nibble * scale + min                                     */
 typedef enum { MOE_Q4_SYM = 0, MOE_Q4_ASYM = 1 } moe_quant_t;
 
+/* Byte order of the packed 4-bit weight matrices (w13, w2, s13, s2; the
+ * scales and mins are always row-major [rows][K/G]):
+ *   MOE_W_ROWS : row-major [rows][K/2], the bytes as described above.
+ *   MOE_W_TILED: the same bytes regrouped by moe_pack_w4 into 1024-byte
+ *                blocks, one per 16 rows x 128 elements of K, in the order the
+ *                matrix cores consume them, so that every load of the
+ *                library's GEMM kernels reads whole cache lines. Accepted by
+ *                moe_expert_ffn, moe_layer_forward and moe_layer_forward_static
+ *                (the same results, bit for bit); the integer, mixed-width
+ *                and host-streamed calls return MOE_ERR_UNSUPPORTED for it. */
+typedef enum { MOE_W_ROWS = 0, MOE_W_TILED = 1 } moe_w_layout_t;
+
 typedef struct {
   int64_t hidden;        /* H */
   int64_t num_experts;   /* E routed experts */
@@ -82,7 +94,7 @@ typedef struct {
   int64_t inter;         /* I, routed expert intermediate size */
   int64_t group_size;    /* G, quantization group along K */
   int32_t quant;         /* moe_quant_t */
-  int32_t reserved;      /* must be 0 */
+  int32_t w_layout;      /* moe_w_layout_t of the expert weights */
   int64_t shared_inter;  /* I_s of the always-on shared expert; 0 = none */
 } moe_shape_t;
 
@@ -375,6 +387,19 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t *shape, int64_t T, con
 /* RMSNorm over rows of [T][H] bf16:
  *   out[t,h] = bf16( x[t,h] * (mean_h x[t,h]^2 + eps)^(-1/2) * weight[h] )
  * computed in fp32; weight [H] fp32. out must not alias x. */
+/* Regroups one packed 4-bit matrix from MOE_W_ROWS into MOE_W_TILED, once,
+ * when the weights are loaded (the layout a forward call then reads with
+ * shape.w_layout = MOE_W_TILED):
+ *   dst[((r / 16) * (K / 128) + k / 128) * 1024
+ *       + (((k % 128) / 32) * 16 + r % 16) * 16 + (k % 32) / 2] = src[r * (K / 2) + k / 2]
+ * for every row r < rows and even k < K (each byte holds elements k, k + 1).
+ *   src [rows][K/2] bytes, dst the same size (device; must not overlap);
+ *   rows % 16 == 0, K % 128 == 0, rows * K / 2 < 2^31 (else INVALID_ARGUMENT /
+ *   UNSUPPORTED). Pack w13 with (E * 2I, H), w2 with (E * H, I), s13 with
+ *   (2 I_s, H), s2 with (H, I_s). Enqueued on `stream`. */
+moe_status_t moe_pack_w4(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K,
+                         hipStream_t stream);
+
 moe_status_t moe_rmsnorm(int64_t T, int64_t H, const uint16_t *x, const float *weight,
                          float eps, uint16_t *out, hipStream_t stream);
 

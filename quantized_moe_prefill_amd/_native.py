@@ -20,6 +20,9 @@ MOE_ERR_HIP = 4
 MOE_Q4_SYM = 0
 MOE_Q4_ASYM = 1
 
+MOE_W_ROWS = 0
+MOE_W_TILED = 1
+
 MOE_WS_LAYER = 0
 MOE_WS_ROUTE = 1
 MOE_WS_PERMUTE = 2
@@ -47,6 +50,7 @@ EXPORTED = [
     "moe_layer_forward_mixed",
     "moe_stream_stage_bytes",
     "moe_layer_forward_streamed",
+    "moe_pack_w4",
     "moe_rmsnorm",
     "moe_profile_enable",
     "moe_profile_reset",
@@ -62,7 +66,7 @@ class MoeShape(ctypes.Structure):
         ("inter", ctypes.c_int64),
         ("group_size", ctypes.c_int64),
         ("quant", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("w_layout", ctypes.c_int32),
         ("shared_inter", ctypes.c_int64),
     ]
 
@@ -139,6 +143,8 @@ def lib():
     L.moe_layer_forward_streamed.restype = st
     L.moe_layer_forward_streamed.argtypes = [sp, i64, P, P, P, ep, i32, ep, P, P, ctypes.c_size_t,
                                              P, P, P, ctypes.c_size_t, P, P]
+    L.moe_pack_w4.restype = st
+    L.moe_pack_w4.argtypes = [P, P, i64, i64, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

@@ -72,6 +72,7 @@ LaunchScope::~LaunchScope() {
 struct Shape {
   int H, E, k, I, G, Is;
   bool asym;
+  bool tiled;  // expert weights in MOE_W_TILED
 };
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -80,8 +81,10 @@ static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
   if (s == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "shape is NULL");
   if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %lld)", (long long)T);
   if (s->hidden <= 0 || s->num_experts <= 0 || s->top_k <= 0 || s->inter <= 0 ||
-      s->group_size <= 0 || s->shared_inter < 0 || s->reserved != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "shape fields must be positive (reserved must be 0)");
+      s->group_size <= 0 || s->shared_inter < 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shape fields must be positive");
+  if (s->w_layout != MOE_W_ROWS && s->w_layout != MOE_W_TILED)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_layout must be MOE_W_ROWS or MOE_W_TILED");
   if (s->quant != MOE_Q4_SYM && s->quant != MOE_Q4_ASYM)
     return fail(MOE_ERR_INVALID_ARGUMENT, "quant must be MOE_Q4_SYM or MOE_Q4_ASYM");
   if (s->top_k > s->num_experts)
@@ -119,6 +122,13 @@ static moe_status_t check_shape(const moe_shape_t* s, int64_t T, Shape* out) {
   out->G = (int)G;
   out->Is = (int)s->shared_inter;
   out->asym = s->quant == MOE_Q4_ASYM;
+  out->tiled = s->w_layout == MOE_W_TILED;
+  return MOE_OK;
+}
+
+// calls whose kernels read only row-major weights
+static moe_status_t rows_only(const Shape& s, const char* call) {
+  if (s.tiled) return fail(MOE_ERR_UNSUPPORTED, "%s reads MOE_W_ROWS weights only", call);
   return MOE_OK;
 }
 
@@ -165,6 +175,7 @@ static size_t ffn_ws(const Shape& s, int64_t T) {
 
 // ---- integer route ----
 static moe_status_t check_i8(const Shape& s, int64_t T) {
+  if (rows_only(s, "the integer route") != MOE_OK) return MOE_ERR_UNSUPPORTED;
   if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "the integer route needs MOE_Q4_SYM experts");
   if (s.G != 128) return fail(MOE_ERR_UNSUPPORTED, "the integer route needs group_size 128");
   if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "the integer route has no shared expert");
@@ -301,6 +312,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
   g.C = h;
   g.ldc = s.I;
   g.expect_rows = (int)T;
+  g.w_tiled = s.tiled;
   // the weight-streaming gate/up reads the bf16 activations itself; the tiled
   // one wants them as fp16 in kperm order
   const bool x_direct = gemm_streams(g, true);
@@ -371,6 +383,7 @@ static moe_status_t ffn_impl(const Shape& s, int64_t T, const uint16_t* x,
     gs.C = hs;
     gs.ldc = s.Is;
     gs.expect_rows = (int)T;
+    gs.w_tiled = s.tiled;
     if (!fold_gu) {
       if (gs.a_bf16 && !gemm_streams(gs, true)) {
         if (!x16_ready) QMOE_HIP(launch_x_to_f16(x, x16, T * s.H, st), "x_to_f16 launch");
@@ -442,6 +455,7 @@ static moe_status_t ffn_i8_impl(const Shape& s, int64_t T, const uint16_t* x,
 
 // ---- mixed-width experts ----
 static moe_status_t check_tiers(const Shape& s, const moe_tier_t* tiers, int32_t n) {
+  if (rows_only(s, "the mixed-width route") != MOE_OK) return MOE_ERR_UNSUPPORTED;
   if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "mixed-width experts need MOE_Q4_SYM");
   if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "mixed-width layers have no shared expert");
   if (tiers == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "tiers is NULL");
@@ -613,6 +627,7 @@ static moe_status_t layer_run(const Shape& s, int64_t T, const uint16_t* x,
     a.I = s.I;
     a.G = s.G;
     a.has_shared = s.Is > 0 ? 1 : 0;
+    a.w_tiled = s.tiled;
     a.Epad = router_padded_rows(s.E, s.Is > 0);
     a.nbits = 0;
     while ((1 << a.nbits) < s.E) ++a.nbits;
@@ -1046,6 +1061,8 @@ moe_status_t moe_stream_stage_bytes(const moe_shape_t* shape, int32_t experts, s
   Shape s;
   moe_status_t st = check_shape(shape, 0, &s);
   if (st != MOE_OK) return st;
+  st = rows_only(s, "moe_stream_stage_bytes");
+  if (st != MOE_OK) return st;
   if (bytes == nullptr || experts < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "bad argument");
   // two slots of experts / 2 (at least one) experts each
   const int per = experts > 1 ? (experts + 1) / 2 : 1;
@@ -1065,6 +1082,8 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
   moe_status_t st = check_shape(shape, T, &s);
   if (st != MOE_OK) return st;
   if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "streamed experts need MOE_Q4_SYM");
+  st = rows_only(s, "moe_layer_forward_streamed");
+  if (st != MOE_OK) return st;
   if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "streamed layers have no shared expert");
   if (hot_slot == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "hot_slot is NULL");
   if (hot_count < 0 || hot_count > s.E) return fail(MOE_ERR_INVALID_ARGUMENT, "bad hot_count");
@@ -1246,6 +1265,24 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t* shape, int64_t T, con
   }
   QMOE_HIP(launch_combine(yperm, inv, tw, nullptr, nullptr, residual, out, (int)T, s.H, s.k, stream),
            "combine launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                         hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || rows <= 0 || K <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_w4: null pointer or non-positive size");
+  if (rows % 16 != 0 || K % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_w4: rows must be a multiple of 16, K of 128");
+  if (rows * (K / 2) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_w4: matrix must be below 2^31 bytes");
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_w4: pointers must be 16-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), b0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)(rows * (K / 2));
+  if (a0 < b0 + n && b0 < a0 + n)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_w4: src and dst overlap");
+  QMOE_HIP(launch_pack_w4(src, dst, rows, K, stream), "pack_w4 launch");
   return MOE_OK;
 }
 

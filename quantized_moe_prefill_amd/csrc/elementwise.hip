@@ -129,6 +129,37 @@ hipError_t launch_write_maps(const ExpertMaps& m, int E, int32_t* group, int32_t
   return hipGetLastError();
 }
 
+// The tiled 4-bit layout: 16-byte chunk c of the destination is lane
+// l = c % 64 of block b = c / 64, i.e. row group b / nk, K stage b % nk;
+// lane l = 16 lg + r holds row 16 (b / nk) + r, bytes [64 stage + 16 lg, +16)
+// of the row-major matrix (the 32 elements the lane feeds the matrix cores
+// in that stage).
+__global__ __launch_bounds__(256) void pack_w4_kernel(const uint8_t* __restrict__ src,
+                                                      uint8_t* __restrict__ dst, int64_t chunks,
+                                                      int nk, int row_bytes) {
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int64_t b = c >> 6;
+    const int l = (int)(c & 63);
+    const int64_t grp = b / nk;
+    const int st = (int)(b - grp * nk);
+    const int64_t so = (grp * 16 + (l & 15)) * row_bytes + st * 64 + (l >> 4) * 16;
+    st16(dst + c * 16, ld16(src + so));
+  }
+}
+
+hipError_t launch_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                          hipStream_t s) {
+  const int64_t chunks = rows * K / 32;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) return hipSuccess;
+  LaunchScope ls("pack_w4", s);
+  hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, chunks,
+                     (int)(K / 128), (int)(K / 2));
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* out, int T,
                           int H, hipStream_t s) {
   const dim3 grid(cdiv(T, 4)), block(256);

@@ -374,9 +374,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   uint32_t sl = 0;     // SC_STAGE: this lane's scales
   uint32_t wl = 0;     // SC_WINDOW: this lane's row's scale groups
   int ash = 0, wsh = 0;
+  // tiled 4-bit weights (moe_pack_w4): fragment f's 16 rows x 128 K of a
+  // stage are one 1 KB block, lane l's 16 bytes at 16 l (BITS == 4 only)
+  const bool wt = BITS == 4 && g.w_tiled;
+  const int w_kstep = wt ? 1024 : BK / 8 * BITS;  // bytes from one K stage to the next
   auto set_w = [&](const TileU& t) {
     const int wr0 = wrow_first(t);
-    bl = (uint32_t)(wr0 + prow(r16)) * wrow_bytes + lg * 4 * BITS;
+    bl = wt ? (uint32_t)wr0 * wrow_bytes + (uint32_t)lane_o * 16u
+            : (uint32_t)(wr0 + prow(r16)) * wrow_bytes + lg * 4 * BITS;
     if (SCM == SC_STAGE) sl = ((uint32_t)(wr0 + prow(r16)) * KG + (lg * 32) / g.G) * 2;
     if (WIN) {
       // lane l loads the window of the wave's weight row l: gate/up lanes
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   auto load_b = [&](int kt, WV* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-      const int so = frow(f) * wrow_bytes + kt * (BK / 8 * BITS);
+      const int so = frow(f) * wrow_bytes + kt * w_kstep;
       if constexpr (BITS == 4) {
         cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               wsh ? rW2 : rW, bl, so, 0));

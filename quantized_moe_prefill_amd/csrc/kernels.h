@@ -102,6 +102,9 @@ struct GroupedGemm {
   int tier_id;
   int w_experts;
   int bits;
+  // W and W2 in the tiled 4-bit layout (moe_pack_w4: 1024-byte blocks of 16
+  // rows x 128 K) instead of row-major; 4-bit only
+  bool w_tiled;
 };
 
 // Per-expert group and slot maps of a mixed layer (at most 256 experts),
@@ -141,6 +144,7 @@ struct SmallLayer {
   uint16_t *h, *hs, *yperm, *ysh;
   int32_t *ids, *inv, *sorted, *counts, *offsets;
   float *tw, *sw;
+  bool w_tiled;  // the packed weights in the tiled layout
 };
 // shapes these kernels cover (T <= kRouterGemvT, k <= 8, E <= 256, G 32 or
 // 128, a shared expert of the routed experts' width, H and I whose
@@ -150,6 +154,10 @@ bool small_layer_supported(int T, int H, int I, int Is, int E, int k, int G);
 // Two launches, after the router logits: top-k, grouping and gate/up (with
 // the shared expert), then down (with the shared expert).
 hipError_t launch_small_experts(const SmallLayer& a, hipStream_t s);
+// One 4-bit matrix [rows][K/2] regrouped into the tiled layout (rows % 16 == 0,
+// K % 128 == 0).
+hipError_t launch_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
+                          hipStream_t s);
 // The router logits alone for at most kRouterGemvT tokens (one plane, [T][Epad]).
 hipError_t launch_router_gemv(const uint16_t* x, const float* w_router, const float* shared_gate,
                               int T, int H, int E, float* partial, hipStream_t s);

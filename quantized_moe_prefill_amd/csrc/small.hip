@@ -165,6 +165,7 @@ __global__ __launch_bounds__(STHREADS, 2) void small_gateup_kernel(SmallLayer a)
   g.K = a.H;
   g.C = a.h;
   g.ldc = a.I;
+  g.w_tiled = a.w_tiled;
   stream_items<true, ASYM, NSG, NFG, G>(g, a.E, n_cb, i0, min(i1, nR), s_grp, s_rows, s_row0,
                                         s_tok, red);
   if (a.has_shared) {
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(STHREADS, 2) void small_down_kernel(SmallLayer a) {
   d.K = a.I;
   d.C = a.yperm;
   d.ldc = a.H;
+  d.w_tiled = a.w_tiled;
   stream_items<false, ASYM, NSD, NFD, G>(d, E, n_cb, i0, min(i1, nR), s_grp, s_rows, s_row0,
                                          nullptr, red);
   if (a.has_shared) {

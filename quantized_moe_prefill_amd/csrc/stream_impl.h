@@ -98,14 +98,22 @@ __device__ __forceinline__ void stream_items(const GroupedGemm& g, int n_groups,
     const int e = s_grp[slot];
     const int c0 = (it - slot * n_cb) * cstep;
     const uint32_t wrow0 = (uint32_t)(e * N + c0 + r16);
-    const uint32_t b_lane = wrow0 * (uint32_t)(K / 2) + kbc / 2;
+    // row-major: row wrow0, bytes from kbc / 2 on, 16 per load; tiled
+    // (moe_pack_w4): the 1 KB block of the fragment's 16 rows and kbc's K
+    // stage, 16-byte slot 16 ((kbc % 128) / 32 + i) + r16 for load i
+    // (a lane's 32 NS elements never cross a stage)
+    const uint32_t b_lane =
+        g.w_tiled ? (wrow0 - r16) * (uint32_t)(K / 2) + (uint32_t)(kbc >> 7) * 1024u +
+                        (uint32_t)((kbc >> 5) & 3) * 256u + (uint32_t)r16 * 16u
+                  : wrow0 * (uint32_t)(K / 2) + kbc / 2;
+    const int i_step = g.w_tiled ? 256 : 16;
     const uint32_t s_lane = (wrow0 * (uint32_t)KG + kbc / G) * 2;
 #pragma unroll
     for (int i = 0; i < NS; ++i)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
         W.w[i][f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rW, b_lane, frow(f) * (K / 2) + 16 * i, 0));
+                                                  rW, b_lane, frow(f) * (K / 2) + i_step * i, 0));
     auto load_sc = [&](__amdgpu_buffer_rsrc_t r, int so, uint32_t* d) {
       if (NSC == 4) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, s_lane, so, 0);

@@ -8,7 +8,9 @@ runs in the library's kernels.
 """
 from __future__ import annotations
 
+import copy
 import ctypes
+import dataclasses
 from typing import Optional
 
 import torch
@@ -18,14 +20,15 @@ from . import _native as N
 _U16 = (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
 
 
-def make_shape(H: int, E: int, k: int, I: int, G: int, quant: str, shared_I: int = 0) -> N.MoeShape:
+def make_shape(H: int, E: int, k: int, I: int, G: int, quant: str, shared_I: int = 0,
+               w_layout: int = N.MOE_W_ROWS) -> N.MoeShape:
     q = {"sym": N.MOE_Q4_SYM, "asym": N.MOE_Q4_ASYM}[quant]
-    return N.MoeShape(H, E, k, I, G, q, 0, shared_I)
+    return N.MoeShape(H, E, k, I, G, q, w_layout, shared_I)
 
 
-def shape_of(cfg) -> N.MoeShape:
-    """Shape struct of a synth.MoEConfig."""
-    return make_shape(cfg.H, cfg.E, cfg.k, cfg.I, cfg.G, cfg.quant, cfg.shared_I)
+def shape_of(cfg, w_layout: int = N.MOE_W_ROWS) -> N.MoeShape:
+    """Shape struct of a synth.MoEConfig (expert weights in `w_layout`)."""
+    return make_shape(cfg.H, cfg.E, cfg.k, cfg.I, cfg.G, cfg.quant, cfg.shared_I, w_layout)
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None, device=None) -> Optional[int]:
@@ -67,6 +70,33 @@ class Experts:
 
     def ref(self):
         return ctypes.byref(self.struct)
+
+
+def moe_pack_w4(src: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """The MOE_W_TILED copy of one packed 4-bit matrix src [rows][K/2] (u8,
+    any leading shape with that many bytes)."""
+    dev = src.device
+    if src.numel() != rows * K // 2:
+        raise ValueError(f"src holds {src.numel()} bytes, expected rows * K / 2 = {rows * K // 2}")
+    dst = torch.empty_like(src)
+    N.check(N.lib().moe_pack_w4(_ptr(src, "src", (torch.uint8,), dev), _ptr(dst, "dst", (torch.uint8,), dev),
+                                int(rows), int(K), _stream(dev)))
+    return dst
+
+
+def pack_layer(cfg, li):
+    """A copy of a layer's tensors (synth.LayerInputs or alike) whose four
+    4-bit matrices (w13, w2 and the shared expert's s13, s2) are in the
+    MOE_W_TILED layout, for calls with shape_of(cfg, N.MOE_W_TILED). The
+    other tensors are shared with li."""
+    out = dataclasses.replace(li) if dataclasses.is_dataclass(li) else copy.copy(li)
+    E, H, I, Is = cfg.E, cfg.H, cfg.I, cfg.shared_I
+    out.w13 = moe_pack_w4(li.w13, E * 2 * I, H)
+    out.w2 = moe_pack_w4(li.w2, E * H, I)
+    if Is > 0 and getattr(li, "s13", None) is not None:
+        out.s13 = moe_pack_w4(li.s13, 2 * Is, H)
+        out.s2 = moe_pack_w4(li.s2, H, Is)
+    return out
 
 
 def moe_workspace_size(shape: N.MoeShape, T: int, kind: int = N.MOE_WS_LAYER) -> int:
@@ -389,11 +419,13 @@ class MoELayer:
     workspace (its own, or one shared with other layers of the same shape),
     for repeated moe_layer_forward calls."""
 
-    def __init__(self, cfg, li, device, T_max: int, ws=None):
+    def __init__(self, cfg, li, device, T_max: int, ws=None, tiled: bool = False):
+        # tiled: the 4-bit matrices are regrouped once into MOE_W_TILED (a
+        # packed copy; li itself is left as it is)
         self.cfg = cfg
-        self.shape = shape_of(cfg)
-        self.li = li
-        self.experts = Experts(li)
+        self.shape = shape_of(cfg, N.MOE_W_TILED if tiled else N.MOE_W_ROWS)
+        self.li = pack_layer(cfg, li) if tiled else li
+        self.experts = Experts(self.li)
         self.ws = ws if ws is not None else workspace(self.shape, T_max, device)
 
     def forward(self, x, residual=None, out=None):
@@ -415,13 +447,15 @@ class MoEStack:
     every step runs in the library's kernels; the layers share one
     workspace."""
 
-    def __init__(self, cfg, layers, device, eps: float = 1e-6, chunk: int = 0):
+    def __init__(self, cfg, layers, device, eps: float = 1e-6, chunk: int = 0,
+                 tiled: bool = False):
         self.cfg = cfg
         self.eps = eps
         self.chunk = chunk if chunk > 0 else cfg.T
         shape = shape_of(cfg)
         self.ws = workspace(shape, self.chunk, device)
-        self.layers = [MoELayer(cfg, li, device, self.chunk, ws=self.ws) for li in layers]
+        self.layers = [MoELayer(cfg, li, device, self.chunk, ws=self.ws, tiled=tiled)
+                       for li in layers]
         self.xn = torch.empty((self.chunk, cfg.H), dtype=torch.bfloat16, device=device)
 
     def layer_step(self, layer: "MoELayer", xc: torch.Tensor) -> torch.Tensor:

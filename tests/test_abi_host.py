@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def _shape(**kw):
     d = dict(hidden=2048, num_experts=128, top_k=8, inter=768, group_size=128, quant=0,
-             reserved=0, shared_inter=0)
+             w_layout=0, shared_inter=0)
     d.update(kw)
     return N.MoeShape(**d)
 
@@ -77,7 +77,8 @@ def test_workspace_sizes():
     (dict(top_k=9, num_experts=16), N.MOE_ERR_UNSUPPORTED),
     (dict(top_k=9, num_experts=8), N.MOE_ERR_INVALID_ARGUMENT),
     (dict(quant=5), N.MOE_ERR_INVALID_ARGUMENT),
-    (dict(reserved=1), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(w_layout=2), N.MOE_ERR_INVALID_ARGUMENT),
+    (dict(w_layout=-1), N.MOE_ERR_INVALID_ARGUMENT),
     (dict(shared_inter=100), N.MOE_ERR_UNSUPPORTED),
     (dict(shared_inter=-64), N.MOE_ERR_INVALID_ARGUMENT),
 ])
@@ -294,3 +295,29 @@ def test_static_layer_validation_before_launch():
         assert (n.value <= N.MOE_STATIC_WS_BYTES) == (T == 2583)
     assert L.moe_layer_forward_static(ctypes.byref(s), 2584, FAKE, FAKE, None, None, ctypes.byref(ex), None, FAKE, None) == N.MOE_ERR_UNSUPPORTED
     assert b"static workspace" in L.moe_last_error()
+
+
+def test_tiled_layout_validation():
+    """MOE_W_TILED weights: the fp16 route sizes its workspace as for row-major
+    weights; the calls whose kernels read row-major weights only refuse the
+    layout on the host; moe_pack_w4 checks its arguments before launching
+    (include/moe.h, moe_w_layout_t and moe_pack_w4)."""
+    L = _lib()
+    t = _shape(w_layout=N.MOE_W_TILED)
+    st, n = _ws(t, 8192)
+    st0, n0 = _ws(_shape(), 8192)
+    assert st == st0 == N.MOE_OK and n == n0
+    st, _ = _ws(t, 16, N.MOE_WS_LAYER_I8)
+    assert st == N.MOE_ERR_UNSUPPORTED and b"MOE_W_ROWS" in L.moe_last_error()
+    n = ctypes.c_size_t(0)
+    assert L.moe_stream_stage_bytes(ctypes.byref(t), 2, ctypes.byref(n)) == N.MOE_ERR_UNSUPPORTED
+    e = _experts()
+    assert L.moe_layer_forward_i8(ctypes.byref(t), 4, FAKE, FAKE, None, ctypes.byref(e), None, FAKE,
+                                  FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
+    pk = L.moe_pack_w4
+    assert pk(None, FAKE, 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert pk(FAKE, FAKE + (1 << 24), 24, 128, None) == N.MOE_ERR_INVALID_ARGUMENT   # rows % 16
+    assert pk(FAKE, FAKE + (1 << 24), 16, 192, None) == N.MOE_ERR_INVALID_ARGUMENT   # K % 128
+    assert pk(FAKE, FAKE + 512, 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT         # overlap
+    assert pk(FAKE + 8, FAKE + (1 << 24), 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT  # alignment
+    assert pk(FAKE, FAKE + (1 << 34), 1 << 20, 1 << 12, None) == N.MOE_ERR_UNSUPPORTED  # >= 2^31 B
