@@ -8,14 +8,6 @@
 
 namespace qmoe {
 
-// (value, index) order used by the selection: larger value first, then the
-// lower index. idx < 0 marks "nothing".
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  return va > vb || (va == vb && ia < ib);
-}
-
 // DPP row patterns: after xor-1, xor-2 (quad_perm), half-mirror and mirror
 // exchanges every lane of a 16-lane row has combined all 16 lanes.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
@@ -26,10 +18,10 @@ __device__ __forceinline__ int dpp(int v) {
 }
 
 template <int CTRL>
-__device__ __forceinline__ void best_step(float& bv, int& bi) {
-  const float ov = __int_as_float(dpp<CTRL>(__float_as_int(bv)));
-  const int oi = dpp<CTRL>(bi);
-  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = dpp<CTRL>((int)(uint32_t)v);
+  const int hi = dpp<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
 template <int CTRL>
@@ -38,7 +30,8 @@ __device__ __forceinline__ float sum_step(float x) {
 }
 
 // 16 lanes per token (16 tokens per 256-thread workgroup). Lane r holds the
-// logits of experts 64*i + 4*r + c (i < Q/4, c < 4). Each of the k rounds
+// logits of experts 64*i + 4*r + c (i < Q/4, c < 4). The selection order is
+// the larger logit first, then the lower expert index; each of the k rounds
 // takes the lane-local best, reduces it over the row with DPP exchanges and
 // retires the winner; lane j keeps round j's winner for the softmax.
 // Logits, top-k and softmax of token t (16 lanes per token: lane r of the
@@ -92,29 +85,43 @@ __device__ __forceinline__ void select_token(
     put_sw(1.f / (1.f + expf(-x)));
   }
 
-  uint32_t avail = 0;  // bit q: v[q] is a candidate
+  // Each candidate as one 64-bit key whose unsigned order is the selection
+  // order: the logit's bits mapped to an order-preserving integer (-0.0
+  // made +0.0 first, so the two compare equal), then 0xffff - e, so that of
+  // equal logits the lower expert index wins. 0 marks "nothing" (every
+  // finite logit maps above it). Each round takes the largest key of the
+  // lane, reduces it over the row with DPP exchanges (unique keys: every lane
+  // ends with the same winner) and clears it where it came from.
+  uint64_t kq[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q)
-    if (64 * (q >> 2) + 4 * r + (q & 3) < E) avail |= 1u << q;
-
-  float m0 = 0.f, selv = 0.f;
-  int seli = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int bi = -1;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int e = 64 * (q >> 2) + 4 * r + (q & 3);
-      if (((avail >> q) & 1) && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
-    }
-    best_step<kDppXor1>(bv, bi);
-    best_step<kDppXor2>(bv, bi);
-    best_step<kDppHalfMirror>(bv, bi);
-    best_step<kDppMirror>(bv, bi);
-    if (j == 0) m0 = bv;
-    if (r == j) { selv = bv; seli = bi; }
-    if (((bi & 63) >> 2) == r) avail &= ~(1u << (4 * (bi >> 6) + (bi & 3)));
+  for (int q = 0; q < Q; ++q) {
+    const int e = 64 * (q >> 2) + 4 * r + (q & 3);
+    uint32_t b = __float_as_uint(v[q] + 0.0f);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    kq[q] = e < E ? ((uint64_t)b << 32) | (uint32_t)(0xffff - e) : 0ull;
   }
+  auto kmax = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  uint64_t best0 = 0, selk = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t bk = kq[0];
+#pragma unroll
+    for (int q = 1; q < Q; ++q) bk = kmax(bk, kq[q]);
+    bk = kmax(bk, dpp64<kDppXor1>(bk));
+    bk = kmax(bk, dpp64<kDppXor2>(bk));
+    bk = kmax(bk, dpp64<kDppHalfMirror>(bk));
+    bk = kmax(bk, dpp64<kDppMirror>(bk));
+    if (j == 0) best0 = bk;
+    if (r == j) selk = bk;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) kq[q] = kq[q] == bk ? 0ull : kq[q];
+  }
+  // back to the logit and the expert index
+  auto key_value = [](uint64_t kk) {
+    const uint32_t b = (uint32_t)(kk >> 32);
+    return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+  };
+  const float m0 = key_value(best0), selv = key_value(selk);
+  const int seli = 0xffff - (int)(uint32_t)(selk & 0xffffu);
   // softmax over the k winners (the largest is round 0's)
   const float ex = r < k ? expf(selv - m0) : 0.f;
   float sum = sum_step<kDppXor1>(ex);
