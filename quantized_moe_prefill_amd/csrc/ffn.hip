@@ -666,9 +666,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   int tile = t_begin + wg_in_xcd;
   if (tile >= t_end) return;
   const int klast = nk - 1;
-  // (not with 3- or 2-bit weights: the wider dequant leaves no registers
-  // for the next tile's load state, and their tiles keep the plain loop)
-  constexpr bool XT = BITS == 4;
+  // (not with 3-bit weights, whose wider dequant leaves no registers for the
+  // next tile's load state, nor for the 2-bit gate/up kernel, which it did
+  // not make faster: their tiles keep the plain loop)
+  constexpr bool XT = BITS == 4 || (!GATEUP && BITS == 2);
   const bool xt = XT && nk >= 3;
   TileU cu = decode(tile);
   int ntile_id = tile + wgs_per_xcd;
