@@ -22,7 +22,9 @@ struct LaunchScope {
 // the shared-gate row (if any), then zeros.
 int router_padded_rows(int E, bool has_shared);
 size_t router_split_bytes(int E, bool has_shared, int H);
-// fp32 partial logits of the router GEMM (one plane per K slice)
+// fp32 partial logits of the router GEMM (one plane per K slice, at most
+// kRouterMaxKsplit planes)
+constexpr int kRouterMaxKsplit = 16;
 size_t router_partial_bytes(int T, int E, bool has_shared, int H);
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
                                uint16_t* split, hipStream_t s);

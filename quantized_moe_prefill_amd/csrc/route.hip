@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
 int router_ksplit(int T, int E, bool has_shared, int H) {
   const int tiles = cdiv(T, RBM) * cdiv(router_padded_rows(E, has_shared), RBE);
   int ks = 1;
-  while (ks < 16 && tiles * ks * 2 <= 256 && (H / RBK) % (ks * 2) == 0) ks *= 2;
+  while (ks < kRouterMaxKsplit && tiles * ks * 2 <= 256 && (H / RBK) % (ks * 2) == 0) ks *= 2;
   return ks;
 }
 

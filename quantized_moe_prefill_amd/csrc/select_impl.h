@@ -36,8 +36,8 @@ __device__ __forceinline__ float sum_step(float x) {
 // retires the winner; lane j keeps round j's winner for the softmax.
 // Logits, top-k and softmax of token t (16 lanes per token: lane r of the
 // group); the selected ids also go to lds_ids[t * k + j] if it is given.
-// P holds ksplit planes [T][Epad] of partial sums over slices of K, added in
-// plane order.
+// P holds ksplit (at most kRouterMaxKsplit) planes [T][Epad] of partial sums
+// over slices of K, added in plane order.
 template <int Q>
 __device__ __forceinline__ void select_token(
     const float* __restrict__ P, int ksplit, int T, int E, int Epad, int k,
@@ -60,9 +60,16 @@ __device__ __forceinline__ void select_token(
     const int e0 = 64 * i + 4 * r;
     f32x4 l = {0.f, 0.f, 0.f, 0.f};
     if (e0 < Epad) {
+      // every plane's load in flight at once, then the sum in plane order
       const float* p = P + (int64_t)tt * Epad + e0;
-      l = *reinterpret_cast<const f32x4*>(p);
-      for (int s = 1; s < ksplit; ++s) l += *reinterpret_cast<const f32x4*>(p + s * plane);
+      f32x4 pl[kRouterMaxKsplit];
+#pragma unroll
+      for (int s = 0; s < kRouterMaxKsplit; ++s)
+        if (s < ksplit) pl[s] = *reinterpret_cast<const f32x4*>(p + s * plane);
+      l = pl[0];
+#pragma unroll
+      for (int s = 1; s < kRouterMaxKsplit; ++s)
+        if (s < ksplit) l += pl[s];
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -80,8 +87,14 @@ __device__ __forceinline__ void select_token(
   // the shared-gate column past the last lane's range (E a multiple of 64)
   if (has_shared && E >= 16 * Q && r == 0 && live) {
     const float* p = P + (int64_t)tt * Epad + E;
-    float x = p[0];
-    for (int s = 1; s < ksplit; ++s) x += p[s * plane];
+    float pl[kRouterMaxKsplit];
+#pragma unroll
+    for (int s = 0; s < kRouterMaxKsplit; ++s)
+      if (s < ksplit) pl[s] = p[s * plane];
+    float x = pl[0];
+#pragma unroll
+    for (int s = 1; s < kRouterMaxKsplit; ++s)
+      if (s < ksplit) x += pl[s];
     put_sw(1.f / (1.f + expf(-x)));
   }
 
