@@ -39,30 +39,53 @@ constexpr int RBN = 3 * RBE;  // split rows per tile (the three terms of each ro
 constexpr int RBK = 64;    // K per stage
 constexpr int RTHREADS = 512;
 
+// Three bf16 terms per fp32 router weight whose sum is the weight exactly.
+// Thread (x, row) takes eight consecutive weights of router row blockIdx.y
+// (the shared gate after the E experts, zeros up to Epad): two 16-byte
+// loads, one 16-byte store per term.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr,
                                                           const float* __restrict__ sg, int E,
                                                           int H, int Epad,
                                                           uint16_t* __restrict__ out) {
-  const int64_t n = (int64_t)Epad * H;
-  const int64_t plane = n;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int e = (int)(i / H);
-    const int h = (int)(i - (int64_t)e * H);
-    float w = 0.f;
-    if (e < E)
-      w = wr[(int64_t)e * H + h];
-    else if (e == E && sg != nullptr)
-      w = sg[h];
-    const uint32_t u1 = __float_as_uint(w) & 0xffff0000u;  // top 8 significant bits
-    const float r1 = w - __uint_as_float(u1);                // exact
-    const uint32_t u2 = __float_as_uint(r1) & 0xffff0000u;  // next 8
-    const float r2 = r1 - __uint_as_float(u2);               // exact, <= 8 bits left
-    const uint32_t u3 = __float_as_uint(r2) >> 16;           // r2 fits bf16 exactly
-    out[i] = (uint16_t)(u1 >> 16);
-    out[plane + i] = (uint16_t)(u2 >> 16);
-    out[2 * plane + i] = (uint16_t)u3;
+  const int e = blockIdx.y;
+  const int h = 8 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (h >= H) return;
+  const float* src = e < E ? wr + (int64_t)e * H : (e == E ? sg : nullptr);
+  float w[8];
+  if (src != nullptr) {
+    const u32x4 a = ld16(src + h), b = ld16(src + h + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = __uint_as_float(a[i]);
+      w[4 + i] = __uint_as_float(b[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0.f;
   }
+  u32x4 t1, t2, t3;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    uint32_t hi[3][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float x = w[i + j];
+      const uint32_t u1 = __float_as_uint(x) & 0xffff0000u;  // top 8 significant bits
+      const float r1 = x - __uint_as_float(u1);                // exact
+      const uint32_t u2 = __float_as_uint(r1) & 0xffff0000u;  // next 8
+      const float r2 = r1 - __uint_as_float(u2);               // exact, <= 8 bits left
+      hi[0][j] = u1 >> 16;
+      hi[1][j] = u2 >> 16;
+      hi[2][j] = __float_as_uint(r2) >> 16;                    // r2 fits bf16 exactly
+    }
+    t1[i / 2] = hi[0][0] | (hi[0][1] << 16);
+    t2[i / 2] = hi[1][0] | (hi[1][1] << 16);
+    t3[i / 2] = hi[2][0] | (hi[2][1] << 16);
+  }
+  const int64_t plane = (int64_t)Epad * H, o = (int64_t)e * H + h;
+  st16(out + o, t1);
+  st16(out + plane + o, t2);
+  st16(out + 2 * plane + o, t3);
 }
 
 // bf16 GEMM P = x * (sum of the three split terms)^T over one K slice. LDS
@@ -345,12 +368,9 @@ size_t router_partial_bytes(int T, int E, bool has_shared, int H) {
 hipError_t launch_router_split(const float* w_router, const float* shared_gate, int E, int H,
                                uint16_t* split, hipStream_t s) {
   const int Epad = router_padded_rows(E, shared_gate != nullptr);
-  const int64_t n = (int64_t)Epad * H;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
   LaunchScope ls("router_split", s);
-  hipLaunchKernelGGL(router_split_kernel, dim3(blocks), dim3(256), 0, s, w_router, shared_gate, E,
-                     H, Epad, split);
+  hipLaunchKernelGGL(router_split_kernel, dim3(cdiv(H / 8, 256), Epad), dim3(256), 0, s, w_router,
+                     shared_gate, E, H, Epad, split);
   return hipGetLastError();
 }
 

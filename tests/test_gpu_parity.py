@@ -319,8 +319,10 @@ def test_permute_large_and_duplicates():
     """Several 2048-pair chunks with a ragged tail, all 256 experts, skewed
     and repeated ids (moe_permute does not need distinct ids per token)."""
     rng = np.random.default_rng(11)
+    # (8192 pairs: four whole chunks; 8200: a tail chunk of eight)
     for E, k, T, kind in [(256, 8, 1000, "zipf"), (200, 7, 3001, "uniform"), (1, 1, 4097, "one"),
-                          (32, 8, 513, "dup")]:
+                          (32, 8, 513, "dup"), (64, 8, 1024, "uniform"),
+                          (64, 8, 1025, "uniform")]:
         cfg = replace(CONFIGS["tiny"], E=E, k=k)
         if kind == "zipf":
             p = 1.0 / np.arange(1, E + 1)
