@@ -109,8 +109,9 @@ def parse():
     ap.add_argument("--tiers", default="",
                     help="mixed widths, e.g. 4:32,3:48,2:48 (bits:experts, hottest first)")
     ap.add_argument("--w-layout", choices=("tiled", "rows"), default="tiled",
-                    help="layout of the 4-bit expert weights of the fp16 route: regrouped once "
-                         "by moe_pack_w4 before the timed steps (tiled), or row-major")
+                    help="layout of the expert weights of the fp16 and mixed-width routes: "
+                         "regrouped once by moe_pack_w4 / moe_pack_tier before the timed "
+                         "steps (tiled), or row-major")
     ap.add_argument("--no-regimes", action="store_true",
                     help="skip the T=1/4/16 sweep and the skewed shared-expert layer that the "
                          "default headline run adds as extra fields")
@@ -463,8 +464,8 @@ def main():
     i8 = a.route == "i8"
     tiers = [(int(b), int(n)) for b, n in (t.split(":") for t in a.tiers.split(","))] if a.tiers else []
     streamed = a.stream_hot >= 0
-    # (the integer, mixed-width and host-streamed routes read row-major weights only)
-    tiled = a.w_layout == "tiled" and not (i8 or tiers or streamed)
+    # (the integer and host-streamed routes read row-major weights only)
+    tiled = a.w_layout == "tiled" and not (i8 or streamed)
     if streamed and (i8 or tiers or stacked or cfg.quant != "sym" or cfg.shared_I):
         print("streamed experts need one layer of symmetric experts without a shared expert",
               file=sys.stderr)
@@ -533,11 +534,13 @@ def main():
                     widths[e] = b
                 pos += n
             mixed = make_mixed_layer(cfg, widths, device=dev)
-            experts = qm.MixedExperts(mixed, dev)
+            # tiled: every tier regrouped once by moe_pack_tier
+            mshape = qm.shape_of(cfg, qm.MOE_W_TILED) if tiled else shape
+            experts = qm.MixedExperts(qm.pack_mixed(cfg, mixed) if tiled else mixed, dev)
             ws = qm.workspace(shape, T, dev, qm.MOE_WS_LAYER)
 
             def step():
-                qm.moe_layer_forward_mixed(shape, x, mixed.w_router, mixed.router_bias, experts,
+                qm.moe_layer_forward_mixed(mshape, x, mixed.w_router, mixed.router_bias, experts,
                                            out=out, ws=ws)
         elif i8:
             shape = qm.shape_of(cfg)
@@ -757,8 +760,10 @@ def main():
                       ("fp16, mixed widths " + a.tiers if tiers else
                        (f"fp16, {cfg.E - a.stream_hot} experts streamed from host memory, "
                         f"{a.stream_hot} on the GPU" if streamed else "fp16"))),
-            "weights": ("4-bit matrices regrouped once into the tiled layout (moe_pack_w4) "
-                        "before the timed steps" if tiled else "row-major 4-bit matrices"),
+            "weights": (("every tier's matrices regrouped once into the tiled layout "
+                         "(moe_pack_tier)" if tiers else
+                         "4-bit matrices regrouped once into the tiled layout (moe_pack_w4)") +
+                        " before the timed steps" if tiled else "row-major matrices"),
         },
         "layer_tflops": round(layer_tflops, 1),
         "layer_mfma_frac": round(layer_tflops / peak, 4),

@@ -83,8 +83,9 @@ typedef enum { MOE_Q4_SYM = 0, MOE_Q4_ASYM = 1 } moe_quant_t;
  *                matrix cores consume them, so that every load of the
  *                library's GEMM kernels reads whole cache lines. Accepted by
  *                moe_expert_ffn, moe_layer_forward and moe_layer_forward_static
- *                (the same results, bit for bit); the integer, mixed-width
- *                and host-streamed calls return MOE_ERR_UNSUPPORTED for it. */
+ *                (the same results, bit for bit), and by the mixed-width calls
+ *                with every tier regrouped by moe_pack_tier; the integer and
+ *                host-streamed calls return MOE_ERR_UNSUPPORTED for it. */
 typedef enum { MOE_W_ROWS = 0, MOE_W_TILED = 1 } moe_w_layout_t;
 
 typedef struct {
@@ -324,8 +325,9 @@ typedef struct {
  *   expert_bits  [E] int32 device array: each expert's width (one of the tiers')
  *   expert_slot  [E] int32 device array: its index within that tier's tensors
  *                (a slot outside [0, E_b) reads zeros, no fault)
- * Needs quant == MOE_Q4_SYM and shared_inter == 0; ws as moe_expert_ffn
- * (MOE_WS_EXPERT_FFN). One launch per tier and GEMM. */
+ * Needs quant == MOE_Q4_SYM and shared_inter == 0; the tiers' w13 and w2 in
+ * shape.w_layout (MOE_W_TILED: each one regrouped by moe_pack_tier); ws as
+ * moe_expert_ffn (MOE_WS_EXPERT_FFN). One launch per tier and GEMM. */
 moe_status_t moe_expert_ffn_mixed(const moe_shape_t *shape, int64_t T, const uint16_t *x,
                                   const moe_tier_t *tiers, int32_t n_tiers,
                                   const int32_t *expert_bits, const int32_t *expert_slot,
@@ -399,6 +401,26 @@ moe_status_t moe_layer_forward_streamed(const moe_shape_t *shape, int64_t T, con
  *   (2 I_s, H), s2 with (H, I_s). Enqueued on `stream`. */
 moe_status_t moe_pack_w4(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K,
                          hipStream_t stream);
+
+/* Regroups one packed matrix of a mixed-width tier (bits 4, 3 or 2, the row
+ * layouts of moe_tier_t) into MOE_W_TILED, once, when the weights are
+ * loaded; a mixed-width call with shape.w_layout = MOE_W_TILED reads every
+ * tier this way. Each row's 32-element blocks (4 * bits bytes) move whole:
+ *   block k / 32 of source row sigma(r) goes to byte offset
+ *   ((r / 16) * (K / 128) + k / 128) * 256 * bits
+ *       + (((k % 128) / 32) * 16 + r % 16) * 4 * bits
+ * of dst, for every destination row r < rows. sigma(r) = r, except for the
+ * 3- and 2-bit gate/up matrices (gate_up != 0, bits < 4), whose kernel reads
+ * the rows of each 32-row group in pairs: for r = 32 g + 16 p + i (i < 16),
+ *   sigma(r) = 32 g + 2 p + 8 (i / 4) + (0, 4, 1, 5)[i % 4].
+ * With bits = 4 the result is that of moe_pack_w4.
+ *   src [rows][K * bits / 8] bytes, dst the same size (device; 4-byte
+ *   aligned; must not overlap); rows % 16 == 0 (% 32 for a 3- or 2-bit
+ *   gate/up matrix), K % 128 == 0, rows * K * bits / 8 < 2^31 (else
+ *   INVALID_ARGUMENT / UNSUPPORTED). Pack a tier's w13 with (E_b * 2I, H,
+ *   bits, 1) and its w2 with (E_b * H, I, bits, 0). Enqueued on `stream`. */
+moe_status_t moe_pack_tier(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K,
+                           int32_t bits, int32_t gate_up, hipStream_t stream);
 
 moe_status_t moe_rmsnorm(int64_t T, int64_t H, const uint16_t *x, const float *weight,
                          float eps, uint16_t *out, hipStream_t stream);

@@ -51,6 +51,7 @@ EXPORTED = [
     "moe_stream_stage_bytes",
     "moe_layer_forward_streamed",
     "moe_pack_w4",
+    "moe_pack_tier",
     "moe_rmsnorm",
     "moe_profile_enable",
     "moe_profile_reset",
@@ -145,6 +146,8 @@ def lib():
                                              P, P, P, ctypes.c_size_t, P, P]
     L.moe_pack_w4.restype = st
     L.moe_pack_w4.argtypes = [P, P, i64, i64, P]
+    L.moe_pack_tier.restype = st
+    L.moe_pack_tier.argtypes = [P, P, i64, i64, i32, i32, P]
     L.moe_rmsnorm.restype = st
     L.moe_rmsnorm.argtypes = [i64, i64, P, P, ctypes.c_float, P, P]
     L.moe_profile_enable.restype = st

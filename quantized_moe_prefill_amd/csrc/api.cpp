@@ -455,7 +455,6 @@ static moe_status_t ffn_i8_impl(const Shape& s, int64_t T, const uint16_t* x,
 
 // ---- mixed-width experts ----
 static moe_status_t check_tiers(const Shape& s, const moe_tier_t* tiers, int32_t n) {
-  if (rows_only(s, "the mixed-width route") != MOE_OK) return MOE_ERR_UNSUPPORTED;
   if (s.asym) return fail(MOE_ERR_UNSUPPORTED, "mixed-width experts need MOE_Q4_SYM");
   if (s.Is != 0) return fail(MOE_ERR_UNSUPPORTED, "mixed-width layers have no shared expert");
   if (tiers == nullptr) return fail(MOE_ERR_INVALID_ARGUMENT, "tiers is NULL");
@@ -502,6 +501,7 @@ static moe_status_t ffn_mixed_impl(const Shape& s, int64_t T, const uint16_t* x,
   g.ldc = s.I;
   g.tier = ebits;
   g.slot = eslot;
+  g.w_tiled = s.tiled;  // every tier packed by moe_pack_tier
   for (int i = 0; i < n_tiers; ++i) {
     g.W = tiers[i].w13;
     g.Wscale = tiers[i].w13_scale;
@@ -1283,6 +1283,28 @@ moe_status_t moe_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t
   if (a0 < b0 + n && b0 < a0 + n)
     return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_w4: src and dst overlap");
   QMOE_HIP(launch_pack_w4(src, dst, rows, K, stream), "pack_w4 launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_tier(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K, int32_t bits,
+                           int32_t gate_up, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || rows <= 0 || K <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_tier: null pointer or non-positive size");
+  if (bits != 4 && bits != 3 && bits != 2)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_tier: bits must be 4, 3 or 2 (got %d)", bits);
+  const bool inter = gate_up != 0 && bits != 4;
+  if (rows % (inter ? 32 : 16) != 0 || K % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "moe_pack_tier: rows must be a multiple of %d, K of 128", inter ? 32 : 16);
+  const int64_t bytes = rows * (K / 8) * bits;
+  if (bytes >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_tier: matrix must be below 2^31 bytes");
+  if ((reinterpret_cast<uintptr_t>(src) & 3) != 0 || (reinterpret_cast<uintptr_t>(dst) & 3) != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_tier: pointers must be 4-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), b0 = reinterpret_cast<uintptr_t>(dst);
+  if (a0 < b0 + (uintptr_t)bytes && b0 < a0 + (uintptr_t)bytes)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "moe_pack_tier: src and dst overlap");
+  QMOE_HIP(launch_pack_tier(src, dst, rows, K, bits, inter, stream), "pack_tier launch");
   return MOE_OK;
 }
 

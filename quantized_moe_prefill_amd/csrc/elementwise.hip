@@ -160,6 +160,48 @@ hipError_t launch_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_
   return hipGetLastError();
 }
 
+// Any width b (4, 3 or 2 bits): the 4b-byte 32-element blocks of a matrix
+// [rows][K b / 8] regrouped into blocks of 16 rows x 128 K (256 b bytes;
+// lane l = ((k % 128) / 32) * 16 + r % 16 at 4 b l), one 32-bit word per
+// thread. With `interleave` (the 3- and 2-bit gate/up matrices, whose kernel
+// gives fragment f of a 32-row group the rows 2 (f % 2) + prow(r)), block
+// row 16 p + r of each 32-row group takes source row 2 p + prow(r),
+// prow(r) = 8 (r / 4) + kperm(r % 4).
+__global__ __launch_bounds__(256) void pack_tier_kernel(const uint32_t* __restrict__ src,
+                                                        uint32_t* __restrict__ dst,
+                                                        int64_t words, int nk, int bits,
+                                                        int row_words, int interleave) {
+  const int blk_words = 64 * bits;  // words of one 16-row x 128-K block
+  for (int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x; w < words;
+       w += (int64_t)gridDim.x * 256) {
+    const int64_t b = w / blk_words;
+    const int in = (int)(w - b * blk_words);
+    const int l = in / bits, j = in - l * bits;
+    const int64_t stripe = b / nk;
+    const int st = (int)(b - stripe * nk);
+    const int r = l & 15;
+    int64_t row = stripe * 16 + r;
+    if (interleave) {
+      const int p = (int)(stripe & 1);
+      row = (stripe >> 1) * 32 + 2 * p + 8 * (r >> 2) + kperm(r & 3);
+    }
+    dst[w] = src[row * row_words + st * 4 * bits + (l >> 4) * bits + j];
+  }
+}
+
+hipError_t launch_pack_tier(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K, int bits,
+                            bool interleave, hipStream_t s) {
+  const int64_t words = rows * K / 32 * bits;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) return hipSuccess;
+  LaunchScope ls("pack_tier", s);
+  hipLaunchKernelGGL(pack_tier_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), words,
+                     (int)(K / 128), bits, (int)(K / 32 * bits), interleave ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* out, int T,
                           int H, hipStream_t s) {
   const dim3 grid(cdiv(T, 4)), block(256);

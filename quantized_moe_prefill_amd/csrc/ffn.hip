@@ -133,9 +133,12 @@ constexpr int SC_STAGE = 0, SC_TILE = 1, SC_WINDOW = 2;
 // 8-byte load per fragment and stage. MIX: one group of experts of a
 // mixed layer (the expert filter and slot map of GroupedGemm are read).
 // TBM: rows per tile, 128, or 64 for layers whose experts get about 64
-// rows or fewer (a 128-row tile would be mostly padding there).
+// rows or fewer (a 128-row tile would be mostly padding there). WT: a mixed
+// layer's weights are tiled (a compile-time choice there: the runtime one
+// makes the 3-bit gate/up instance spill; the plain instances read
+// g.w_tiled).
 template <bool GATEUP, bool ASYM, int SCM, bool FOLD, int BITS = 4, bool MIX = false,
-          int TBM = 128>
+          int TBM = 128, bool WT = false>
 __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g, int n_ntiles) {
   static_assert(TBM == 128 || TBM == 64, "tile rows");
   static_assert(TBM / 4 / NWAVES <= 4, "activation loads per wave");
@@ -374,13 +377,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   uint32_t sl = 0;     // SC_STAGE: this lane's scales
   uint32_t wl = 0;     // SC_WINDOW: this lane's row's scale groups
   int ash = 0, wsh = 0;
-  // tiled 4-bit weights (moe_pack_w4): fragment f's 16 rows x 128 K of a
-  // stage are one 1 KB block, lane l's 16 bytes at 16 l (BITS == 4 only)
-  const bool wt = BITS == 4 && g.w_tiled;
-  const int w_kstep = wt ? 1024 : BK / 8 * BITS;  // bytes from one K stage to the next
+  // tiled weights (moe_pack_w4, moe_pack_tier): fragment f's 16 rows x 128
+  // K of a stage are one block of 256 BITS bytes, lane l's 4 BITS bytes at
+  // 4 BITS l. The block of fragment f is the 16-row stripe at frow_t(f);
+  // with DIRECT the pack has already put the rows frow(f) + prow(r) of each
+  // 32-row group into that stripe's row r.
+  const bool wt = MIX ? WT : BITS == 4 && g.w_tiled;
+  const int w_kstep = wt ? 256 * BITS : BK / 8 * BITS;  // bytes from one K stage to the next
+  auto frow_t = [&](int f) { return GATEUP ? 16 * (f & 1) + (f < 2 ? 0 : N / 2) : 16 * f; };
   auto set_w = [&](const TileU& t) {
     const int wr0 = wrow_first(t);
-    bl = wt ? (uint32_t)wr0 * wrow_bytes + (uint32_t)lane_o * 16u
+    bl = wt ? (uint32_t)wr0 * wrow_bytes + (uint32_t)lane_o * (4u * BITS)
             : (uint32_t)(wr0 + prow(r16)) * wrow_bytes + lg * 4 * BITS;
     if (SCM == SC_STAGE) sl = ((uint32_t)(wr0 + prow(r16)) * KG + (lg * 32) / g.G) * 2;
     if (WIN) {
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   auto load_b = [&](int kt, WV* cb, uint32_t* rs, uint32_t* rm) {
 #pragma unroll
     for (int f = 0; f < NFRAG; ++f) {
-      const int so = frow(f) * wrow_bytes + kt * w_kstep;
+      const int so = (wt ? frow_t(f) : frow(f)) * wrow_bytes + kt * w_kstep;
       if constexpr (BITS == 4) {
         cb[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               wsh ? rW2 : rW, bl, so, 0));
@@ -900,8 +907,12 @@ hipError_t launch_grouped(const GroupedGemm& g, hipStream_t s, const char* name)
     // one width of a mixed-width layer (symmetric, no extra group)
     auto go_b = [&](auto m, auto b) {
       constexpr int M = decltype(m)::value, B = decltype(b)::value;
-      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, false, M, false, B, true>), grid, block, 0,
-                         s, g, n_ntiles);
+      if (g.w_tiled)
+        hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, false, M, false, B, true, 128, true>), grid,
+                           block, 0, s, g, n_ntiles);
+      else
+        hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, false, M, false, B, true>), grid, block, 0,
+                           s, g, n_ntiles);
     };
     const std::integral_constant<int, 4> b4{};
     const std::integral_constant<int, 3> b3{};

@@ -160,6 +160,10 @@ hipError_t launch_small_experts(const SmallLayer& a, hipStream_t s);
 // K % 128 == 0).
 hipError_t launch_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K,
                           hipStream_t s);
+// Any width, into the tiled layout (interleave: the 3- and 2-bit gate/up row
+// order within 32-row groups); rows % 16 == 0 (32 with interleave), K % 128 == 0.
+hipError_t launch_pack_tier(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K, int bits,
+                            bool interleave, hipStream_t s);
 // The router logits alone for at most kRouterGemvT tokens (one plane, [T][Epad]).
 hipError_t launch_router_gemv(const uint16_t* x, const float* w_router, const float* shared_gate,
                               int T, int H, int E, float* partial, hipStream_t s);

@@ -84,6 +84,37 @@ def moe_pack_w4(src: torch.Tensor, rows: int, K: int) -> torch.Tensor:
     return dst
 
 
+def moe_pack_tier(src: torch.Tensor, rows: int, K: int, bits: int, gate_up: bool) -> torch.Tensor:
+    """The MOE_W_TILED copy of one packed matrix of a mixed-width tier,
+    src [rows][K * bits / 8] (u8, any leading shape with that many bytes);
+    gate_up: a w13 matrix (its 3- and 2-bit rows are also put in the order
+    the gate/up kernel reads them)."""
+    dev = src.device
+    if src.numel() != rows * K * bits // 8:
+        raise ValueError(f"src holds {src.numel()} bytes, expected rows * K * bits / 8 = "
+                         f"{rows * K * bits // 8}")
+    dst = torch.empty_like(src)
+    N.check(N.lib().moe_pack_tier(_ptr(src, "src", (torch.uint8,), dev),
+                                  _ptr(dst, "dst", (torch.uint8,), dev), int(rows), int(K),
+                                  int(bits), 1 if gate_up else 0, _stream(dev)))
+    return dst
+
+
+def pack_mixed(cfg, ml):
+    """A copy of a mixed-width layer (synth.MixedLayer or alike) whose tiers'
+    w13 and w2 are in the MOE_W_TILED layout (moe_pack_tier), for the
+    mixed-width calls with shape_of(cfg, N.MOE_W_TILED). Scales are shared."""
+    out = dataclasses.replace(ml) if dataclasses.is_dataclass(ml) else copy.copy(ml)
+    H, I = cfg.H, cfg.I
+    tiers = {}
+    for b, (w13, s13, w2, s2) in ml.tiers.items():
+        n = int(w13.shape[0])
+        tiers[b] = (moe_pack_tier(w13, n * 2 * I, H, int(b), True), s13,
+                    moe_pack_tier(w2, n * H, I, int(b), False), s2)
+    out.tiers = tiers
+    return out
+
+
 def pack_layer(cfg, li):
     """A copy of a layer's tensors (synth.LayerInputs or alike) whose four
     4-bit matrices (w13, w2 and the shared expert's s13, s2) are in the

@@ -314,6 +314,9 @@ def test_tiled_layout_validation():
     e = _experts()
     assert L.moe_layer_forward_i8(ctypes.byref(t), 4, FAKE, FAKE, None, ctypes.byref(e), None, FAKE,
                                   FAKE, 1 << 30, None) == N.MOE_ERR_UNSUPPORTED
+    # the mixed-width calls take tiled tiers (moe_pack_tier): the host checks pass
+    st, n = _ws(t, 8192, N.MOE_WS_EXPERT_FFN)
+    assert st == N.MOE_OK
     pk = L.moe_pack_w4
     assert pk(None, FAKE, 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT
     assert pk(FAKE, FAKE + (1 << 24), 24, 128, None) == N.MOE_ERR_INVALID_ARGUMENT   # rows % 16
@@ -321,3 +324,23 @@ def test_tiled_layout_validation():
     assert pk(FAKE, FAKE + 512, 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT         # overlap
     assert pk(FAKE + 8, FAKE + (1 << 24), 16, 128, None) == N.MOE_ERR_INVALID_ARGUMENT  # alignment
     assert pk(FAKE, FAKE + (1 << 34), 1 << 20, 1 << 12, None) == N.MOE_ERR_UNSUPPORTED  # >= 2^31 B
+
+
+def test_pack_tier_validation():
+    """moe_pack_tier checks its arguments before launching (include/moe.h,
+    moe_pack_tier): width, row and K multiples (32 rows for a 3- or 2-bit
+    gate/up matrix, whose rows interleave in 32-row groups), size, alignment
+    and overlap."""
+    L = _lib()
+    pk = L.moe_pack_tier
+    far = FAKE + (1 << 24)
+    assert pk(None, FAKE, 16, 128, 4, 0, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert pk(FAKE, far, 16, 128, 5, 0, None) == N.MOE_ERR_UNSUPPORTED           # bits
+    assert pk(FAKE, far, 24, 128, 3, 0, None) == N.MOE_ERR_INVALID_ARGUMENT      # rows % 16
+    assert pk(FAKE, far, 16, 128, 3, 1, None) == N.MOE_ERR_INVALID_ARGUMENT      # rows % 32
+    assert pk(FAKE, far, 16, 128, 2, 1, None) == N.MOE_ERR_INVALID_ARGUMENT
+    assert pk(FAKE, far, 16, 192, 2, 0, None) == N.MOE_ERR_INVALID_ARGUMENT      # K % 128
+    assert pk(FAKE, FAKE + 256, 32, 128, 3, 1, None) == N.MOE_ERR_INVALID_ARGUMENT  # overlap
+    assert pk(FAKE + 2, far, 16, 128, 3, 0, None) == N.MOE_ERR_INVALID_ARGUMENT  # alignment
+    assert pk(FAKE, FAKE + (1 << 34), 1 << 20, 1 << 13, 2, 0, None) == N.MOE_ERR_UNSUPPORTED
+    assert b"moe_pack_tier" in L.moe_last_error()

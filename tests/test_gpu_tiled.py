@@ -86,3 +86,70 @@ def test_tiled_expert_ffn_bitwise(name, T):
             assert a is None
             continue
         assert torch.equal(bits16(a), bits16(b))
+
+
+def tier_tiled_ref(src: np.ndarray, rows: int, K: int, bits: int, gate_up: bool) -> np.ndarray:
+    """moe_pack_tier written out from its definition: rows reordered by sigma
+    (the 3- and 2-bit gate/up matrices: within each 32-row group, row
+    16 p + i takes row 2 p + 8 (i // 4) + (0, 4, 1, 5)[i % 4]), then each
+    row's 4 bits-byte blocks of 32 elements ordered (stripe, stage, lg, r16)."""
+    a = src.reshape(rows, K * bits // 8)
+    if gate_up and bits < 4:
+        sigma = np.empty(rows, dtype=np.int64)
+        for r in range(rows):
+            g, q = divmod(r, 32)
+            p, i = divmod(q, 16)
+            sigma[r] = 32 * g + 2 * p + 8 * (i // 4) + (0, 4, 1, 5)[i % 4]
+        assert np.array_equal(np.sort(sigma), np.arange(rows))
+        a = a[sigma]
+    a = a.reshape(rows // 16, 16, K // 128, 4, 4 * bits)
+    return a.transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
+@pytest.mark.parametrize("gate_up", [False, True])
+@pytest.mark.parametrize("rows,K", [(32, 128), (96, 384), (1536, 2048)])
+def test_pack_tier_layout(bits, gate_up, rows, K):
+    g = torch.Generator(device="cpu").manual_seed(rows * 11 + K + bits)
+    src = torch.randint(0, 256, (rows, K * bits // 8), dtype=torch.uint8, generator=g)
+    dst = qm.moe_pack_tier(src.to(DEV), rows, K, bits, gate_up).cpu().numpy().reshape(-1)
+    assert np.array_equal(dst, tier_tiled_ref(src.numpy(), rows, K, bits, gate_up))
+    if bits == 4:
+        assert np.array_equal(dst, qm.moe_pack_w4(src.to(DEV), rows, K).cpu().numpy().reshape(-1))
+
+
+# mixed-width layers: (workload, tokens, width pattern); the patterns of
+# tests/test_gpu_mixed.py, whose row-major calls are checked against the oracle
+MIXED_CASES = [("tiny", 64, [4, 3, 2]), ("a3b_pp512", 512, [4, 3, 3, 2, 2, 2, 3, 2]),
+               ("a3b_pp8192", 8192, [4, 3, 2, 3]), ("a3b_pp8192", 8192, [3]),
+               ("a3b_pp8192", 8192, [2]), ("a3b_pp512", 3, [2, 3, 4, 2])]
+
+
+@pytest.mark.parametrize("name,T,pattern", MIXED_CASES)
+def test_tiled_mixed_bitwise(name, T, pattern):
+    """Mixed-width layers on tiers regrouped by moe_pack_tier: y_perm and the
+    layer output bit-equal to the same calls on row-major tiers."""
+    from synth.mixed import make_mixed_layer
+    cfg = replace(CONFIGS[name], T=T)
+    perm = np.random.default_rng(0).permutation(cfg.E)
+    widths = [4] * cfg.E
+    for i, e in enumerate(perm):
+        widths[e] = pattern[i % len(pattern)]
+    ml = make_mixed_layer(cfg, widths, device=DEV)
+    x = make_tokens(cfg, device=DEV)
+    shape = qm.shape_of(cfg)
+    tshape = qm.shape_of(cfg, qm.MOE_W_TILED)
+    ex = qm.MixedExperts(ml, DEV)
+    mt = qm.pack_mixed(cfg, ml)
+    ext = qm.MixedExperts(mt, DEV)
+    for b in ml.tiers:
+        assert not torch.equal(mt.tiers[b][0], ml.tiers[b][0])
+    _, ids, _, _ = qm.moe_route(shape, x, ml.w_router, ml.router_bias, None)
+    counts, offsets, sp, _ = qm.moe_permute(shape, ids)
+    y_ref = qm.moe_expert_ffn_mixed(shape, x, ex, counts, offsets, sp).clone()
+    y_got = qm.moe_expert_ffn_mixed(tshape, x, ext, counts, offsets, sp)
+    out_ref = qm.moe_layer_forward_mixed(shape, x, ml.w_router, ml.router_bias, ex).clone()
+    out_got = qm.moe_layer_forward_mixed(tshape, x, ml.w_router, ml.router_bias, ext)
+    torch.cuda.synchronize()
+    assert torch.equal(bits16(y_got), bits16(y_ref)), f"{name} T={T} {pattern}: tiled y_perm differs"
+    assert torch.equal(bits16(out_got), bits16(out_ref)), f"{name} T={T} {pattern}: tiled out differs"
