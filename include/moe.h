@@ -413,6 +413,9 @@ moe_status_t moe_pack_w4(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t
  * 3- and 2-bit gate/up matrices (gate_up != 0, bits < 4), whose kernel reads
  * the rows of each 32-row group in pairs: for r = 32 g + 16 p + i (i < 16),
  *   sigma(r) = 32 g + 2 p + 8 (i / 4) + (0, 4, 1, 5)[i % 4].
+ * With bits = 3 the block's third 32-bit word (the third bits) is also
+ * re-ordered: its bit 4c + i + 16h (c, i < 4, h < 2) moves to bit
+ *   (2 + 2i + 16h + (0, 1, 8, 9)[c]) mod 32.
  * With bits = 4 the result is that of moe_pack_w4.
  *   src [rows][K * bits / 8] bytes, dst the same size (device; 4-byte
  *   aligned; must not overlap); rows % 16 == 0 (% 32 for a 3- or 2-bit

@@ -109,4 +109,75 @@ __device__ __forceinline__ f16x8 dequant8_f16_b3(uint32_t w, uint32_t hb, int c,
   return __builtin_bit_cast(f16x8, o);
 }
 
+// The same codes without a shift per pair: the fp16 pattern ORed around pair
+// i (bits 2i, 2i + 1 of each half) has exponent 25 - 2i, which makes mantissa
+// bit 2i count in units of one, so the pair reads as 2^(10 - 2i) + q from the
+// unshifted word (one shift by 8 for the upper byte of each half). The
+// subtraction of 2^(10 - 2i) + 2^(b-1) is exact and the multiply rounds once:
+// the same fp16 weights as the per-pair shift form.
+struct LowBitMagic {
+  uint32_t magic[4];  // 2^(10 - 2i) in both halves, in vector registers
+  uint32_t m2[4];     // 0x00030003 << 2i, in scalar registers
+  uint32_t m4[4];     // 0x00040004 << 2i (the 3-bit high bit of pair i)
+};
+__device__ __forceinline__ LowBitMagic low_bit_magic() {
+  LowBitMagic k;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    k.magic[i] = (uint32_t)(0x6400 - 0x0800 * i) * 0x10001u;
+    asm("" : "+v"(k.magic[i]));
+    k.m2[i] = __builtin_amdgcn_readfirstlane(0x00030003u << (2 * i));
+    k.m4[i] = __builtin_amdgcn_readfirstlane(0x00040004u << (2 * i));
+  }
+  return k;
+}
+
+// Chunk `h` (0 or 1) of a word of 2-bit codes -> eight fp16 weights.
+__device__ __forceinline__ f16x8 dequant8_f16_b2x(uint32_t w, int h, f16x2 s2) {
+  const LowBitMagic k = low_bit_magic();
+  const uint32_t wl = h ? w >> 8 : w;
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 base = (_Float16)(float)((1024 >> (2 * i)) + 2);
+    const uint32_t t = (wl & k.m2[i]) | k.magic[i];
+    o[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, t) - f16x2{base, base}) * s2);
+  }
+  return __builtin_bit_cast(f16x8, o);
+}
+
+// 3-bit codes in the tiled layout (moe_pack_tier), whose third-bit word holds
+// the high bit of element 8c + i + 4h at bit (2 + 2i + 16h + (0, 1, 8, 9)[c])
+// mod 32: rotated right by (0, 1, 8, 9)[c], chunk c's high bits sit just
+// above the low bits of their pair (bit 2i + 2 of each half), so one rotate
+// per chunk replaces a shift per pair.
+__device__ __forceinline__ f16x8 dequant8_f16_b3t(uint32_t w, uint32_t hb, int c, f16x2 s2) {
+  asm("" : "+v"(hb));
+  const LowBitMagic k = low_bit_magic();
+  const uint32_t wl = (c & 1) ? w >> 8 : w;
+  constexpr int rot[4] = {0, 1, 8, 9};
+  const uint32_t hc = c == 0 ? hb : __builtin_amdgcn_alignbit(hb, hb, rot[c & 3]);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 base = (_Float16)(float)((1024 >> (2 * i)) + 4);
+    uint32_t t = (wl & k.m2[i]) | k.magic[i];
+    t |= hc & k.m4[i];
+    o[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, t) - f16x2{base, base}) * s2);
+  }
+  return __builtin_bit_cast(f16x8, o);
+}
+
+// The third-bit word of a 3-bit block rearranged for dequant8_f16_b3t: bit
+// 4c + i + 16h moves to bit (2 + 2i + 16h + (0, 1, 8, 9)[c]) mod 32.
+__host__ __device__ inline uint32_t b3_high_tiled(uint32_t hb) {
+  const int rot[4] = {0, 1, 8, 9};
+  uint32_t o = 0;
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 4; ++i)
+      for (int h = 0; h < 2; ++h)
+        o |= ((hb >> (4 * c + i + 16 * h)) & 1u) << ((2 + 2 * i + 16 * h + rot[c]) & 31);
+  return o;
+}
+
 }  // namespace qmoe

@@ -4,6 +4,7 @@
 // consecutive channels of a row, so every row is read and written with
 // fully coalesced 16-byte accesses.
 #include "common.h"
+#include "dequant.h"
 #include "kernels.h"
 
 namespace qmoe {
@@ -166,7 +167,8 @@ hipError_t launch_pack_w4(const uint8_t* src, uint8_t* dst, int64_t rows, int64_
 // thread. With `interleave` (the 3- and 2-bit gate/up matrices, whose kernel
 // gives fragment f of a 32-row group the rows 2 (f % 2) + prow(r)), block
 // row 16 p + r of each 32-row group takes source row 2 p + prow(r),
-// prow(r) = 8 (r / 4) + kperm(r % 4).
+// prow(r) = 8 (r / 4) + kperm(r % 4). With 3 bits the third word of each
+// lane's 12 bytes (the block's high bits) is rearranged by b3_high_tiled.
 __global__ __launch_bounds__(256) void pack_tier_kernel(const uint32_t* __restrict__ src,
                                                         uint32_t* __restrict__ dst,
                                                         int64_t words, int nk, int bits,
@@ -185,7 +187,10 @@ __global__ __launch_bounds__(256) void pack_tier_kernel(const uint32_t* __restri
       const int p = (int)(stripe & 1);
       row = (stripe >> 1) * 32 + 2 * p + 8 * (r >> 2) + kperm(r & 3);
     }
-    dst[w] = src[row * row_words + st * 4 * bits + (l >> 4) * bits + j];
+    const uint32_t v = src[row * row_words + st * 4 * bits + (l >> 4) * bits + j];
+    // (3 bits: the third-bit word of each 32-element block in the order the
+    // tiled kernels decode it)
+    dst[w] = bits == 3 && j == 2 ? b3_high_tiled(v) : v;
   }
 }
 

@@ -490,8 +490,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
   auto dequant_chunk = [&](const WV& w, int c, f16x2 s2, f16x2 m2) {
     // (the down GEMM keeps the shift-per-nibble form: with the one-shift
     // form its 128-row instance spills)
+    // (3 bits, tiled: the third-bit word rearranged by the pack, one rotate
+    // per chunk instead of a shift per pair)
     if constexpr (BITS == 4) return dequant8_f16<ASYM, GATEUP>(w[c], s2, m2);
-    else if constexpr (BITS == 2) return dequant8_f16_b2(w[c >> 1], c & 1, s2);
+    else if constexpr (BITS == 2) return dequant8_f16_b2x(w[c >> 1], c & 1, s2);
+    else if constexpr (MIX && WT) return dequant8_f16_b3t(w[c >> 1], w[2], c, s2);
     else return dequant8_f16_b3(w[c >> 1], w[2], c, s2);
   };
 

@@ -103,7 +103,21 @@ def tier_tiled_ref(src: np.ndarray, rows: int, K: int, bits: int, gate_up: bool)
         assert np.array_equal(np.sort(sigma), np.arange(rows))
         a = a[sigma]
     a = a.reshape(rows // 16, 16, K // 128, 4, 4 * bits)
-    return a.transpose(0, 2, 3, 1, 4).reshape(-1)
+    out = a.transpose(0, 2, 3, 1, 4).reshape(-1)
+    if bits == 3:
+        # the third word of every 12-byte block: bit 4c + i + 16h moves to
+        # bit (2 + 2i + 16h + (0, 1, 8, 9)[c]) mod 32
+        words = out.view("<u4").reshape(-1, 3).copy()
+        hb = words[:, 2]
+        new = np.zeros_like(hb)
+        for c in range(4):
+            for i in range(4):
+                for h in range(2):
+                    bit = (hb >> np.uint32(4 * c + i + 16 * h)) & np.uint32(1)
+                    new |= bit << np.uint32((2 + 2 * i + 16 * h + (0, 1, 8, 9)[c]) % 32)
+        words[:, 2] = new
+        out = words.reshape(-1).view(np.uint8)
+    return out
 
 
 @pytest.mark.parametrize("bits", [4, 3, 2])
@@ -114,6 +128,9 @@ def test_pack_tier_layout(bits, gate_up, rows, K):
     src = torch.randint(0, 256, (rows, K * bits // 8), dtype=torch.uint8, generator=g)
     dst = qm.moe_pack_tier(src.to(DEV), rows, K, bits, gate_up).cpu().numpy().reshape(-1)
     assert np.array_equal(dst, tier_tiled_ref(src.numpy(), rows, K, bits, gate_up))
+    if bits < 4:
+        # every bit kept: the same number of ones per matrix
+        assert (np.unpackbits(dst).sum() == np.unpackbits(src.numpy().reshape(-1)).sum())
     if bits == 4:
         assert np.array_equal(dst, qm.moe_pack_w4(src.to(DEV), rows, K).cpu().numpy().reshape(-1))
 
