@@ -303,11 +303,26 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __rest
   router_row(x, wr, sg, T, H, E, Epad, blockIdx.x, out, part);
 }
 
+// The K split that finishes the tiles in the fewest stage times on one
+// workgroup per CU: rounds of 256 workgroups times the stages per tile (the
+// smallest split on ties). Beyond one round it stops at 4 planes, since the
+// top-k reads every plane: 320 tiles (E = 256 with the shared gate at T =
+// 8192) take 5 rounds of 8 stages at 4 planes instead of 2 rounds of 32 at
+// one; within one round it is the largest split that fits, as before.
 int router_ksplit(int T, int E, bool has_shared, int H) {
   const int tiles = cdiv(T, RBM) * cdiv(router_padded_rows(E, has_shared), RBE);
-  int ks = 1;
-  while (ks < kRouterMaxKsplit && tiles * ks * 2 <= 256 && (H / RBK) % (ks * 2) == 0) ks *= 2;
-  return ks;
+  const int S = H / RBK;
+  int best = 1;
+  int64_t best_cost = (int64_t)cdiv(tiles, 256) * S;
+  for (int ks = 2; ks <= kRouterMaxKsplit && S % ks == 0; ks *= 2) {
+    if (ks > 4 && tiles * ks > 256) break;
+    const int64_t cost = (int64_t)cdiv(tiles * ks, 256) * (S / ks);
+    if (cost < best_cost) {
+      best = ks;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 }  // namespace
