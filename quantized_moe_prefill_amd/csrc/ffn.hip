@@ -767,7 +767,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void expert_gemm_kernel(GroupedGemm g,
         }
       };
       if (XDQ && SCL) next_sc();
+      // a wave in its MFMA and dequant stream outranks its SIMD partner while
+      // that one issues loads, waits or crosses the barrier (gate/up 1.4-2.4 %
+      // faster over six A/B runs on two boxes; down unchanged)
+      __builtin_amdgcn_s_setprio(1);
       compute_stage(curs, cb, rs, rm, b0, cbn, rsn, rmn, nkt);
+      __builtin_amdgcn_s_setprio(0);
       if (!XDQ && SCL) next_sc();
       // The activation loads go last: their direct writes into the LDS then
       // land while the stage ends and the next one starts, not in the middle
