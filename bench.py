@@ -68,7 +68,7 @@ KERNELS_I8 = ("router_split", "router_gemm", "router_select", "permute_rank", "p
 # FETCH_SIZE + WRITE_SIZE (each scaled by the copy-kernel calibration factor),
 # keyed by the hash of the expert-GEMM sources they were measured on: a
 # changed kernel reports null until it is measured again.
-GATEUP_TRAFFIC = {"83610306a843ee18": 660900195}   # {source sha256[:16]: bytes per launch}
+GATEUP_TRAFFIC = {"df1d68e32e6e58bd": 660900258}   # {source sha256[:16]: bytes per launch}
 GEMM_SOURCES = ("quantized_moe_prefill_amd/csrc/ffn.hip", "quantized_moe_prefill_amd/csrc/common.h",
                 "quantized_moe_prefill_amd/csrc/dequant.h")
 # the same for the integer route's gate/up launch
